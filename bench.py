@@ -1,0 +1,283 @@
+"""Benchmark of the ViT encoder forward pass on one MI355X.
+
+One step = vit_forward + vit_descriptor over one batch (patch embedding, every
+encoder block, final LayerNorm, L2-normalised CLS descriptor), inputs already in
+HBM.  Prints ONE JSON line: images/s on ViT-S/16 @336 batch 32 (the headline
+workload), its fraction of the bf16 MFMA peak, the same for ViT-L/16 @1024
+batch 1, the roofline of the dominant kernel (timed with HIP events on the
+launch stream), and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu] [--no-large]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "images/s and % of bf16 MFMA peak, ViT-S/16@336 b32 and ViT-L/16@1024 b1"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flops_per_image(cfg: dict) -> dict:
+    """Algorithmic FLOPs (2 per multiply-add) of one image, by operation."""
+    p, D, Hm = cfg["patch"], cfg["dim"], cfg["mlp_hidden"]
+    gh, gw = cfg["img_h"] // p, cfg["img_w"] // p
+    P = gh * gw
+    N = P + 1 + cfg["registers"]
+    L = cfg["depth"] + cfg.get("extra_blocks", 0)
+    f = {
+        "patch_embed": 2 * P * 3 * p * p * D,
+        "qkv": L * 2 * N * D * 3 * D,
+        "attention": L * 4 * N * N * D,
+        "out_proj": L * 2 * N * D * D,
+        "fc1": L * 2 * N * D * Hm,
+        "fc2": L * 2 * N * Hm * D,
+    }
+    f["total"] = sum(f.values())
+    return f
+
+
+def time_gpu(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(stop) / steps, wall / steps * 1e3
+
+
+def bench_workload(name, batch, steps, warmup):
+    import torch
+    import synth
+    import vision_transformer_encoder_block_amd as vit
+    cfg = synth.preset(name)
+    P = synth.make_params(cfg)
+    enc = vit.Encoder(cfg, P, max_batch=batch)
+    x = torch.from_numpy(synth.make_images(cfg, batch)).cuda()
+    tok = torch.empty((batch, enc.tokens, cfg["dim"]), dtype=torch.float32, device="cuda")
+    desc = torch.empty((batch, cfg["dim"]), dtype=torch.float32, device="cuda")
+
+    def step():
+        enc.forward(x, tokens_out=tok)
+        enc.descriptor(tok, desc_out=desc)
+
+    ms, wall_ms = time_gpu(step, steps, warmup)
+    torch.cuda.synchronize()
+    assert torch.isfinite(desc).all().item(), "non-finite descriptor"
+    fl = flops_per_image(cfg)
+    tflops = fl["total"] * batch / (ms * 1e-3) / 1e12
+    res = dict(images_per_s=batch / (ms * 1e-3), ms_per_step=ms, wall_ms_per_step=wall_ms, tflops=tflops,
+               frac_bf16_peak=tflops / PEAK_BF16_TFLOPS, gflop_per_image=fl["total"] / 1e9)
+    return cfg, enc, res
+
+
+def kernel_breakdown(cfg, batch, steps=20, warmup=5):
+    """Average duration of each block kernel at the workload's shapes (HIP events
+    on the launch stream), through the per-op C ABI entry points."""
+    import torch
+    import vision_transformer_encoder_block_amd as vit
+    D, Hm, H = cfg["dim"], cfg["mlp_hidden"], cfg["heads"]
+    p = cfg["patch"]
+    N = (cfg["img_h"] // p) * (cfg["img_w"] // p) + 1 + cfg["registers"]
+    M = batch * N
+    L = cfg["depth"] + cfg.get("extra_blocks", 0)
+    nv = (N + 15) // 16 * 16
+    g = torch.Generator(device="cuda").manual_seed(7)
+    bf = torch.bfloat16
+
+    def rnd(*shape, dtype=bf, scale=0.05):
+        return (torch.randn(*shape, generator=g, device="cuda") * scale).to(dtype)
+
+    x = rnd(M, D, dtype=torch.float32, scale=1.0)
+    gam, bet = torch.ones(D, device="cuda"), torch.zeros(D, device="cuda")
+    h = rnd(M, D, scale=1.0)
+    wqkv, bqkv = rnd(3 * D, D), rnd(3 * D, dtype=torch.float32)
+    q = torch.empty((batch, H, N, 64), dtype=bf, device="cuda")
+    k = torch.empty_like(q)
+    vt = torch.zeros((batch, H, 64, nv), dtype=bf, device="cuda")
+    o = torch.empty((M, D), dtype=bf, device="cuda")
+    wo, bo, ls = rnd(D, D), rnd(D, dtype=torch.float32), torch.full((D,), 1e-5, device="cuda")
+    w1, b1 = rnd(Hm, D), rnd(Hm, dtype=torch.float32)
+    w2, b2 = rnd(D, Hm), rnd(D, dtype=torch.float32)
+    f = torch.empty((M, Hm), dtype=bf, device="cuda")
+    vit.vit_op_qkv(h, wqkv, bqkv, batch, N, H, q, k, vt)
+    ops = {
+        "layernorm": (lambda: vit.vit_op_layernorm(x, M, D, gam, bet, 1e-6, h, 0), 2 * L, 0.0,
+                      M * D * (4 + 2) + 8 * D, "hbm"),
+        "qkv": (lambda: vit.vit_op_qkv(h, wqkv, bqkv, batch, N, H, q, k, vt), L, 2.0 * M * D * 3 * D,
+                M * D * 2 + 3 * D * D * 2 + 3 * M * D * 2, "mfma"),
+        "attention": (lambda: vit.vit_op_attention(q, k, vt, batch, N, H, o), L, 4.0 * batch * N * N * D,
+                      4 * M * D * 2, "mfma"),
+        "out_proj": (lambda: vit.vit_op_linear(o, wo, bo, M, D, D, vit.EPI_RESIDUAL, ls, x), L,
+                     2.0 * M * D * D, M * D * 2 + D * D * 2 + 2 * M * D * 4, "mfma"),
+        "fc1": (lambda: vit.vit_op_linear(h, w1, b1, M, Hm, D, vit.EPI_GELU_BF16, None, f), L,
+                2.0 * M * D * Hm, M * D * 2 + Hm * D * 2 + M * Hm * 2, "mfma"),
+        "fc2": (lambda: vit.vit_op_linear(f, w2, b2, M, D, Hm, vit.EPI_RESIDUAL, ls, x), L,
+                2.0 * M * Hm * D, M * Hm * 2 + D * Hm * 2 + 2 * M * D * 4, "mfma"),
+    }
+    out = {}
+    for name, (fn, per_step, flops, nbytes, bound) in ops.items():
+        ms, _ = time_gpu(fn, steps, warmup)
+        out[name] = dict(ms=ms, launches_per_step=per_step, ms_per_step=ms * per_step, flops=flops,
+                         bytes=nbytes, bound=bound)
+    return out
+
+
+def roofline(breakdown, kernel_names):
+    name = max(breakdown, key=lambda n: breakdown[n]["ms_per_step"])
+    b = breakdown[name]
+    if b["bound"] == "mfma":
+        achieved = b["flops"] / (b["ms"] * 1e-3) / 1e12
+        rl = dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                  frac=achieved / PEAK_BF16_TFLOPS)
+    else:
+        achieved = b["bytes"] / (b["ms"] * 1e-3) / 1e9
+        rl = dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s", frac=achieved / PEAK_HBM_GBS)
+    rl["kernel"] = kernel_names.get(name, name)
+    rl["avg_launch_us"] = b["ms"] * 1e3
+    rl["traffic"] = traffic_for(name)
+    return name, rl
+
+
+def _source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "vision_transformer_encoder_block_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(op):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else null)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        t = json.load(open(path))
+    except ValueError:
+        return None
+    if t.get("source_digest") != _source_digest():
+        return None
+    entry = t.get("ops", {}).get(op)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def cpu_baseline(budget_s=12.0, max_images=32):
+    """The oracle (float64 NumPy), untuned, on ViT-S/16 @336 images until the budget is spent."""
+    import synth
+    from oracle import vit_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    cfg = synth.preset("vits16_336")
+    P = synth.make_params(cfg)
+    x = synth.make_images(cfg, max_images)
+    done, t0 = 0, time.perf_counter()
+    chunk = 2
+    while done < max_images and (time.perf_counter() - t0) < budget_s:
+        O.forward(x[done:done + chunk], P, cfg)
+        done += chunk
+    dt = time.perf_counter() - t0
+    return dict(value=done / dt, unit="images/s", cores=cores, kind="oracle",
+                sample=f"{done} ViT-S/16@336 images (float64 NumPy oracle, batches of {chunk}), {dt:.1f} s")
+
+
+KERNEL_NAMES = {
+    "qkv": "gemm_bf16_kernel<EpiQKV>",
+    "attention": "attention_kernel",
+    "out_proj": "gemm_bf16_kernel<EpiResidual> (out-proj)",
+    "fc1": "gemm_bf16_kernel<EpiGeluBf16>",
+    "fc2": "gemm_bf16_kernel<EpiResidual> (fc2)",
+    "layernorm": "layernorm_kernel<6,false>",
+}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-large", action="store_true", help="skip the ViT-L/16 @1024 b1 line")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the encoder path is single-GPU (images are independent, "
+              "so several GPUs would each run their own batch); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+
+    log("ViT-S/16 @336 b32 ...")
+    cfg, enc, small = bench_workload("vits16_336", 32, args.steps, args.warmup)
+    enc.close()
+    log(json.dumps(small))
+    large = None
+    if not args.no_large:
+        log("ViT-L/16 @1024 b1 ...")
+        cfg_l, enc_l, large = bench_workload("vitl16_1024", 1, args.steps, args.warmup)
+        enc_l.close()
+        log(json.dumps(large))
+    log("kernel breakdown ...")
+    bd = kernel_breakdown(cfg, 32)
+    for n, b in bd.items():
+        log(f"  {n:10s} {b['ms'] * 1e3:9.1f} us/launch  x{b['launches_per_step']:3d} = {b['ms_per_step']:.3f} ms/step")
+    dom, rl = roofline(bd, KERNEL_NAMES)
+    out = {
+        "metric": METRIC,
+        "value": small["images_per_s"],
+        "unit": "images/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": small["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) images, N(0,0.02) random-init weights)",
+        "config": {"workload": "ViT-S/16@336 b32 (DINOv3-style, 446 tokens, 4 registers, attention sink)",
+                   "global_batch": 32, "tokens": 446, "dim": 384, "depth": 12, "heads": 6},
+        "tflops": small["tflops"],
+        "pct_bf16_peak": 100 * small["frac_bf16_peak"],
+        "roofline": rl,
+        "kernels_ms_per_step": {n: round(b["ms_per_step"], 4) for n, b in bd.items()},
+    }
+    if large:
+        out["vitl16_1024_b1"] = {"images_per_s": large["images_per_s"], "ms_per_step": large["ms_per_step"],
+                                 "tflops": large["tflops"], "pct_bf16_peak": 100 * large["frac_bf16_peak"]}
+    if not args.no_cpu:
+        log("CPU oracle baseline ...")
+        out["cpu_baseline"] = cpu_baseline()
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

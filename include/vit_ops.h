@@ -1,0 +1,69 @@
+/*
+ * vit_ops.h - the individual kernels of the encoder block, exposed for
+ * per-operation checking and for callers composing their own blocks.
+ *
+ * Same conventions as vit.h: raw device pointers owned by the caller, fp32
+ * unless stated, bf16 = IEEE-754 binary32 truncated to its upper 16 bits
+ * (stored as uint16, produced by round-to-nearest-even), work enqueued on
+ * `stream` without synchronisation, 0 on success or a negative vit_status
+ * with a message in vit_last_error().
+ */
+#ifndef VIT_OPS_H
+#define VIT_OPS_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* LayerNorm over the last axis (LibreYOLO DINOv2 diagram, "Encoder block":
+ * LayerNorm eps 1e-6): y = (x - mean) / sqrt(var + eps) * g + b, biased var.
+ *   x [rows, dim] fp32; g, b [dim]; y [rows, dim], bf16 if out_fp32 == 0 else fp32.
+ *   dim must be a multiple of 64 and <= 4096. */
+int vit_op_layernorm(const float* x, int rows, int dim, const float* g, const float* b, float eps,
+                     void* y, int out_fp32, void* stream);
+
+/* Epilogues of vit_op_linear. */
+enum vit_epilogue {
+  VIT_EPI_BIAS_BF16 = 0,   /* c_bf16[m,n] = bf16(acc + bias[n]) */
+  VIT_EPI_GELU_BF16 = 1,   /* c_bf16[m,n] = bf16(GELU(acc + bias[n])), exact erf GELU */
+  VIT_EPI_RESIDUAL = 2,    /* c_f32[m,n] += ls[n] * (acc + bias[n])  (LayerScale + residual) */
+  VIT_EPI_BIAS_F32 = 3     /* c_f32[m,n] = acc + bias[n]  (bias may be NULL: 0) */
+};
+
+/* Linear layer acc = a @ w^T (torch.nn.Linear; LibreYOLO diagram "Encoder
+ * block" Linear D->Hm and Hm->D, "Encoder self-attention" Linear output).
+ *   a [M,K] bf16 row-major, w [N,K] bf16 row-major, bias [N] fp32,
+ *   ls [N] fp32 (RESIDUAL only), c [M,N] (bf16 or fp32 per epilogue).
+ *   K must be a multiple of 64; M, N >= 1. */
+int vit_op_linear(const void* a, const void* w, const float* bias, int M, int N, int K,
+                  int epilogue, const float* ls, void* c, void* stream);
+
+/* Fused Q/K/V projection with the head split of the attention kernel
+ * (LibreYOLO diagram, "Encoder self-attention": Linear Q/K/V, reshape heads).
+ *   h [batch*tokens, D] bf16 (LayerNorm output), wqkv [3D, D] bf16 (rows: the
+ *   D rows of wq, then wk, then wv), bqkv [3D] fp32, D = 64*heads.
+ * Outputs (bf16), with Nv = tokens rounded up to a multiple of 16:
+ *   q  [batch, heads, tokens, 64]  = (h wq^T + bq) * log2(e) / sqrt(64)
+ *   k  [batch, heads, tokens, 64]  = h wk^T + bk
+ *   vt [batch, heads, 64, Nv]      = (h wv^T + bv) transposed per head; token t
+ *        is stored at column t with bits 2 and 3 of t exchanged (so the eight
+ *        tokens one MFMA lane consumes are contiguous).  Columns >= tokens are
+ *        not written. */
+int vit_op_qkv(const void* h, const void* wqkv, const float* bqkv, int batch, int tokens,
+               int heads, void* q, void* k, void* vt, void* stream);
+
+/* Multi-head attention core, O = softmax(Q K^T / sqrt(64)) V per (batch, head)
+ * with the softmax over keys (LibreYOLO diagram, "Encoder self-attention";
+ * the logits stay fp32, model card "Build BF16, not FP16").
+ *   q, k, vt as produced by vit_op_qkv; o [batch, tokens, heads*64] bf16
+ *   (heads merged in channel order). */
+int vit_op_attention(const void* q, const void* k, const void* vt, int batch, int tokens, int heads,
+                     void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VIT_OPS_H */

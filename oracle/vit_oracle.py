@@ -149,6 +149,18 @@ def softmax_rows(s: np.ndarray) -> np.ndarray:
         return e / e.sum(axis=-1, keepdims=True)
 
 
+def sdpa(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, logit_format: str | None = None):
+    """One head: softmax over keys of scale * q k^T, times v; q [N, c], k [M, c], v [M, c'].
+
+    Returns (output [N, c'], max |logit|).  ``logit_format`` rounds the scaled
+    logits to a float format before the softmax (fp16 overflow demonstration).
+    """
+    s = (q @ k.T) * scale
+    smax = float(np.abs(s).max()) if s.size else 0.0
+    s = to_format(s, logit_format)
+    return softmax_rows(s) @ v, smax
+
+
 def attention(h: np.ndarray, blk: dict, heads: int, logit_format: str | None = None,
               stats: dict | None = None) -> np.ndarray:
     """Multi-head self-attention of the LayerNormed tokens ``h`` [B, N, D].
@@ -169,11 +181,8 @@ def attention(h: np.ndarray, blk: dict, heads: int, logit_format: str | None = N
     for bi in range(B):
         for j in range(heads):
             sl = slice(j * hd, (j + 1) * hd)
-            s = (q[bi, :, sl] @ k[bi, :, sl].T) * scale
-            if stats is not None:
-                smax = max(smax, float(np.abs(s).max()))
-            s = to_format(s, logit_format)
-            o[bi, :, sl] = softmax_rows(s) @ v[bi, :, sl]
+            o[bi, :, sl], m = sdpa(q[bi, :, sl], k[bi, :, sl], v[bi, :, sl], scale, logit_format)
+            smax = max(smax, m)
     if stats is not None:
         _track(stats, "logits", smax)
         _track(stats, "q", np.abs(q).max())
@@ -405,10 +414,13 @@ def scores_slide(image: np.ndarray, P: dict, cfg: dict, class_emb: np.ndarray) -
     C = class_emb.shape[0]
     probs = np.zeros((C, H, W), dtype=F64)
     counts = np.zeros((H, W), dtype=F64)
+    cos_all = []
     for wi, (y, c) in enumerate(wins):
         cos = cosine_maps(feats[wi], class_emb)
+        cos_all.append(cos)
         up = bilinear_resize(cos, side, side)
         probs[:, y:y + side, c:c + side] += softmax_rows(up.transpose(1, 2, 0)).transpose(2, 0, 1)
         counts[y:y + side, c:c + side] += 1.0
     probs /= counts
-    return {"probs": probs, "counts": counts, "labels": probs.argmax(axis=0), "windows": wins}
+    return {"probs": probs, "counts": counts, "labels": probs.argmax(axis=0), "windows": wins,
+            "cos": np.stack(cos_all)}

@@ -1,0 +1,50 @@
+"""Helpers shared by the GPU parity tests (marshalling only, no arithmetic of the method)."""
+
+import sys
+
+import numpy as np
+import torch
+
+import vision_transformer_encoder_block_amd as vit
+
+
+def require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    vit.lib()  # raises LibraryMissing: no fallback exists
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_dev(a: np.ndarray):
+    """Round to bf16 (nearest even) on the host and move to the GPU; also return the rounded values."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.cuda(), t.to(torch.float64).numpy()
+
+
+def f32_dev(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def host(t) -> np.ndarray:
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy().astype(np.float64)
+
+
+def bf16_view(t_uint8_or_bf16, shape):
+    return t_uint8_or_bf16.view(torch.bfloat16).reshape(shape)
+
+
+def vt_position(t: np.ndarray) -> np.ndarray:
+    """Column of token t in the vt layout: bits 2 and 3 exchanged (documented in vit_ops.h)."""
+    return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1)
+
+
+def cosine(a, b):
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))

@@ -1,0 +1,163 @@
+"""Per-kernel parity: each C-ABI op on the GPU against the oracle on identical
+(bf16-rounded) inputs, at sizes spanning several tiles with ragged tails.
+
+Tolerances follow from the arithmetic (see the design notes): products of two
+bf16 values are exact in fp32, so a K-term fp32 sum is within
+K * 2^-24 * sum|a_k w_k| of the exact value; a bf16 output adds half an ulp,
+2^-9 |y|; the attention probabilities are rounded to bf16 (2^-9 relative) before
+the P.V product.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import vision_transformer_encoder_block_amd as vit
+from oracle import vit_oracle as O
+from tests.gpu_util import bf16_dev, f32_dev, host, require_gpu, say, vt_position
+
+pytestmark = pytest.mark.gpu
+RNG = np.random.default_rng(2024)
+U24 = 2.0 ** -24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+# ------------------------------------------------------------------ LayerNorm
+
+@pytest.mark.parametrize("rows,dim", [(1, 64), (7, 384), (446, 384), (1001, 1024), (33, 768)])
+@pytest.mark.parametrize("out_fp32", [0, 1])
+def test_layernorm(rows, dim, out_fp32):
+    say(f"layernorm rows={rows} dim={dim} fp32={out_fp32}")
+    x = RNG.standard_normal((rows, dim)).astype(np.float32) * 2 + 0.3
+    g = (1 + 0.02 * RNG.standard_normal(dim)).astype(np.float32)
+    b = (0.02 * RNG.standard_normal(dim)).astype(np.float32)
+    y = torch.empty((rows, dim), dtype=torch.float32 if out_fp32 else torch.bfloat16, device="cuda")
+    vit.vit_op_layernorm(f32_dev(x), rows, dim, f32_dev(g), f32_dev(b), 1e-6, y, out_fp32)
+    got = host(y)
+    ref = O.layer_norm(x.astype(np.float64), g, b, 1e-6)
+    tol = (2.0 ** -8 * np.abs(ref) if not out_fp32 else 0) + 2e-5 * (1 + np.abs(ref))
+    assert np.all(np.abs(got - ref) <= tol), np.abs(got - ref).max()
+
+
+# ------------------------------------------------------------------ GEMM epilogues
+
+SHAPES = [(1, 64, 64), (5, 150, 384), (130, 384, 384), (446, 1152, 384), (1000, 1536, 384), (257, 384, 1536),
+          (4101, 1024, 128), (300, 96, 768)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("epi", [vit.EPI_BIAS_BF16, vit.EPI_GELU_BF16, vit.EPI_RESIDUAL, vit.EPI_BIAS_F32])
+def test_linear(M, N, K, epi):
+    say(f"linear M={M} N={N} K={K} epi={epi}")
+    a_d, a = bf16_dev(RNG.standard_normal((M, K)) * 0.7)
+    w_d, w = bf16_dev(RNG.standard_normal((N, K)) * 0.05)
+    bias = (0.1 * RNG.standard_normal(N)).astype(np.float32)
+    ls = (0.5 + RNG.standard_normal(N)).astype(np.float32)
+    z = O.linear(a, w, bias)
+    s_abs = np.abs(a) @ np.abs(w).T
+    acc_err = K * U24 * s_abs + 1e-7
+    if epi == vit.EPI_BIAS_BF16:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ref, tol = z, 2.0 ** -8 * np.abs(z) + acc_err
+    elif epi == vit.EPI_GELU_BF16:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ref = O.gelu(z)
+        tol = 2.0 ** -8 * np.abs(ref) + 1.13 * acc_err + 2e-6
+    elif epi == vit.EPI_RESIDUAL:
+        r0 = RNG.standard_normal((M, N)).astype(np.float32)
+        out = f32_dev(r0)
+        ref = r0 + ls * z
+        tol = np.abs(ls) * acc_err + 4 * U24 * (np.abs(r0) + np.abs(ls * z))
+    else:
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        ref, tol = z, acc_err + 2 * U24 * np.abs(z)
+    vit.vit_op_linear(a_d, w_d, f32_dev(bias), M, N, K, epi, f32_dev(ls), out)
+    got = host(out)
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), (np.argwhere(bad)[:5], np.abs(got - ref).max())
+
+
+# ------------------------------------------------------------------ QKV head split
+
+@pytest.mark.parametrize("batch,tokens,heads", [(1, 5, 1), (2, 201, 6), (1, 446, 6), (3, 70, 2)])
+def test_qkv_split(batch, tokens, heads):
+    say(f"qkv batch={batch} tokens={tokens} heads={heads}")
+    D = 64 * heads
+    M = batch * tokens
+    h_d, h = bf16_dev(RNG.standard_normal((M, D)))
+    w_d, w = bf16_dev(RNG.standard_normal((3 * D, D)) * 0.05)
+    bias = (0.1 * RNG.standard_normal(3 * D)).astype(np.float32)
+    nv = (tokens + 15) // 16 * 16
+    q = torch.empty((batch, heads, tokens, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty_like(q)
+    vt = torch.zeros((batch, heads, 64, nv), dtype=torch.bfloat16, device="cuda")
+    vit.vit_op_qkv(h_d, w_d, f32_dev(bias), batch, tokens, heads, q, k, vt)
+    z = O.linear(h, w, bias).reshape(batch, tokens, 3, heads, 64)
+    acc = (3 * D) * U24 * (np.abs(h) @ np.abs(w).T).reshape(batch, tokens, 3, heads, 64) + 1e-7
+    c = math.log2(math.e) / 8.0
+    ref_q = z[:, :, 0].transpose(0, 2, 1, 3) * c
+    ref_k = z[:, :, 1].transpose(0, 2, 1, 3)
+    ref_v = z[:, :, 2].transpose(0, 2, 3, 1)          # [b, h, d, t]
+    gq, gk, gv = host(q), host(k), host(vt)
+    assert np.all(np.abs(gq - ref_q) <= 2 ** -8 * np.abs(ref_q) + c * acc[:, :, 0].transpose(0, 2, 1, 3) + 1e-7)
+    assert np.all(np.abs(gk - ref_k) <= 2 ** -8 * np.abs(ref_k) + acc[:, :, 1].transpose(0, 2, 1, 3))
+    cols = vt_position(np.arange(tokens))
+    gv_t = gv[:, :, :, cols]
+    assert np.all(np.abs(gv_t - ref_v) <= 2 ** -8 * np.abs(ref_v) + acc[:, :, 2].transpose(0, 2, 3, 1))
+    untouched = np.setdiff1d(np.arange(nv), cols)
+    assert np.all(gv[:, :, :, untouched] == 0)
+
+
+# ------------------------------------------------------------------ attention core
+
+def _attention_case(batch, tokens, heads, q_scale=1.0, k_spike=None):
+    nv = (tokens + 15) // 16 * 16
+    qr = RNG.standard_normal((batch, heads, tokens, 64)) * q_scale
+    kr = RNG.standard_normal((batch, heads, tokens, 64))
+    vr = RNG.standard_normal((batch, heads, tokens, 64))
+    if k_spike is not None:  # every query ~ q_scale * e and one key = 8 e: a huge logit
+        e = RNG.choice([-1.0, 1.0], size=64)
+        qr = q_scale * (e + 0.05 * RNG.standard_normal((batch, heads, tokens, 64)))
+        kr[:, :, k_spike] = 8.0 * e
+    q_d, q = bf16_dev(qr)
+    k_d, k = bf16_dev(kr)
+    v_d, v = bf16_dev(vr)
+    vt = torch.zeros((batch, heads, 64, nv), dtype=torch.bfloat16, device="cuda")
+    vt[:, :, :, torch.from_numpy(vt_position(np.arange(tokens))).cuda()] = v_d.transpose(2, 3)
+    o = torch.empty((batch, tokens, heads * 64), dtype=torch.bfloat16, device="cuda")
+    vit.vit_op_attention(q_d, k_d, vt, batch, tokens, heads, o)
+    got = host(o).reshape(batch, tokens, heads, 64)
+    return q, k, v, got
+
+
+@pytest.mark.parametrize("batch,tokens,heads", [(1, 1, 1), (1, 5, 1), (2, 31, 2), (1, 64, 1), (1, 65, 3),
+                                                (2, 127, 1), (1, 129, 2), (2, 201, 6), (1, 446, 6), (1, 1370, 2)])
+def test_attention_matches_oracle(batch, tokens, heads):
+    say(f"attention batch={batch} tokens={tokens} heads={heads}")
+    q, k, v, got = _attention_case(batch, tokens, heads)
+    # q is given pre-multiplied by log2(e)/8: softmax_2(q k^T) = softmax_e(ln2 * q k^T)
+    for b in range(batch):
+        for h in range(heads):
+            ref, _ = O.sdpa(q[b, h], k[b, h], v[b, h], math.log(2.0))
+            vmax = np.abs(v[b, h]).max()
+            err = np.abs(got[b, :, h] - ref)
+            assert np.all(err <= 2 ** -8 * np.abs(ref) + 2 ** -7 * vmax), (b, h, err.max())
+
+
+def test_attention_large_logits_stay_finite():
+    # spike logit ~ 64 * 5000 * 8 * ln2 = 1.8e6, far beyond fp16's 65504; it wins every row
+    say("attention large logits")
+    q, k, v, got = _attention_case(1, 200, 2, q_scale=5000.0, k_spike=3)
+    assert np.isfinite(got).all()
+    for h in range(2):
+        ref, smax = O.sdpa(q[0, h], k[0, h], v[0, h], math.log(2.0))
+        assert smax > 1e6
+        np.testing.assert_array_equal(ref, np.broadcast_to(v[0, h, 3], ref.shape))
+        np.testing.assert_allclose(got[0, :, h], ref, atol=2 ** -8 * np.abs(ref).max() + 1e-6)

@@ -263,3 +263,14 @@ def test_slide_windows_count_and_coverage():
         cover[y:y + 384, x:x + 384] += 1
     assert cover.min() >= 1 and cover.max() <= 6
     assert O.slide_windows(384, 384, 384, 192) == [(0, 0)]
+
+
+def test_sdpa_matches_torch_with_scale():
+    q = RNG.standard_normal((13, 64))
+    k = RNG.standard_normal((21, 64))
+    v = RNG.standard_normal((21, 64))
+    for scale in (0.125, math.log(2.0)):
+        got, smax = O.sdpa(q, k, v, scale)
+        ref = F.scaled_dot_product_attention(t64(q)[None], t64(k)[None], t64(v)[None], scale=scale)[0].numpy()
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+        assert smax == pytest.approx(np.abs(q @ k.T).max() * scale)

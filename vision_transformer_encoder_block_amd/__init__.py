@@ -1,0 +1,284 @@
+"""Python binding of libvit, the MI355X (gfx950) ViT encoder forward pass.
+
+The C ABI (``include/vit.h``, ``include/vit_ops.h``) does all the work; this
+module only marshals arguments: it loads ``libvit.so`` with ctypes, mirrors the
+C structs, packs a parameter dictionary into the documented fp32 blob order, and
+passes torch device pointers and the current HIP stream.  PyTorch supplies the
+device memory and the stream; no step of the encoder runs in Python or torch.
+
+Importing this module never touches the GPU.  Calling into the library needs
+the built ``libvit.so`` (``python -m vision_transformer_encoder_block_amd.build``)
+and raises ``LibraryMissing`` otherwise: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "LibraryMissing", "VitError", "VitConfig", "VitSizes", "lib", "config_from_dict", "pack_params",
+    "vit_config_preset", "vit_plan", "vit_create", "vit_forward", "vit_descriptor", "vit_patch_scores",
+    "vit_destroy", "vit_last_error", "vit_op_layernorm", "vit_op_linear", "vit_op_qkv", "vit_op_attention",
+    "Encoder", "EPI_BIAS_BF16", "EPI_GELU_BF16", "EPI_RESIDUAL", "EPI_BIAS_F32",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvit.so")
+
+EPI_BIAS_BF16, EPI_GELU_BF16, EPI_RESIDUAL, EPI_BIAS_F32 = 0, 1, 2, 3
+STATUS = {0: "VIT_OK", -1: "VIT_ERR_ARG", -2: "VIT_ERR_SHAPE", -3: "VIT_ERR_SIZE", -4: "VIT_ERR_HIP",
+          -5: "VIT_ERR_UNSUPPORTED"}
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class VitError(RuntimeError):
+    def __init__(self, func, code, msg):
+        super().__init__(f"{func} -> {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class VitConfig(ctypes.Structure):
+    _fields_ = [
+        ("img_h", ctypes.c_int), ("img_w", ctypes.c_int), ("patch", ctypes.c_int), ("dim", ctypes.c_int),
+        ("depth", ctypes.c_int), ("extra_blocks", ctypes.c_int), ("heads", ctypes.c_int),
+        ("mlp_hidden", ctypes.c_int), ("registers", ctypes.c_int), ("max_batch", ctypes.c_int),
+        ("ln_eps", ctypes.c_float), ("tap_mask", ctypes.c_uint), ("pos_grid_h", ctypes.c_int),
+        ("pos_grid_w", ctypes.c_int), ("window", ctypes.c_int), ("window_stride", ctypes.c_int),
+        ("max_classes", ctypes.c_int),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class VitSizes(ctypes.Structure):
+    _fields_ = [
+        ("weight_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t), ("host_floats", ctypes.c_size_t),
+        ("tokens", ctypes.c_int), ("window_tokens", ctypes.c_int), ("windows", ctypes.c_int), ("taps", ctypes.c_int),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+_SIGNATURES = {
+    "vit_last_error": (ctypes.c_char_p, []),
+    "vit_config_preset": (_I, [_I, ctypes.POINTER(VitConfig)]),
+    "vit_plan": (_I, [ctypes.POINTER(VitConfig), ctypes.POINTER(VitSizes)]),
+    "vit_create": (_I, [ctypes.POINTER(VitConfig), _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P,
+                        ctypes.POINTER(_P)]),
+    "vit_forward": (_I, [_P, _P, _I, _P, _P, _P]),
+    "vit_descriptor": (_I, [_P, _P, _I, _P, _P]),
+    "vit_patch_scores": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _P]),
+    "vit_destroy": (_I, [_P]),
+    "vit_op_layernorm": (_I, [_P, _I, _I, _P, _P, ctypes.c_float, _P, _I, _P]),
+    "vit_op_linear": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "vit_op_qkv": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
+    "vit_op_attention": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
+}
+
+
+def lib():
+    """The loaded libvit (raises LibraryMissing if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryMissing(f"{LIB_PATH} not built; run python -m vision_transformer_encoder_block_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def vit_last_error() -> str:
+    return lib().vit_last_error().decode()
+
+
+def _check(name, code):
+    if code != 0:
+        raise VitError(name, code, vit_last_error())
+    return code
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ------------------------------------------------------------------ C ABI, same names
+
+def vit_config_preset(cfg_id: int) -> VitConfig:
+    c = VitConfig()
+    _check("vit_config_preset", lib().vit_config_preset(cfg_id, ctypes.byref(c)))
+    return c
+
+
+def vit_plan(cfg: VitConfig) -> VitSizes:
+    s = VitSizes()
+    _check("vit_plan", lib().vit_plan(ctypes.byref(cfg), ctypes.byref(s)))
+    return s
+
+
+def vit_create(cfg: VitConfig, blob: np.ndarray, d_weights, d_workspace, stream=None):
+    blob = np.ascontiguousarray(blob, dtype=np.float32)
+    handle = ctypes.c_void_p()
+    _check("vit_create", lib().vit_create(
+        ctypes.byref(cfg), blob.ctypes.data_as(ctypes.c_void_p), blob.size, _ptr(d_weights),
+        d_weights.numel() * d_weights.element_size(), _ptr(d_workspace),
+        d_workspace.numel() * d_workspace.element_size(), _stream(stream), ctypes.byref(handle)))
+    return handle
+
+
+def vit_forward(handle, d_images, batch, d_tokens, d_taps=None, stream=None):
+    return _check("vit_forward", lib().vit_forward(handle, _ptr(d_images), batch, _ptr(d_tokens), _ptr(d_taps),
+                                                   _stream(stream)))
+
+
+def vit_descriptor(handle, d_tokens, batch, d_desc, stream=None):
+    return _check("vit_descriptor", lib().vit_descriptor(handle, _ptr(d_tokens), batch, _ptr(d_desc),
+                                                         _stream(stream)))
+
+
+def vit_patch_scores(handle, d_image, d_class_emb, classes, mode, d_labels, d_cos=None, d_dense=None, stream=None):
+    return _check("vit_patch_scores", lib().vit_patch_scores(
+        handle, _ptr(d_image), _ptr(d_class_emb), classes, mode, _ptr(d_labels), _ptr(d_cos), _ptr(d_dense),
+        _stream(stream)))
+
+
+def vit_destroy(handle):
+    return _check("vit_destroy", lib().vit_destroy(handle))
+
+
+def vit_op_layernorm(x, rows, dim, g, b, eps, y, out_fp32, stream=None):
+    return _check("vit_op_layernorm", lib().vit_op_layernorm(_ptr(x), rows, dim, _ptr(g), _ptr(b), eps, _ptr(y),
+                                                             int(out_fp32), _stream(stream)))
+
+
+def vit_op_linear(a, w, bias, M, N, K, epilogue, ls, c, stream=None):
+    return _check("vit_op_linear", lib().vit_op_linear(_ptr(a), _ptr(w), _ptr(bias), M, N, K, epilogue, _ptr(ls),
+                                                       _ptr(c), _stream(stream)))
+
+
+def vit_op_qkv(h, wqkv, bqkv, batch, tokens, heads, q, k, vt, stream=None):
+    return _check("vit_op_qkv", lib().vit_op_qkv(_ptr(h), _ptr(wqkv), _ptr(bqkv), batch, tokens, heads, _ptr(q),
+                                                 _ptr(k), _ptr(vt), _stream(stream)))
+
+
+def vit_op_attention(q, k, vt, batch, tokens, heads, o, stream=None):
+    return _check("vit_op_attention", lib().vit_op_attention(_ptr(q), _ptr(k), _ptr(vt), batch, tokens, heads,
+                                                             _ptr(o), _stream(stream)))
+
+
+# ------------------------------------------------------------------ marshalling helpers
+
+def config_from_dict(cfg: dict, max_batch: int | None = None) -> VitConfig:
+    """A VitConfig from a workload dictionary (keys as in the seeded-input presets)."""
+    gh, gw = cfg.get("pos_grid") or (cfg["img_h"] // cfg["patch"], cfg["img_w"] // cfg["patch"])
+    mask = 0
+    for t in cfg.get("taps", ()):
+        mask |= 1 << (t - 1)
+    mb = max_batch if max_batch is not None else max(cfg.get("batches", (1,)))
+    return VitConfig(cfg["img_h"], cfg["img_w"], cfg["patch"], cfg["dim"], cfg["depth"], cfg.get("extra_blocks", 0),
+                     cfg["heads"], cfg["mlp_hidden"], cfg["registers"], mb, cfg["ln_eps"], mask, gh, gw,
+                     cfg.get("window", 0), cfg.get("window_stride", 0), cfg.get("classes", 0))
+
+
+_BLOCK_ORDER = ("ln1_g", "ln1_b", "wq", "bq", "wk", "bk", "wv", "bv", "wo", "bo", "ls1", "ln2_g", "ln2_b",
+                "w1", "b1", "w2", "b2", "ls2")
+
+
+def pack_params(P: dict) -> np.ndarray:
+    """Concatenate a parameter dictionary into the fp32 blob order of vit_create."""
+    parts = [P["patch_w"], P["patch_b"], P["cls"], P["reg"], P["pos"]]
+    for b in P["blocks"]:
+        parts.extend(b[k] for k in _BLOCK_ORDER)
+    parts.extend([P["norm_g"], P["norm_b"]])
+    return np.concatenate([np.ascontiguousarray(a, dtype=np.float32).ravel() for a in parts])
+
+
+class Encoder:
+    """A created model with torch-owned weight and workspace buffers on one device."""
+
+    def __init__(self, cfg: dict | VitConfig, params: dict | np.ndarray, max_batch: int | None = None,
+                 device: str = "cuda", stream=None):
+        import torch
+        self.cfg = cfg if isinstance(cfg, VitConfig) else config_from_dict(cfg, max_batch)
+        self.sizes = vit_plan(self.cfg)
+        blob = params if isinstance(params, np.ndarray) else pack_params(params)
+        self.device = torch.device(device)
+        self.weights = torch.empty(self.sizes.weight_bytes, dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(self.sizes.workspace_bytes, dtype=torch.uint8, device=self.device)
+        self.handle = vit_create(self.cfg, blob, self.weights, self.workspace, stream)
+
+    @property
+    def tokens(self) -> int:
+        return self.sizes.tokens
+
+    def forward(self, images, with_taps: bool = False, tokens_out=None, taps_out=None, stream=None):
+        import torch
+        B = images.shape[0]
+        c = self.cfg
+        if tokens_out is None:
+            tokens_out = torch.empty((B, self.sizes.tokens, c.dim), dtype=torch.float32, device=self.device)
+        if with_taps and taps_out is None:
+            taps_out = torch.empty((B, self.sizes.taps, c.dim, c.img_h // c.patch, c.img_w // c.patch),
+                                   dtype=torch.float32, device=self.device)
+        vit_forward(self.handle, images, B, tokens_out, taps_out if with_taps else None, stream)
+        return (tokens_out, taps_out) if with_taps else tokens_out
+
+    def descriptor(self, tokens, desc_out=None, stream=None):
+        import torch
+        B = tokens.shape[0]
+        if desc_out is None:
+            desc_out = torch.empty((B, self.cfg.dim), dtype=torch.float32, device=self.device)
+        vit_descriptor(self.handle, tokens, B, desc_out, stream)
+        return desc_out
+
+    def patch_scores(self, image, class_emb, mode: int, want_cos: bool = False, want_dense: bool = False,
+                     stream=None):
+        import torch
+        c = self.cfg
+        C = class_emb.shape[0]
+        labels = torch.empty((c.img_h, c.img_w), dtype=torch.int32, device=self.device)
+        cos = dense = None
+        p = c.patch
+        if want_cos:
+            if mode == 0:
+                cos = torch.empty((C, c.img_h // p, c.img_w // p), dtype=torch.float32, device=self.device)
+            else:
+                g = c.window // p
+                cos = torch.empty((self.sizes.windows, C, g, g), dtype=torch.float32, device=self.device)
+        if want_dense:
+            dense = torch.empty((C, c.img_h, c.img_w), dtype=torch.float32, device=self.device)
+        vit_patch_scores(self.handle, image, class_emb, C, mode, labels, cos, dense, stream)
+        return labels, cos, dense
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            vit_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

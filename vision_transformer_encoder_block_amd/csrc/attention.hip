@@ -1,0 +1,208 @@
+// Fused multi-head attention for gfx950, head size 64:
+//   O = softmax_keys(Q K^T / sqrt(64)) V   per (image, head)
+// computed flash-style without storing the N x N logits.
+//
+// Each wave owns 32 queries.  It computes the TRANSPOSED logits S^T = K Q^T
+// with v_mfma_f32_32x32x16_bf16 (keys on the MFMA rows, queries on the
+// columns), so every lane holds 32 logits of ONE query: the per-query running
+// max and sum are lane-local plus one exchange with the partner lane (lane ^
+// 32) that holds the other keys of the same query.  The probabilities then
+// feed O^T = V^T P^T straight from the accumulator registers (no LDS round
+// trip): the key order inside each 16-key MFMA step is the accumulator's
+// order, and V^T is stored with bits 2 and 3 of the token index exchanged so
+// that the eight keys one lane needs are 16 contiguous bytes.
+//
+// Q arrives pre-multiplied by log2(e)/8, so p = exp2(s - m) with s, m, the
+// running max and sum all fp32: logits of ~2.5e6 (the DINOv3 attention sink)
+// stay finite, and the largest key of every row gets p = exp2(0) = 1 exactly.
+// K and V^T tiles of 64 keys are staged in LDS (double-buffered, 16-byte
+// chunks XOR-swizzled by row) and shared by the 4 waves of a workgroup.
+#include "common.h"
+#include "kernels.h"
+
+namespace vit {
+namespace {
+
+constexpr int QT = 128;  // queries per workgroup (4 waves x 32)
+constexpr int KT = 64;   // keys per tile
+
+// Inverse of the token permutation used by vt (an involution).
+__device__ __forceinline__ int vt_tok(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+__global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
+                                                        const bf16_t* __restrict__ Vt, bf16_t* __restrict__ O,
+                                                        int N, int H, int nv) {
+  __shared__ uint4 Ks[2][KT * 8];
+  __shared__ uint4 Vs[2][64 * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const size_t bh = (size_t)b * H + h;
+  const bf16_t* Qp = Q + bh * N * 64;
+  const bf16_t* Kp = K + bh * N * 64;
+  const bf16_t* Vp = Vt + bh * 64 * nv;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int qrow = blockIdx.x * QT + wave * 32 + lrow;
+
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  bf16x8 qf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 u = zero;
+    if (qrow < N) u = *reinterpret_cast<const uint4*>(Qp + (size_t)qrow * 64 + ks * 16 + lhalf * 8);
+    qf[ks] = as_bf16x8(u);
+  }
+
+  // cooperative tile loads: 512 chunks of K and 512 of V^T, 2 + 2 per thread
+  int k_row[2], k_q[2], k_dst[2], v_row[2], v_q[2], v_dst[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int cid = tid + c * 256;
+    k_row[c] = cid >> 3;
+    k_q[c] = cid & 7;
+    k_dst[c] = k_row[c] * 8 + (k_q[c] ^ (k_row[c] & 7));
+    v_row[c] = cid >> 3;  // channel d
+    v_q[c] = cid & 7;     // 8 stored token positions
+    v_dst[c] = v_row[c] * 8 + (v_q[c] ^ (v_row[c] & 7));
+  }
+  auto load_tile = [&](int t, uint4* rk, uint4* rv) {
+    const int k0 = t * KT;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int key = k0 + k_row[c];
+      rk[c] = key < N ? *reinterpret_cast<const uint4*>(Kp + (size_t)key * 64 + k_q[c] * 8) : zero;
+      const int p0 = k0 + v_q[c] * 8;
+      uint4 u = zero;
+      if (p0 < nv) u = *reinterpret_cast<const uint4*>(Vp + (size_t)v_row[c] * nv + p0);
+      if (k0 + KT > N) {  // last tile: zero the positions of keys >= N
+        uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (vt_tok(p0 + e) >= N) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        u = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      rv[c] = u;
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[2];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = 0.f;
+
+  const int ntiles = (N + KT - 1) / KT;
+  uint4 rk[2], rv[2];
+  load_tile(0, rk, rv);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    Ks[0][k_dst[c]] = rk[c];
+    Vs[0][v_dst[c]] = rv[c];
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1, rk, rv);
+
+    // S^T for keys t*64 + kb*32 + [0, 32): element e <-> key 8*(e/4) + 4*lhalf + e%4
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+      const int r = kb * 32 + lrow;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int qd = ks * 2 + lhalf;
+        s[kb] = mfma32x32x16(as_bf16x8(Ks[cur][r * 8 + (qd ^ (r & 7))]), qf[ks], s[kb]);
+      }
+    }
+    if ((t + 1) * KT > N) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = t * KT + kb * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
+          if (key >= N) s[kb][e] = -INFINITY;
+        }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);  // finite: tile 0 always holds key 0
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      o[0][e] *= alpha;
+      o[1][e] *= alpha;
+    }
+    // probabilities, packed as the B operand of the 4 key steps of P V
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = exp2f(s[kb][half * 8 + e] - m_new);
+          l_run += p[e];
+        }
+        uint4 u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                             pack_bf16x2(p[6], p[7]));
+        pf[kb * 2 + half] = as_bf16x8(u);
+      }
+    }
+    // O^T[d, q] += V^T[d, keys] P^T[keys, q]; d = db*32 + row of the MFMA
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int r = db * 32 + lrow;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int qd = ks * 2 + lhalf;
+        o[db] = mfma32x32x16(as_bf16x8(Vs[cur][r * 8 + (qd ^ (r & 7))]), pf[ks], o[db]);
+      }
+    }
+
+    if (t + 1 < ntiles) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        Ks[cur ^ 1][k_dst[c]] = rk[c];
+        Vs[cur ^ 1][v_dst[c]] = rv[c];
+      }
+    }
+    __syncthreads();
+  }
+
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l;
+  if (qrow < N) {
+    bf16_t* op = O + ((size_t)b * N + qrow) * (size_t)(H * 64) + h * 64;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = db * 32 + i * 8 + lhalf * 4;
+        uint2 u = make_uint2(pack_bf16x2(o[db][i * 4 + 0] * inv, o[db][i * 4 + 1] * inv),
+                             pack_bf16x2(o[db][i * 4 + 2] * inv, o[db][i * 4 + 3] * inv));
+        *reinterpret_cast<uint2*>(op + d) = u;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
+                            int heads, int nv, uint16_t* o, hipStream_t s) {
+  if (batch <= 0 || tokens <= 0 || heads <= 0 || nv < tokens || nv % 16 != 0) return hipErrorInvalidValue;
+  dim3 grid((tokens + QT - 1) / QT, heads, batch);
+  hipLaunchKernelGGL(attention_kernel, grid, dim3(256), 0, s, q, k, vt, o, tokens, heads, nv);
+  return hipGetLastError();
+}
+
+}  // namespace vit

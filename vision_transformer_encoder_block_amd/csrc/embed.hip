@@ -1,0 +1,147 @@
+// Input side of the encoder on gfx950: im2col of the fp32 images into the
+// bf16 patch matrix (the A operand of the patch-embedding GEMM), CLS/register
+// rows of the token sequence, bicubic resampling of the position table, the
+// slide-mode window crops and a plain fp32 -> bf16 conversion.
+#include "common.h"
+#include "kernels.h"
+
+namespace vit {
+namespace {
+
+// One thread writes 8 consecutive columns (16 bytes) of one patch row.
+__global__ __launch_bounds__(256) void patchify_kernel(const float* __restrict__ img, int batch, int H, int W, int p,
+                                                       int kpad, bf16_t* __restrict__ out) {
+  const int gw = W / p, gh = H / p;
+  const int chunks = kpad / 8;
+  const size_t total = (size_t)batch * gh * gw * chunks;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int ch = (int)(idx % chunks);
+  const size_t prow = idx / chunks;
+  const int gx = (int)(prow % gw);
+  const int gy = (int)((prow / gw) % gh);
+  const int b = (int)(prow / ((size_t)gw * gh));
+  const int kvalid = 3 * p * p;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = ch * 8 + e;
+    float x = 0.f;
+    if (k < kvalid) {
+      const int c = k / (p * p);
+      const int r = k - c * p * p;
+      const int ky = r / p, kx = r - ky * p;
+      x = img[(((size_t)b * 3 + c) * H + gy * p + ky) * W + gx * p + kx];
+    }
+    v[e] = x;
+  }
+  uint4 u = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7]));
+  *reinterpret_cast<uint4*>(out + prow * kpad + ch * 8) = u;
+}
+
+__global__ __launch_bounds__(256) void assemble_kernel(float* __restrict__ x, int tokens, int dim,
+                                                       const float* __restrict__ cls, const float* __restrict__ pos0,
+                                                       const float* __restrict__ reg, int regs) {
+  const int b = blockIdx.y;
+  const int r = blockIdx.x;  // 0 = CLS, 1..regs = registers
+  float* row = x + ((size_t)b * tokens + r) * dim;
+  for (int c = threadIdx.x; c < dim; c += blockDim.x)
+    row[c] = r == 0 ? cls[c] + pos0[c] : reg[(size_t)(r - 1) * dim + c];
+}
+
+// Cubic-convolution weight (a = -0.75) of a tap at distance d.
+__device__ __forceinline__ float cubic_w(float d) {
+  const float a = -0.75f;
+  d = fabsf(d);
+  if (d <= 1.f) return ((a + 2.f) * d - (a + 3.f)) * d * d + 1.f;
+  if (d < 2.f) return ((a * d - 5.f * a) * d + 8.f * a) * d - 4.f * a;
+  return 0.f;
+}
+
+// One thread per (output row, channel); 4 x 4 taps with edge clamping.
+__global__ __launch_bounds__(256) void pos_resample_kernel(const float* __restrict__ in, int gh, int gw,
+                                                           float* __restrict__ out, int th, int tw, int dim) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t total = (size_t)(1 + th * tw) * dim;
+  if (idx >= total) return;
+  const int c = (int)(idx % dim);
+  const int row = (int)(idx / dim);
+  if (row == 0) {
+    out[c] = in[c];
+    return;
+  }
+  const int oy = (row - 1) / tw, ox = (row - 1) % tw;
+  const float sy = (oy + 0.5f) * ((float)gh / th) - 0.5f;
+  const float sx = (ox + 0.5f) * ((float)gw / tw) - 0.5f;
+  const int y0 = (int)floorf(sy), x0 = (int)floorf(sx);
+  float acc = 0.f;
+  for (int ty = -1; ty <= 2; ++ty) {
+    const float wy = cubic_w(sy - (float)(y0 + ty));
+    const int yy = min(max(y0 + ty, 0), gh - 1);
+    float racc = 0.f;
+    for (int tx = -1; tx <= 2; ++tx) {
+      const float wx = cubic_w(sx - (float)(x0 + tx));
+      const int xx = min(max(x0 + tx, 0), gw - 1);
+      racc += wx * in[(size_t)(1 + yy * gw + xx) * dim + c];
+    }
+    acc += wy * racc;
+  }
+  out[(size_t)row * dim + c] = acc;
+}
+
+__global__ __launch_bounds__(256) void crops_kernel(const float* __restrict__ img, int H, int W,
+                                                    const int* __restrict__ corners, int side,
+                                                    float* __restrict__ out) {
+  const int w = blockIdx.z;
+  const int c = blockIdx.y;
+  const int y0 = corners[2 * w], x0 = corners[2 * w + 1];
+  const size_t n = (size_t)side * side;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int yy = (int)(i / side), xx = (int)(i % side);
+    out[(((size_t)w * 3 + c) * side + yy) * side + xx] = img[((size_t)c * H + y0 + yy) * W + x0 + xx];
+  }
+}
+
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ x, size_t n, bf16_t* __restrict__ y) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = f2bf(x[i]);
+}
+
+}  // namespace
+
+hipError_t launch_patchify(const float* img, int batch, int H, int W, int p, int kpad, uint16_t* out,
+                           hipStream_t s) {
+  if (kpad % 8 != 0 || kpad < 3 * p * p) return hipErrorInvalidValue;
+  const size_t total = (size_t)batch * (H / p) * (W / p) * (kpad / 8);
+  hipLaunchKernelGGL(patchify_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, img, batch, H, W, p,
+                     kpad, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_assemble(float* x, int batch, int tokens, int dim, const float* cls, const float* pos0,
+                           const float* reg, int regs, hipStream_t s) {
+  hipLaunchKernelGGL(assemble_kernel, dim3(1 + regs, batch), dim3(256), 0, s, x, tokens, dim, cls, pos0, reg, regs);
+  return hipGetLastError();
+}
+
+hipError_t launch_pos_resample(const float* pos_in, int gh, int gw, float* pos_out, int th, int tw, int dim,
+                               hipStream_t s) {
+  const size_t total = (size_t)(1 + th * tw) * dim;
+  hipLaunchKernelGGL(pos_resample_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, pos_in, gh, gw,
+                     pos_out, th, tw, dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_crops(const float* img, int H, int W, const int* corners_dev, int nwin, int side, float* out,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(crops_kernel, dim3(64, 3, nwin), dim3(256), 0, s, img, H, W, corners_dev, side, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_bf16(const float* x, size_t n, uint16_t* y, hipStream_t s) {
+  hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, n, y);
+  return hipGetLastError();
+}
+
+}  // namespace vit

@@ -1,0 +1,99 @@
+// Host-side launchers of the gfx950 kernels (internal to libvit).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vit {
+
+// Epilogue selector of the bf16 GEMM acc = A @ W^T.
+enum EpiKind {
+  EPI_BIAS_BF16 = 0,   // out_bf16[m,n] = acc + bias[n]
+  EPI_GELU_BF16 = 1,   // out_bf16[m,n] = GELU(acc + bias[n])
+  EPI_RESIDUAL = 2,    // out_f32[m,n] += ls[n] * (acc + bias[n])
+  EPI_BIAS_F32 = 3,    // out_f32[m,n] = acc + bias[n]
+  EPI_QKV = 4,         // head split into q (scaled), k, vt (transposed, permuted)
+  EPI_PATCH = 5,       // residual row of patch token: acc + bias[n] + pos[1 + i][n]
+};
+
+struct EpiParams {
+  int kind = EPI_BIAS_BF16;
+  const float* bias = nullptr;
+  const float* ls = nullptr;
+  void* out = nullptr;   // [M, ldc]
+  int ldc = 0;
+  // EPI_QKV
+  uint16_t* q = nullptr;
+  uint16_t* k = nullptr;
+  uint16_t* vt = nullptr;
+  int tokens = 0;        // rows per image (N)
+  int heads = 0;
+  int nv = 0;            // row length of vt
+  // EPI_PATCH: rows m = b * patches + i go to residual row b * tokens + 1 + regs + i
+  const float* pos = nullptr;
+  int patches = 0;
+  int regs = 0;
+};
+
+hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, int M, int N, int K, const EpiParams& ep,
+                       hipStream_t s);
+
+// LayerNorm of rows of x [rows, dim] into bf16 (out_f32 == false) or fp32.
+hipError_t launch_layernorm(const float* x, int rows, int dim, const float* g, const float* b, float eps,
+                            void* y, bool out_f32, hipStream_t s);
+
+// Taps: LayerNorm of the patch rows of x [batch, tokens, dim], written
+// channel-first to taps + b * tap_stride + (d * patches + i).
+hipError_t launch_tap(const float* x, int batch, int tokens, int first_patch, int patches, int dim,
+                      const float* g, const float* b, float eps, float* taps, size_t tap_stride,
+                      hipStream_t s);
+
+// Patch features for scoring: LayerNorm then L2 normalisation of the patch
+// rows, bf16 out [batch * patches, dim].
+hipError_t launch_ln_l2(const float* x, int batch, int tokens, int first_patch, int patches, int dim,
+                        const float* g, const float* b, float eps, uint16_t* feats, hipStream_t s);
+
+// Descriptor: desc[b] = x[b * row_stride + 0..dim) / max(||.||, 1e-12).
+hipError_t launch_descriptor(const float* x, int batch, size_t row_stride, int dim, float* desc,
+                             hipStream_t s);
+
+// im2col of fp32 images [batch, 3, H, W] into bf16 [batch * gh * gw, kpad]
+// with columns in (c, ky, kx) order, zero beyond 3 p^2.
+hipError_t launch_patchify(const float* img, int batch, int H, int W, int p, int kpad, uint16_t* out,
+                           hipStream_t s);
+
+// Rows 0..R of every image: CLS + pos[0], then the registers.
+hipError_t launch_assemble(float* x, int batch, int tokens, int dim, const float* cls, const float* pos0,
+                           const float* reg, int regs, hipStream_t s);
+
+// Bicubic (a = -0.75, half-pixel centres, clamped taps) resampling of the
+// patch rows of a position table; row 0 copied.
+hipError_t launch_pos_resample(const float* pos_in, int gh, int gw, float* pos_out, int th, int tw, int dim,
+                               hipStream_t s);
+
+// Attention core (see vit_op_attention).
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
+                            int heads, int nv, uint16_t* o, hipStream_t s);
+
+// fp32 -> bf16 (nearest even) of n values.
+hipError_t launch_to_bf16(const float* x, size_t n, uint16_t* y, hipStream_t s);
+
+// Slide-mode crops: out[w] = img[:, y_w : y_w + side, x_w : x_w + side].
+hipError_t launch_crops(const float* img, int H, int W, const int* corners_dev, int nwin, int side, float* out,
+                        hipStream_t s);
+
+// Whole mode: bilinear upsample of cos [gh*gw, ldc] (class-minor) to H x W,
+// first argmax over classes; dense [C, H, W] written if non-null.
+hipError_t launch_upsample_argmax(const float* cos, int gh, int gw, int classes, int ldc, int H, int W,
+                                  int* labels, float* dense, hipStream_t s);
+
+// Slide mode: per window upsample + softmax over classes, accumulate with
+// overlap counts, average, first argmax.
+hipError_t launch_slide_merge(const float* cos, int nwin, const int* corners_dev, int wg, int classes, int ldc,
+                              int side, int H, int W, int* labels, float* dense, hipStream_t s);
+
+// Transpose cos [rows = nimg * g, ldc] into [nimg, classes, g] (for the low-resolution output).
+hipError_t launch_cos_out(const float* cos, int nimg, int g, int classes, int ldc, float* out, hipStream_t s);
+
+}  // namespace vit
