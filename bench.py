@@ -103,7 +103,7 @@ def kernel_breakdown(cfg, batch, steps=20, warmup=5):
     N = (cfg["img_h"] // p) * (cfg["img_w"] // p) + 1 + cfg["registers"]
     M = batch * N
     L = cfg["depth"] + cfg.get("extra_blocks", 0)
-    nv = (N + 15) // 16 * 16
+    nv = (N + 63) // 64 * 64
     g = torch.Generator(device="cuda").manual_seed(7)
     bf = torch.bfloat16
 

@@ -44,7 +44,7 @@ int vit_op_linear(const void* a, const void* w, const float* bias, int M, int N,
  * (LibreYOLO diagram, "Encoder self-attention": Linear Q/K/V, reshape heads).
  *   h [batch*tokens, D] bf16 (LayerNorm output), wqkv [3D, D] bf16 (rows: the
  *   D rows of wq, then wk, then wv), bqkv [3D] fp32, D = 64*heads.
- * Outputs (bf16), with Nv = tokens rounded up to a multiple of 16:
+ * Outputs (bf16), with Nv = tokens rounded up to a multiple of 64:
  *   q  [batch, heads, tokens, 64]  = (h wq^T + bq) * log2(e) / sqrt(64)
  *   k  [batch, heads, tokens, 64]  = h wk^T + bk
  *   vt [batch, heads, 64, Nv]      = (h wv^T + bv) transposed per head; token t

@@ -94,7 +94,7 @@ def test_qkv_split(batch, tokens, heads):
     h_d, h = bf16_dev(RNG.standard_normal((M, D)))
     w_d, w = bf16_dev(RNG.standard_normal((3 * D, D)) * 0.05)
     bias = (0.1 * RNG.standard_normal(3 * D)).astype(np.float32)
-    nv = (tokens + 15) // 16 * 16
+    nv = (tokens + 63) // 64 * 64
     q = torch.empty((batch, heads, tokens, 64), dtype=torch.bfloat16, device="cuda")
     k = torch.empty_like(q)
     vt = torch.zeros((batch, heads, 64, nv), dtype=torch.bfloat16, device="cuda")
@@ -118,7 +118,7 @@ def test_qkv_split(batch, tokens, heads):
 # ------------------------------------------------------------------ attention core
 
 def _attention_case(batch, tokens, heads, q_scale=1.0, k_spike=None):
-    nv = (tokens + 15) // 16 * 16
+    nv = (tokens + 63) // 64 * 64
     qr = RNG.standard_normal((batch, heads, tokens, 64)) * q_scale
     kr = RNG.standard_normal((batch, heads, tokens, 64))
     vr = RNG.standard_normal((batch, heads, tokens, 64))

@@ -93,7 +93,7 @@ def test_plan_rejects_bad_configs(L):
     assert plan() == 0
     assert plan(img_h=337) == -2          # not a multiple of the patch
     assert plan(heads=5) == -5            # heads * 64 != dim
-    assert plan(dim=320, heads=5) == -5   # unsupported width
+    assert plan(dim=1088, heads=17) == -5  # unsupported width
     assert plan(mlp_hidden=1500) == -5
     assert plan(max_batch=0) == -1
     assert plan(ln_eps=0.0) == -1

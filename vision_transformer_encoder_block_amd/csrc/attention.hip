@@ -16,7 +16,8 @@
 // running max and sum all fp32: logits of ~2.5e6 (the DINOv3 attention sink)
 // stay finite, and the largest key of every row gets p = exp2(0) = 1 exactly.
 // K and V^T tiles of 64 keys are staged in LDS (double-buffered, 16-byte
-// chunks XOR-swizzled by row) and shared by the 4 waves of a workgroup.
+// chunks XOR-swizzled by row) and shared by the 4 waves of a workgroup; rows
+// past the sequence end are read as zeros through buffer range checks.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,6 +29,10 @@ constexpr int KT = 64;   // keys per tile
 
 // Inverse of the token permutation used by vt (an involution).
 __device__ __forceinline__ int vt_tok(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+// LDS position of 16-byte chunk c of row r: the 16 rows read by 16 lanes of one
+// ds_read_b128 cover all 64 banks.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                                                         const bf16_t* __restrict__ Vt, bf16_t* __restrict__ O,
@@ -44,14 +49,13 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int qrow = blockIdx.x * QT + wave * 32 + lrow;
 
-  const uint4 zero = make_uint4(0, 0, 0, 0);
+  // rows past N read as zeros through the buffer range checks
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qp, (uint32_t)N * 128u);
+  const __amdgpu_buffer_rsrc_t rk_src = make_rsrc(Kp, (uint32_t)N * 128u);
+  const __amdgpu_buffer_rsrc_t rv_src = make_rsrc(Vp, (uint32_t)nv * 128u);
   bf16x8 qf[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    uint4 u = zero;
-    if (qrow < N) u = *reinterpret_cast<const uint4*>(Qp + (size_t)qrow * 64 + ks * 16 + lhalf * 8);
-    qf[ks] = as_bf16x8(u);
-  }
+  for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(buf_load16(rq, (uint32_t)qrow * 128u + ks * 32 + lhalf * 16));
 
   // cooperative tile loads: 512 chunks of K and 512 of V^T, 2 + 2 per thread
   int k_row[2], k_q[2], k_dst[2], v_row[2], v_q[2], v_dst[2];
@@ -60,20 +64,18 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
     const int cid = tid + c * 256;
     k_row[c] = cid >> 3;
     k_q[c] = cid & 7;
-    k_dst[c] = k_row[c] * 8 + (k_q[c] ^ (k_row[c] & 7));
+    k_dst[c] = k_row[c] * 8 + swz(k_row[c], k_q[c]);
     v_row[c] = cid >> 3;  // channel d
     v_q[c] = cid & 7;     // 8 stored token positions
-    v_dst[c] = v_row[c] * 8 + (v_q[c] ^ (v_row[c] & 7));
+    v_dst[c] = v_row[c] * 8 + swz(v_row[c], v_q[c]);
   }
   auto load_tile = [&](int t, uint4* rk, uint4* rv) {
     const int k0 = t * KT;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int key = k0 + k_row[c];
-      rk[c] = key < N ? *reinterpret_cast<const uint4*>(Kp + (size_t)key * 64 + k_q[c] * 8) : zero;
-      const int p0 = k0 + v_q[c] * 8;
-      uint4 u = zero;
-      if (p0 < nv) u = *reinterpret_cast<const uint4*>(Vp + (size_t)v_row[c] * nv + p0);
+      rk[c] = buf_load16(rk_src, (uint32_t)(k0 + k_row[c]) * 128u + k_q[c] * 16);
+      const int p0 = k0 + v_q[c] * 8;  // < nv: nv is a multiple of 64
+      uint4 u = buf_load16(rv_src, ((uint32_t)v_row[c] * nv + p0) * 2u);
       if (k0 + KT > N) {  // last tile: zero the positions of keys >= N
         uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int qd = ks * 2 + lhalf;
-        s[kb] = mfma32x32x16(as_bf16x8(Ks[cur][r * 8 + (qd ^ (r & 7))]), qf[ks], s[kb]);
+        s[kb] = mfma32x32x16(as_bf16x8(Ks[cur][r * 8 + swz(r, qd)]), qf[ks], s[kb]);
       }
     }
     if ((t + 1) * KT > N) {
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = half_swap_max(mt);
     const float m_new = fmaxf(m_run, mt);  // finite: tile 0 always holds key 0
     const float alpha = exp2f(m_run - m_new);
     m_run = m_new;
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int qd = ks * 2 + lhalf;
-        o[db] = mfma32x32x16(as_bf16x8(Vs[cur][r * 8 + (qd ^ (r & 7))]), pf[ks], o[db]);
+        o[db] = mfma32x32x16(as_bf16x8(Vs[cur][r * 8 + swz(r, qd)]), pf[ks], o[db]);
       }
     }
 
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
     __syncthreads();
   }
 
-  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const float l = half_swap_sum(l_run);
   const float inv = 1.0f / l;
   if (qrow < N) {
     bf16_t* op = O + ((size_t)b * N + qrow) * (size_t)(H * 64) + h * 64;
@@ -199,7 +201,8 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
 
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
                             int heads, int nv, uint16_t* o, hipStream_t s) {
-  if (batch <= 0 || tokens <= 0 || heads <= 0 || nv < tokens || nv % 16 != 0) return hipErrorInvalidValue;
+  if (batch <= 0 || tokens <= 0 || heads <= 0 || nv < tokens || nv % 64 != 0) return hipErrorInvalidValue;
+  if ((size_t)nv * 128 >= (1ull << 32)) return hipErrorInvalidValue;
   dim3 grid((tokens + QT - 1) / QT, heads, batch);
   hipLaunchKernelGGL(attention_kernel, grid, dim3(256), 0, s, q, k, vt, o, tokens, heads, nv);
   return hipGetLastError();

@@ -5,11 +5,15 @@
 // [N, K]), so each lane of v_mfma_f32_32x32x16_bf16 reads 16 contiguous bytes
 // of one row for either operand.  A 256-thread workgroup (4 waves in 2 x 2)
 // computes a BM x BN tile; K advances in steps of 64 through a double-buffered
-// LDS tile whose 16-byte chunks are XOR-swizzled by row so that the eight rows
-// read together by consecutive lanes hit distinct banks.  Global loads for the
-// next K step are in flight while the MFMAs of the current step run.
-// Workgroup ids are remapped so that each XCD (8 per chip, its own L2) owns a
-// contiguous range of tiles, grouped along M for operand reuse.
+// LDS tile.  Tiles are fetched with buffer loads whose range check returns 0
+// for rows past M or N, so ragged edges need no branches.  In LDS the 16-byte
+// chunk c of row r sits at chunk c ^ ((r >> 1) & 7): the 16 rows read together
+// by 16 consecutive lanes of one ds_read_b128 then cover all 64 banks.
+// Global loads for the next K step are in flight while the MFMAs of the
+// current step run.  The epilogue stages each wave's accumulators through LDS
+// so that every lane writes 4 consecutive columns of one row (coalesced
+// 8- or 16-byte stores).  Workgroup ids are remapped so that each XCD (8 per
+// chip, own L2) owns a contiguous range of tiles, grouped along M.
 #include "common.h"
 #include "kernels.h"
 
@@ -32,8 +36,10 @@ FastDiv make_fastdiv(uint32_t d) {
 
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.mul) + n) >> f.shift; }
 
-// Exchange bits 2 and 3 of a token index (layout of vt, see vit_op_qkv).
+// Column of token t in vt: bits 2 and 3 exchanged (see vit_op_qkv).
 __device__ __forceinline__ int vt_pos(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int n = tiles_m * tiles_n;
@@ -53,24 +59,48 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = r / gsize;
 }
 
+__device__ __forceinline__ uint2 pack4_bf16(const float (&v)[4]) {
+  return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+
 // ---------------------------------------------------------------- epilogues
+// store4(m, n, v, nvalid): columns n .. n + nvalid - 1 (nvalid <= 4) of row m.
+// `vec` is true when row starts and n are aligned for a 4-wide vector store.
 
 struct EpiBiasBf16 {
   const float* bias;
   bf16_t* out;
   int ldc;
-  struct Col { float b; };
-  __device__ Col col(int n) const { return {bias ? bias[n] : 0.f}; }
-  __device__ void store(int m, int n, float v, Col c) const { out[(size_t)m * ldc + n] = f2bf(v + c.b); }
+  bool vec;
+  __device__ void store4(int m, int n, float (&v)[4], int nvalid) const {
+    bf16_t* p = out + (size_t)m * ldc + n;
+    for (int i = 0; i < 4; ++i) v[i] += (bias && i < nvalid) ? bias[n + i] : 0.f;
+    if (vec && nvalid == 4) {
+      *reinterpret_cast<uint2*>(p) = pack4_bf16(v);
+    } else {
+      for (int i = 0; i < nvalid; ++i) p[i] = f2bf(v[i]);
+    }
+  }
 };
 
 struct EpiGeluBf16 {
   const float* bias;
   bf16_t* out;
   int ldc;
-  struct Col { float b; };
-  __device__ Col col(int n) const { return {bias[n]}; }
-  __device__ void store(int m, int n, float v, Col c) const { out[(size_t)m * ldc + n] = f2bf(gelu_erf(v + c.b)); }
+  bool vec;
+  __device__ void store4(int m, int n, float (&v)[4], int nvalid) const {
+    bf16_t* p = out + (size_t)m * ldc + n;
+    if (vec && nvalid == 4) {
+      const float4 b = *reinterpret_cast<const float4*>(bias + n);
+      v[0] = gelu_erf(v[0] + b.x);
+      v[1] = gelu_erf(v[1] + b.y);
+      v[2] = gelu_erf(v[2] + b.z);
+      v[3] = gelu_erf(v[3] + b.w);
+      *reinterpret_cast<uint2*>(p) = pack4_bf16(v);
+    } else {
+      for (int i = 0; i < nvalid; ++i) p[i] = f2bf(gelu_erf(v[i] + bias[n + i]));
+    }
+  }
 };
 
 struct EpiResidual {
@@ -78,11 +108,21 @@ struct EpiResidual {
   const float* ls;
   float* out;
   int ldc;
-  struct Col { float b, s; };
-  __device__ Col col(int n) const { return {bias[n], ls[n]}; }
-  __device__ void store(int m, int n, float v, Col c) const {
+  bool vec;
+  __device__ void store4(int m, int n, float (&v)[4], int nvalid) const {
     float* p = out + (size_t)m * ldc + n;
-    *p = *p + c.s * (v + c.b);
+    if (vec && nvalid == 4) {
+      const float4 b = *reinterpret_cast<const float4*>(bias + n);
+      const float4 s = *reinterpret_cast<const float4*>(ls + n);
+      float4 r = *reinterpret_cast<float4*>(p);
+      r.x += s.x * (v[0] + b.x);
+      r.y += s.y * (v[1] + b.y);
+      r.z += s.z * (v[2] + b.z);
+      r.w += s.w * (v[3] + b.w);
+      *reinterpret_cast<float4*>(p) = r;
+    } else {
+      for (int i = 0; i < nvalid; ++i) p[i] = p[i] + ls[n + i] * (v[i] + bias[n + i]);
+    }
   }
 };
 
@@ -90,37 +130,38 @@ struct EpiBiasF32 {
   const float* bias;
   float* out;
   int ldc;
-  struct Col { float b; };
-  __device__ Col col(int n) const { return {bias ? bias[n] : 0.f}; }
-  __device__ void store(int m, int n, float v, Col c) const { out[(size_t)m * ldc + n] = v + c.b; }
+  bool vec;
+  __device__ void store4(int m, int n, float (&v)[4], int nvalid) const {
+    float* p = out + (size_t)m * ldc + n;
+    for (int i = 0; i < 4; ++i) v[i] += (bias && i < nvalid) ? bias[n + i] : 0.f;
+    if (vec && nvalid == 4) {
+      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      for (int i = 0; i < nvalid; ++i) p[i] = v[i];
+    }
+  }
 };
 
-struct EpiQKV {
+// Q and K columns (n < 2D) of the fused projection: head-major rows of 64.
+struct EpiQK {
   const float* bias;
   bf16_t* q;
   bf16_t* k;
-  bf16_t* vt;
-  int D, N, heads, nv;
+  int D, N, heads;
   FastDiv divN;
   float qscale;
-  struct Col { float b; int which, head, d; };
-  __device__ Col col(int n) const {
-    const int which = n / D;
+  bool vec;  // always true: D % 64 == 0 and n % 4 == 0
+  __device__ void store4(int m, int n, float (&v)[4], int) const {
+    const int which = n >= D;
     const int c = n - which * D;
-    return {bias[n], which, c >> 6, c & 63};
-  }
-  __device__ void store(int m, int n, float v, Col c) const {
+    const int head = c >> 6, d = c & 63;
     const int b = (int)fdiv((uint32_t)m, divN);
     const int tok = m - b * N;
-    const size_t bh = (size_t)b * heads + c.head;
-    const float x = v + c.b;
-    if (c.which == 0) {
-      q[(bh * N + tok) * 64 + c.d] = f2bf(x * qscale);
-    } else if (c.which == 1) {
-      k[(bh * N + tok) * 64 + c.d] = f2bf(x);
-    } else {
-      vt[(bh * 64 + c.d) * nv + vt_pos(tok)] = f2bf(x);
-    }
+    const size_t row = ((size_t)b * heads + head) * N + tok;
+    const float4 bb = *reinterpret_cast<const float4*>(bias + n);
+    const float s = which ? 1.f : qscale;
+    float o[4] = {(v[0] + bb.x) * s, (v[1] + bb.y) * s, (v[2] + bb.z) * s, (v[3] + bb.w) * s};
+    *reinterpret_cast<uint2*>((which ? k : q) + row * 64 + d) = pack4_bf16(o);
   }
 };
 
@@ -130,26 +171,46 @@ struct EpiPatch {
   float* out;
   int D, tokens, patches, regs;
   FastDiv divP;
-  struct Col { float b; };
-  __device__ Col col(int n) const { return {bias[n]}; }
-  __device__ void store(int m, int n, float v, Col c) const {
+  bool vec;  // always true: D % 64 == 0
+  __device__ void store4(int m, int n, float (&v)[4], int) const {
     const int b = (int)fdiv((uint32_t)m, divP);
     const int i = m - b * patches;
     const size_t row = (size_t)b * tokens + 1 + regs + i;
-    out[row * D + n] = v + c.b + pos[(size_t)(1 + i) * D + n];
+    const float4 bb = *reinterpret_cast<const float4*>(bias + n);
+    const float4 pp = *reinterpret_cast<const float4*>(pos + (size_t)(1 + i) * D + n);
+    *reinterpret_cast<float4*>(out + row * D + n) =
+        make_float4(v[0] + bb.x + pp.x, v[1] + bb.y + pp.y, v[2] + bb.z + pp.z, v[3] + bb.w + pp.w);
+  }
+};
+
+// V columns, computed transposed (A = wv rows, W = token rows): element (m, n)
+// is channel m of token row n, stored in vt.  Written straight from the
+// accumulators: the 32 lanes of a row hold 32 consecutive tokens.
+struct EpiVt {
+  const float* bias;  // bv
+  bf16_t* vt;
+  int N, heads, nv;
+  FastDiv divN;
+  __device__ void store(int m, int n, float v) const {
+    const int b = (int)fdiv((uint32_t)n, divN);
+    const int tok = n - b * N;
+    const int head = m >> 6, d = m & 63;
+    vt[(((size_t)b * heads + head) * 64 + d) * nv + vt_pos(tok)] = f2bf(v + bias[m]);
   }
 };
 
 // ---------------------------------------------------------------- kernel
 
-template <int BM, int BN, class Epi>
+template <int BM, int BN, bool kStaged, class Epi>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
                                                         int M, int N, int K, int tiles_m, int tiles_n, Epi epi) {
-  constexpr int TM = BM / 64, TN = BN / 64;           // 32x32 blocks per wave
+  constexpr int TM = BM / 64, TN = BN / 64;               // 32x32 blocks per wave
+  constexpr int WTM = BM / 2, WTN = BN / 2;               // wave tile
   constexpr int A_CH = BM * 8 / 256, B_CH = BN * 8 / 256;  // 16-byte chunks per thread per K step
   static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
-  __shared__ uint4 As[2][BM * 8];
-  __shared__ uint4 Bs[2][BN * 8];
+  __shared__ uint4 lds[2 * (BM + BN) * 8];
+  uint4* As = lds;                  // [2][BM * 8]
+  uint4* Bs = lds + 2 * BM * 8;     // [2][BN * 8]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -158,25 +219,21 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const uint4* a_src[A_CH];
-  const uint4* b_src[B_CH];
-  bool a_ok[A_CH], b_ok[B_CH];
+  const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(A, (uint32_t)((size_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t rb_src = make_rsrc(W, (uint32_t)((size_t)N * K * 2));
+  uint32_t a_off[A_CH], b_off[B_CH];
   int a_dst[A_CH], b_dst[B_CH];
 #pragma unroll
   for (int c = 0; c < A_CH; ++c) {
     const int cid = tid + c * 256, r = cid >> 3, qd = cid & 7;
-    const int row = m0 + r;
-    a_ok[c] = row < M;
-    a_src[c] = reinterpret_cast<const uint4*>(A + (size_t)(a_ok[c] ? row : 0) * K) + qd;
-    a_dst[c] = r * 8 + (qd ^ (r & 7));
+    a_off[c] = (uint32_t)(m0 + r) * (uint32_t)K * 2u + qd * 16u;
+    a_dst[c] = r * 8 + swz(r, qd);
   }
 #pragma unroll
   for (int c = 0; c < B_CH; ++c) {
     const int cid = tid + c * 256, r = cid >> 3, qd = cid & 7;
-    const int row = n0 + r;
-    b_ok[c] = row < N;
-    b_src[c] = reinterpret_cast<const uint4*>(W + (size_t)(b_ok[c] ? row : 0) * K) + qd;
-    b_dst[c] = r * 8 + (qd ^ (r & 7));
+    b_off[c] = (uint32_t)(n0 + r) * (uint32_t)K * 2u + qd * 16u;
+    b_dst[c] = r * 8 + swz(r, qd);
   }
 
   f32x16 acc[TM][TN];
@@ -187,16 +244,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const uint4 zero = make_uint4(0, 0, 0, 0);
   uint4 ra[A_CH], rb[B_CH];
 #pragma unroll
-  for (int c = 0; c < A_CH; ++c) ra[c] = a_ok[c] ? a_src[c][0] : zero;
+  for (int c = 0; c < A_CH; ++c) ra[c] = buf_load16(ra_src, a_off[c]);
 #pragma unroll
-  for (int c = 0; c < B_CH; ++c) rb[c] = b_ok[c] ? b_src[c][0] : zero;
+  for (int c = 0; c < B_CH; ++c) rb[c] = buf_load16(rb_src, b_off[c]);
 #pragma unroll
-  for (int c = 0; c < A_CH; ++c) As[0][a_dst[c]] = ra[c];
+  for (int c = 0; c < A_CH; ++c) As[a_dst[c]] = ra[c];
 #pragma unroll
-  for (int c = 0; c < B_CH; ++c) Bs[0][b_dst[c]] = rb[c];
+  for (int c = 0; c < B_CH; ++c) Bs[b_dst[c]] = rb[c];
   __syncthreads();
 
   const int KT = K / BK;
@@ -204,25 +260,27 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < KT) {
-      const int off = (kt + 1) * (BK / 8);
+      const uint32_t koff = (uint32_t)(kt + 1) * (BK * 2);
 #pragma unroll
-      for (int c = 0; c < A_CH; ++c) ra[c] = a_ok[c] ? a_src[c][off] : zero;
+      for (int c = 0; c < A_CH; ++c) ra[c] = buf_load16(ra_src, a_off[c] + koff);
 #pragma unroll
-      for (int c = 0; c < B_CH; ++c) rb[c] = b_ok[c] ? b_src[c][off] : zero;
+      for (int c = 0; c < B_CH; ++c) rb[c] = buf_load16(rb_src, b_off[c] + koff);
     }
+    const uint4* Ac = As + cur * BM * 8;
+    const uint4* Bc = Bs + cur * BN * 8;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int qd = ks * 2 + lhalf;
       bf16x8 af[TM], bw[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int r = wm * (BM / 2) + i * 32 + lrow;
-        af[i] = as_bf16x8(As[cur][r * 8 + (qd ^ (r & 7))]);
+        const int r = wm * WTM + i * 32 + lrow;
+        af[i] = as_bf16x8(Ac[r * 8 + swz(r, qd)]);
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int r = wn * (BN / 2) + j * 32 + lrow;
-        bw[j] = as_bf16x8(Bs[cur][r * 8 + (qd ^ (r & 7))]);
+        const int r = wn * WTN + j * 32 + lrow;
+        bw[j] = as_bf16x8(Bc[r * 8 + swz(r, qd)]);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -230,45 +288,77 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(af[i], bw[j], acc[i][j]);
     }
     if (kt + 1 < KT) {
+      uint4* An = As + (cur ^ 1) * BM * 8;
+      uint4* Bn = Bs + (cur ^ 1) * BN * 8;
 #pragma unroll
-      for (int c = 0; c < A_CH; ++c) As[cur ^ 1][a_dst[c]] = ra[c];
+      for (int c = 0; c < A_CH; ++c) An[a_dst[c]] = ra[c];
 #pragma unroll
-      for (int c = 0; c < B_CH; ++c) Bs[cur ^ 1][b_dst[c]] = rb[c];
+      for (int c = 0; c < B_CH; ++c) Bn[b_dst[c]] = rb[c];
     }
     __syncthreads();
   }
 
   // accumulator element e of block (i, j): row 8*(e/4) + 4*lhalf + e%4, column lrow
+  if constexpr (!kStaged) {
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int n = n0 + wn * (BN / 2) + j * 32 + lrow;
-    if (n >= N) continue;
-    const auto cv = epi.col(n);
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * WTN + j * 32 + lrow;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
+          if (m < M && n < N) epi.store(m, n, acc[i][j][e]);
+        }
+    }
+  } else {
+    // Each wave stages one 32-row block of its tile at a time (row stride WTN + 8
+    // floats: the two lane halves land on disjoint banks), then every lane
+    // handles 4 consecutive columns of one row.
+    constexpr int LD = WTN + 8;
+    constexpr int LPR = WTN / 4;        // lanes per staged row
+    constexpr int RPP = 64 / LPR;       // rows per pass
+    float* stage = reinterpret_cast<float*>(lds) + wave * 32 * LD;
+    const int cl = (lane % LPR) * 4;
+    const int n = n0 + wn * WTN + cl;
+    const int nvalid = min(4, N - n);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * (BM / 2) + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
-        if (m < M) epi.store(m, n, acc[i][j][e], cv);
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) stage[((e >> 2) * 8 + lhalf * 4 + (e & 3)) * LD + j * 32 + lrow] = acc[i][j][e];
+      __syncthreads();
+#pragma unroll
+      for (int pass = 0; pass < 32 / RPP; ++pass) {
+        const int r = pass * RPP + lane / LPR;
+        const int m = m0 + wm * WTM + i * 32 + r;
+        if (m < M && nvalid > 0) {
+          const float4 t = *reinterpret_cast<const float4*>(stage + r * LD + cl);
+          float v[4] = {t.x, t.y, t.z, t.w};
+          epi.store4(m, n, v, nvalid);
+        }
       }
+      __syncthreads();
     }
   }
 }
 
-template <int BM, int BN, class Epi>
+template <int BM, int BN, bool kStaged, class Epi>
 hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
+  static_assert(2 * (BM + BN) * 8 * 16 >= 4 * 32 * (BN / 2 + 8) * 4, "staging must fit in the tile LDS");
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi>), dim3(tiles_m * tiles_n), dim3(256), 0, s, A, W, M, N, K,
-                     tiles_m, tiles_n, epi);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, kStaged, Epi>), dim3(tiles_m * tiles_n), dim3(256), 0, s, A, W, M, N,
+                     K, tiles_m, tiles_n, epi);
   return hipGetLastError();
 }
 
-template <class Epi>
+template <bool kStaged, class Epi>
 hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   // Few tiles: a smaller tile keeps more CUs busy.
   const long big_tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (big_tiles < 256) return run<64, 64>(A, W, M, N, K, epi, s);
-  return run<128, 128>(A, W, M, N, K, epi, s);
+  if (big_tiles < 256) return run<64, 64, kStaged>(A, W, M, N, K, epi, s);
+  return run<128, 128, kStaged>(A, W, M, N, K, epi, s);
 }
 
 }  // namespace
@@ -276,25 +366,32 @@ hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const
 hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, int M, int N, int K, const EpiParams& ep,
                        hipStream_t s) {
   if (M <= 0 || N <= 0 || K <= 0 || K % BK != 0) return hipErrorInvalidValue;
+  if ((size_t)(M + 128) * K * 2 >= (1ull << 32) || (size_t)(N + 128) * K * 2 >= (1ull << 32))
+    return hipErrorInvalidValue;  // 32-bit buffer offsets
+  const bool vec = ep.ldc % 4 == 0;
   switch (ep.kind) {
     case EPI_BIAS_BF16:
-      return dispatch(A, W, M, N, K, EpiBiasBf16{ep.bias, (bf16_t*)ep.out, ep.ldc}, s);
+      return dispatch<true>(A, W, M, N, K, EpiBiasBf16{ep.bias, (bf16_t*)ep.out, ep.ldc, vec}, s);
     case EPI_GELU_BF16:
-      return dispatch(A, W, M, N, K, EpiGeluBf16{ep.bias, (bf16_t*)ep.out, ep.ldc}, s);
+      return dispatch<true>(A, W, M, N, K, EpiGeluBf16{ep.bias, (bf16_t*)ep.out, ep.ldc, vec}, s);
     case EPI_RESIDUAL:
-      return dispatch(A, W, M, N, K, EpiResidual{ep.bias, ep.ls, (float*)ep.out, ep.ldc}, s);
+      return dispatch<true>(A, W, M, N, K, EpiResidual{ep.bias, ep.ls, (float*)ep.out, ep.ldc, vec}, s);
     case EPI_BIAS_F32:
-      return dispatch(A, W, M, N, K, EpiBiasF32{ep.bias, (float*)ep.out, ep.ldc}, s);
+      return dispatch<true>(A, W, M, N, K, EpiBiasF32{ep.bias, (float*)ep.out, ep.ldc, vec}, s);
     case EPI_QKV: {
+      // N = 3D: Q and K columns as one GEMM, V columns as a transposed GEMM.
       const int D = N / 3;
-      EpiQKV e{ep.bias, ep.q, ep.k, ep.vt, D, ep.tokens, ep.heads, ep.nv, make_fastdiv(ep.tokens),
-               kLog2e * 0.125f};
-      return dispatch(A, W, M, N, K, e, s);
+      const FastDiv dn = make_fastdiv(ep.tokens);
+      EpiQK eqk{ep.bias, ep.q, ep.k, D, ep.tokens, ep.heads, dn, kLog2e * 0.125f, true};
+      hipError_t e = dispatch<true>(A, W, M, 2 * D, K, eqk, s);
+      if (e != hipSuccess) return e;
+      EpiVt ev{ep.bias + 2 * D, ep.vt, ep.tokens, ep.heads, ep.nv, dn};
+      return dispatch<false>(W + (size_t)2 * D * K, A, D, M, K, ev, s);
     }
     case EPI_PATCH: {
-      EpiPatch e{ep.bias, ep.pos, (float*)ep.out, ep.ldc, ep.tokens, ep.patches, ep.regs,
-                 make_fastdiv(ep.patches)};
-      return dispatch(A, W, M, N, K, e, s);
+      EpiPatch e{ep.bias, ep.pos, (float*)ep.out, ep.ldc, ep.tokens, ep.patches, ep.regs, make_fastdiv(ep.patches),
+                 true};
+      return dispatch<true>(A, W, M, N, K, e, s);
     }
   }
   return hipErrorInvalidValue;

@@ -121,10 +121,19 @@ hipError_t by_width(int dim, Args... args) {
   switch (dim / 64) {
     case 1: return Launch<1>::go(args...);
     case 2: return Launch<2>::go(args...);
+    case 3: return Launch<3>::go(args...);
     case 4: return Launch<4>::go(args...);
+    case 5: return Launch<5>::go(args...);
     case 6: return Launch<6>::go(args...);
+    case 7: return Launch<7>::go(args...);
     case 8: return Launch<8>::go(args...);
+    case 9: return Launch<9>::go(args...);
+    case 10: return Launch<10>::go(args...);
+    case 11: return Launch<11>::go(args...);
     case 12: return Launch<12>::go(args...);
+    case 13: return Launch<13>::go(args...);
+    case 14: return Launch<14>::go(args...);
+    case 15: return Launch<15>::go(args...);
     case 16: return Launch<16>::go(args...);
     case 20: return Launch<20>::go(args...);
     case 24: return Launch<24>::go(args...);

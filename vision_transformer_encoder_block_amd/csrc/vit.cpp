@@ -48,11 +48,9 @@ uint16_t host_bf16(float f) {
 }
 
 bool width_supported(int dim) {
-  switch (dim / 64) {
-    case 1: case 2: case 4: case 6: case 8: case 12: case 16: case 20: case 24: case 32: case 48: case 64:
-      return dim % 64 == 0;
-  }
-  return false;
+  if (dim <= 0 || dim % 64) return false;
+  const int v = dim / 64;
+  return v <= 16 || v == 20 || v == 24 || v == 32 || v == 48 || v == 64;
 }
 
 // Window starts along one axis: ceil((n - side) / stride) + 1 windows every
@@ -105,7 +103,7 @@ int make_geom(const Plan& pl, int img_h, int img_w, Geom& g) {
   g.gw = img_w / pl.p;
   g.P = g.gh * g.gw;
   g.N = g.P + 1 + pl.R;
-  g.nv = round_up(g.N, 16);
+  g.nv = round_up(g.N, 64);
   return VIT_OK;
 }
 
@@ -116,7 +114,7 @@ int build_plan(const vit_config* c, Plan& pl) {
   if (c->img_h <= 0 || c->img_w <= 0 || c->img_h % c->patch || c->img_w % c->patch)
     return fail(VIT_ERR_SHAPE, "image size must be a positive multiple of the patch size");
   if (c->dim <= 0 || !width_supported(c->dim))
-    return fail(VIT_ERR_UNSUPPORTED, "dim must be 64 * {1,2,4,6,8,12,16,20,24,32,48,64}");
+    return fail(VIT_ERR_UNSUPPORTED, "dim must be 64 * {1..16, 20, 24, 32, 48, 64}");
   if (c->heads * 64 != c->dim) return fail(VIT_ERR_UNSUPPORTED, "heads must equal dim / 64 (64-channel heads)");
   if (c->mlp_hidden <= 0 || c->mlp_hidden % 64) return fail(VIT_ERR_UNSUPPORTED, "mlp_hidden must be a multiple of 64");
   if (c->depth < 0 || c->extra_blocks < 0 || c->depth + c->extra_blocks > 256)
@@ -633,7 +631,7 @@ int vit_op_qkv(const void* h, const void* wqkv, const float* bqkv, int batch, in
   eq.vt = (uint16_t*)vt;
   eq.tokens = tokens;
   eq.heads = heads;
-  eq.nv = round_up(tokens, 16);
+  eq.nv = round_up(tokens, 64);
   VIT_HIP(vit::launch_gemm((const uint16_t*)h, (const uint16_t*)wqkv, batch * tokens, 3 * D, D, eq,
                            (hipStream_t)stream),
           "qkv");
@@ -645,7 +643,7 @@ int vit_op_attention(const void* q, const void* k, const void* vt, int batch, in
   if (!q || !k || !vt || !o) return fail(VIT_ERR_ARG, "NULL pointer");
   if (batch < 1 || tokens < 1 || heads < 1 || heads > 64) return fail(VIT_ERR_SHAPE, "bad batch/tokens/heads");
   VIT_HIP(vit::launch_attention((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, batch, tokens, heads,
-                                round_up(tokens, 16), (uint16_t*)o, (hipStream_t)stream),
+                                round_up(tokens, 64), (uint16_t*)o, (hipStream_t)stream),
           "attention");
   return VIT_OK;
 }
