@@ -59,6 +59,47 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
+// Direct-to-LDS loads.  A raw buffer descriptor (base, no stride, byte range,
+// gfx9 data format word); loads at offsets >= `bytes` return zeros.
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int32x4 make_rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  int32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from `voff` into LDS at lds_base + 16 * lane (lds_base is
+// wave-uniform, passed in M0).  Issued from inline assembly so that the
+// compiler does not insert its own conservative waits; the caller waits with
+// wait_vm<> before the barrier that publishes the data.  The instruction has no
+// VGPR result.
+__device__ __forceinline__ void dma16(int32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_base)
+               : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that orders memory operations for the compiler but does
+// not drain outstanding loads (the caller waits for exactly what it needs).
+__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // Sum / max of a value and its copy in the other 32-lane half of the wave.
 __device__ __forceinline__ float half_swap_sum(float v) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -17,10 +17,18 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace vit {
 namespace {
 
 constexpr int BK = 64;
+#ifndef GEMM_STAGES
+#define GEMM_STAGES 3
+#endif
+#ifndef GEMM_STAGES_SMALL
+#define GEMM_STAGES_SMALL 3
+#endif
 
 // Division by a runtime constant for 0 <= n < 2^31 (multiply-high + shift).
 struct FastDiv {
@@ -199,18 +207,38 @@ struct EpiVt {
   }
 };
 
-// ---------------------------------------------------------------- kernel
+// ---------------------------------------------------------------- pipeline helpers
 
-template <int BM, int BN, bool kStaged, class Epi>
+// One LDS object per (size, stage): the compiler then tracks the DMA writes
+// of each stage separately and only waits for the stage it reads.
+template <int BYTES, int STAGE>
+__device__ __forceinline__ uint4* stage_lds() {
+  __shared__ uint4 buf[BYTES / 16];
+  return buf;
+}
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// ---------------------------------------------------------------- kernel
+// S-stage pipeline: K steps of 64 arrive in LDS by direct-to-LDS buffer loads
+// (each wave instruction fills 1 KB = 8 rows x 128 B; every lane fetches the
+// logical chunk that belongs at its swizzled slot) issued S - 1 steps ahead.
+
+template <int BM, int BN, int S, bool kStaged, class Epi>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
                                                         int M, int N, int K, int tiles_m, int tiles_n, Epi epi) {
-  constexpr int TM = BM / 64, TN = BN / 64;               // 32x32 blocks per wave
-  constexpr int WTM = BM / 2, WTN = BN / 2;               // wave tile
-  constexpr int A_CH = BM * 8 / 256, B_CH = BN * 8 / 256;  // 16-byte chunks per thread per K step
-  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
-  __shared__ uint4 lds[2 * (BM + BN) * 8];
-  uint4* As = lds;                  // [2][BM * 8]
-  uint4* Bs = lds + 2 * BM * 8;     // [2][BN * 8]
+  constexpr int TM = BM / 64, TN = BN / 64;     // 32x32 blocks per wave
+  constexpr int WTM = BM / 2, WTN = BN / 2;     // wave tile
+  constexpr int A_IT = BM / 32, B_IT = BN / 32; // DMA instructions per wave per stage
+  constexpr int L = A_IT + B_IT;
+  constexpr int STAGE_BYTES = (BM + BN) * 128;
+  static_assert(S >= 2 && (S - 1) * L < 64, "pipeline depth");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -219,22 +247,33 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(A, (uint32_t)((size_t)M * K * 2));
-  const __amdgpu_buffer_rsrc_t rb_src = make_rsrc(W, (uint32_t)((size_t)N * K * 2));
-  uint32_t a_off[A_CH], b_off[B_CH];
-  int a_dst[A_CH], b_dst[B_CH];
+  const int32x4 ra_src = make_rsrc_words(A, (uint32_t)((size_t)M * K * 2));
+  const int32x4 rb_src = make_rsrc_words(W, (uint32_t)((size_t)N * K * 2));
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // byte offset (at k = 0) of the chunk this lane fetches in each DMA instruction
+  uint32_t a_off[A_IT], b_off[B_IT];
+  {
+    const int sub = lane >> 3, pc = lane & 7;
 #pragma unroll
-  for (int c = 0; c < A_CH; ++c) {
-    const int cid = tid + c * 256, r = cid >> 3, qd = cid & 7;
-    a_off[c] = (uint32_t)(m0 + r) * (uint32_t)K * 2u + qd * 16u;
-    a_dst[c] = r * 8 + swz(r, qd);
-  }
+    for (int j = 0; j < A_IT; ++j) {
+      const int row = (j * 4 + wave) * 8 + sub;
+      a_off[j] = (uint32_t)(m0 + row) * (uint32_t)K * 2u + (uint32_t)swz(row, pc) * 16u;
+    }
 #pragma unroll
-  for (int c = 0; c < B_CH; ++c) {
-    const int cid = tid + c * 256, r = cid >> 3, qd = cid & 7;
-    b_off[c] = (uint32_t)(n0 + r) * (uint32_t)K * 2u + qd * 16u;
-    b_dst[c] = r * 8 + swz(r, qd);
+    for (int j = 0; j < B_IT; ++j) {
+      const int row = (j * 4 + wave) * 8 + sub;
+      b_off[j] = (uint32_t)(n0 + row) * (uint32_t)K * 2u + (uint32_t)swz(row, pc) * 16u;
+    }
   }
+  auto issue = [&](auto stage, int kt) {
+    const uint32_t blk = lds_addr(stage_lds<STAGE_BYTES, decltype(stage)::value>());
+    const uint32_t koff = (uint32_t)kt * (BK * 2);
+#pragma unroll
+    for (int j = 0; j < A_IT; ++j) dma16(ra_src, a_off[j] + koff, blk + (uint32_t)(j * 4 + wave_u) * 1024u);
+#pragma unroll
+    for (int j = 0; j < B_IT; ++j)
+      dma16(rb_src, b_off[j] + koff, blk + (uint32_t)(BM * 128 + (j * 4 + wave_u) * 1024));
+  };
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -244,59 +283,58 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  uint4 ra[A_CH], rb[B_CH];
-#pragma unroll
-  for (int c = 0; c < A_CH; ++c) ra[c] = buf_load16(ra_src, a_off[c]);
-#pragma unroll
-  for (int c = 0; c < B_CH; ++c) rb[c] = buf_load16(rb_src, b_off[c]);
-#pragma unroll
-  for (int c = 0; c < A_CH; ++c) As[a_dst[c]] = ra[c];
-#pragma unroll
-  for (int c = 0; c < B_CH; ++c) Bs[b_dst[c]] = rb[c];
-  __syncthreads();
-
   const int KT = K / BK;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) {
-      const uint32_t koff = (uint32_t)(kt + 1) * (BK * 2);
-#pragma unroll
-      for (int c = 0; c < A_CH; ++c) ra[c] = buf_load16(ra_src, a_off[c] + koff);
-#pragma unroll
-      for (int c = 0; c < B_CH; ++c) rb[c] = buf_load16(rb_src, b_off[c] + koff);
-    }
-    const uint4* Ac = As + cur * BM * 8;
-    const uint4* Bc = Bs + cur * BN * 8;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+  // Fragments of step ks + 1 are read from LDS while the MFMAs of step ks run.
+  auto compute = [&](auto stage) {
+    const uint4* Ac = stage_lds<STAGE_BYTES, decltype(stage)::value>();
+    const uint4* Bc = Ac + BM * 8;
+    bf16x8 af[2][TM], bw[2][TN];
+    auto read = [&](int buf, int ks) {
       const int qd = ks * 2 + lhalf;
-      bf16x8 af[TM], bw[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * WTM + i * 32 + lrow;
-        af[i] = as_bf16x8(Ac[r * 8 + swz(r, qd)]);
+        af[buf][i] = as_bf16x8(Ac[r * 8 + swz(r, qd)]);
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int r = wn * WTN + j * 32 + lrow;
-        bw[j] = as_bf16x8(Bc[r * 8 + swz(r, qd)]);
+        bw[buf][j] = as_bf16x8(Bc[r * 8 + swz(r, qd)]);
       }
+    };
+    read(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) read(cur ^ 1, ks + 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(af[i], bw[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(af[cur][i], bw[cur][j], acc[i][j]);
     }
-    if (kt + 1 < KT) {
-      uint4* An = As + (cur ^ 1) * BM * 8;
-      uint4* Bn = Bs + (cur ^ 1) * BN * 8;
-#pragma unroll
-      for (int c = 0; c < A_CH; ++c) An[a_dst[c]] = ra[c];
-#pragma unroll
-      for (int c = 0; c < B_CH; ++c) Bn[b_dst[c]] = rb[c];
-    }
-    __syncthreads();
+  };
+
+  static_for<0, S - 1>([&](auto s) {
+    if (decltype(s)::value < KT) issue(s, decltype(s)::value);
+  });
+  for (int kt0 = 0; kt0 < KT; kt0 += S) {
+    static_for<0, S>([&](auto s) {
+      constexpr int st = decltype(s)::value;
+      const int kt = kt0 + st;
+      if (kt < KT) {
+        // this wave's loads of stage st are done once at most `later` stages are in flight
+        const int later = min(S - 2, KT - 1 - kt);
+        static_for<0, S - 1>([&](auto c) {
+          if (later == decltype(c)::value) wait_vm<decltype(c)::value * L>();
+        });
+        barrier_keep_loads();  // every wave's loads of stage st have landed
+        if (kt + S - 1 < KT) issue(std::integral_constant<int, (st + S - 1) % S>{}, kt + S - 1);
+        compute(s);
+      }
+    });
   }
+  __syncthreads();
 
   // accumulator element e of block (i, j): row 8*(e/4) + 4*lhalf + e%4, column lrow
   if constexpr (!kStaged) {
@@ -314,11 +352,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
   } else {
     // Each wave stages one 32-row block of its tile at a time (row stride WTN + 8
     // floats: the two lane halves land on disjoint banks), then every lane
-    // handles 4 consecutive columns of one row.
+    // handles 4 consecutive columns of one row.  Waves 0-1 use the LDS of
+    // stage 0, waves 2-3 that of stage 1.
     constexpr int LD = WTN + 8;
     constexpr int LPR = WTN / 4;        // lanes per staged row
     constexpr int RPP = 64 / LPR;       // rows per pass
-    float* stage = reinterpret_cast<float*>(lds) + wave * 32 * LD;
+    static_assert(2 * 32 * LD * 4 <= STAGE_BYTES, "staging must fit in one stage");
+    float* stage = reinterpret_cast<float*>(wave < 2 ? stage_lds<STAGE_BYTES, 0>() : stage_lds<STAGE_BYTES, 1>()) +
+                   (wave & 1) * 32 * LD;
     const int cl = (lane % LPR) * 4;
     const int n = n0 + wn * WTN + cl;
     const int nvalid = min(4, N - n);
@@ -344,12 +385,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
   }
 }
 
-template <int BM, int BN, bool kStaged, class Epi>
+template <int BM, int BN, int S, bool kStaged, class Epi>
 hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
-  static_assert(2 * (BM + BN) * 8 * 16 >= 4 * 32 * (BN / 2 + 8) * 4, "staging must fit in the tile LDS");
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, kStaged, Epi>), dim3(tiles_m * tiles_n), dim3(256), 0, s, A, W, M, N,
-                     K, tiles_m, tiles_n, epi);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, S, kStaged, Epi>), dim3(tiles_m * tiles_n), dim3(256), 0, s, A, W, M,
+                     N, K, tiles_m, tiles_n, epi);
   return hipGetLastError();
 }
 
@@ -357,8 +397,8 @@ template <bool kStaged, class Epi>
 hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   // Few tiles: a smaller tile keeps more CUs busy.
   const long big_tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (big_tiles < 256) return run<64, 64, kStaged>(A, W, M, N, K, epi, s);
-  return run<128, 128, kStaged>(A, W, M, N, K, epi, s);
+  if (big_tiles < 256) return run<64, 64, GEMM_STAGES_SMALL, kStaged>(A, W, M, N, K, epi, s);
+  return run<128, 128, GEMM_STAGES, kStaged>(A, W, M, N, K, epi, s);
 }
 
 }  // namespace
