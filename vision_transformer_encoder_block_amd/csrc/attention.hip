@@ -14,7 +14,9 @@
 //
 // Q arrives pre-multiplied by log2(e)/8, so p = exp2(s - m) with s, m, the
 // running max and sum all fp32: logits of ~2.5e6 (the DINOv3 attention sink)
-// stay finite, and the largest key of every row gets p = exp2(0) = 1 exactly.
+// stay finite.  The reference max m is moved lazily (only when a tile max
+// exceeds it by more than 8), which keeps every p <= 2^8 and skips most
+// rescales of the output accumulators.
 // K and V^T tiles of 64 keys are staged in LDS (double-buffered, 16-byte
 // chunks XOR-swizzled by row) and shared by the 4 waves of a workgroup; rows
 // past the sequence end are read as zeros through buffer range checks.
@@ -128,21 +130,30 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
           if (key >= N) s[kb][e] = -INFINITY;
         }
     }
-    float mt = -INFINITY;
+    float mt = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
+      for (int e = (kb == 0); e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
     mt = half_swap_max(mt);
-    const float m_new = fmaxf(m_run, mt);  // finite: tile 0 always holds key 0
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    // Lazy rescaling: the reference max m_run only moves (and O, l are only
+    // rescaled) when some query's tile max exceeds it by more than 8, so
+    // p = exp2(s - m_run) <= 2^8.  Tile 0 always moves it (m_run = -inf, and
+    // tile 0 holds key 0).  Numerator and denominator share m_run, so the
+    // final O / l is unchanged.
+    const bool grow = mt > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      o[0][e] *= alpha;
-      o[1][e] *= alpha;
+      for (int e = 0; e < 16; ++e) {
+        o[0][e] *= alpha;
+        o[1][e] *= alpha;
+      }
     }
+    const float m_use = m_run;
     // probabilities, packed as the B operand of the 4 key steps of P V
     bf16x8 pf[4];
 #pragma unroll
@@ -152,7 +163,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = exp2f(s[kb][half * 8 + e] - m_new);
+          p[e] = __builtin_amdgcn_exp2f(s[kb][half * 8 + e] - m_use);
           l_run += p[e];
         }
         uint4 u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),

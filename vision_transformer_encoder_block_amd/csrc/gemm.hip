@@ -3,17 +3,18 @@
 //
 // Both operands are K-contiguous (activations [M, K], nn.Linear weights
 // [N, K]), so each lane of v_mfma_f32_32x32x16_bf16 reads 16 contiguous bytes
-// of one row for either operand.  A 256-thread workgroup (4 waves in 2 x 2)
-// computes a BM x BN tile; K advances in steps of 64 through a double-buffered
-// LDS tile.  Tiles are fetched with buffer loads whose range check returns 0
-// for rows past M or N, so ragged edges need no branches.  In LDS the 16-byte
-// chunk c of row r sits at chunk c ^ ((r >> 1) & 7): the 16 rows read together
-// by 16 consecutive lanes of one ds_read_b128 then cover all 64 banks.
-// Global loads for the next K step are in flight while the MFMAs of the
-// current step run.  The epilogue stages each wave's accumulators through LDS
-// so that every lane writes 4 consecutive columns of one row (coalesced
-// 8- or 16-byte stores).  Workgroup ids are remapped so that each XCD (8 per
-// chip, own L2) owns a contiguous range of tiles, grouped along M.
+// of one row for either operand.  A workgroup of WGM x WGN waves computes a
+// BM x BN tile.  K advances in steps of BK through S LDS stages filled by
+// direct-to-LDS buffer loads (no VGPR staging); the buffer range check returns
+// zeros for rows past M or N, so ragged edges need no branches.  In LDS the
+// 16-byte chunks of a row are XOR-swizzled so that the 16 rows read by 16
+// consecutive lanes of one ds_read_b128 hit distinct banks.  The epilogue
+// stages each wave's accumulators through LDS so that every lane writes 4
+// consecutive columns of one row (coalesced 8- or 16-byte stores).  Workgroup
+// ids are remapped so that each XCD (8 per chip, own L2) owns a contiguous
+// range of tiles, grouped along M.  Tile shapes were chosen by measurement on
+// MI355X: small tiles with several workgroups resident per CU beat large tiles
+// on the encoder's shapes (K = 384..4096, M = 4101..16404).
 #include "common.h"
 #include "kernels.h"
 
@@ -23,12 +24,6 @@ namespace vit {
 namespace {
 
 constexpr int BK = 64;
-#ifndef GEMM_STAGES
-#define GEMM_STAGES 3
-#endif
-#ifndef GEMM_STAGES_SMALL
-#define GEMM_STAGES_SMALL 3
-#endif
 
 // Division by a runtime constant for 0 <= n < 2^31 (multiply-high + shift).
 struct FastDiv {
@@ -226,23 +221,44 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // ---------------------------------------------------------------- kernel
-// S-stage pipeline: K steps of 64 arrive in LDS by direct-to-LDS buffer loads
-// (each wave instruction fills 1 KB = 8 rows x 128 B; every lane fetches the
-// logical chunk that belongs at its swizzled slot) issued S - 1 steps ahead.
+// S-stage pipeline: K steps of BK arrive in LDS by direct-to-LDS buffer loads
+// (each wave instruction fills 1 KB; every lane fetches the logical chunk that
+// belongs at its swizzled slot).  All S stages are requested up front; at the
+// end of step kt each wave waits for its own loads of step kt + 1, one barrier
+// publishes them (and retires step kt's buffer), the buffer is refilled with
+// step kt + S, the first fragments of step kt + 1 are read, and only then do
+// the last MFMAs of step kt issue, so the LDS latency of the next step hides
+// under them.
 
-template <int BM, int BN, int S, bool kStaged, class Epi>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
-                                                        int M, int N, int K, int tiles_m, int tiles_n, Epi epi) {
-  constexpr int TM = BM / 64, TN = BN / 64;     // 32x32 blocks per wave
-  constexpr int WTM = BM / 2, WTN = BN / 2;     // wave tile
-  constexpr int A_IT = BM / 32, B_IT = BN / 32; // DMA instructions per wave per stage
+// Chunk swizzle for rows of BK bf16 (BK / 8 chunks of 16 bytes): the 16 rows
+// read by 16 consecutive lanes of one ds_read_b128 hit distinct 4-bank groups.
+template <int BKT>
+__device__ __forceinline__ int swz_k(int r, int c) {
+  if constexpr (BKT == 64) return c ^ ((r >> 1) & 7);
+  else return c ^ (r & 15);
+}
+
+template <int BM, int BN, int BKT, int WGM, int WGN, int S, bool kStaged, class Epi>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t* __restrict__ A,
+                                                                  const bf16_t* __restrict__ W, int M, int N, int K,
+                                                                  int tiles_m, int tiles_n, Epi epi) {
+  constexpr int NW = WGM * WGN;                     // waves per workgroup
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;     // wave tile
+  constexpr int TM = WTM / 32, TN = WTN / 32;       // 32x32 blocks per wave
+  constexpr int CPR = BKT / 8;                      // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                     // rows per DMA instruction
+  constexpr int A_IT = BM / (RPI * NW), B_IT = BN / (RPI * NW);  // DMA instructions per wave per stage
   constexpr int L = A_IT + B_IT;
-  constexpr int STAGE_BYTES = (BM + BN) * 128;
-  static_assert(S >= 2 && (S - 1) * L < 64, "pipeline depth");
+  constexpr int KS = BKT / 16;                      // MFMA k-steps per stage
+  constexpr int STAGE_BYTES = (BM + BN) * BKT * 2;
+  static_assert(BKT == 64 || BKT == 128, "BK");
+  static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  static_assert(A_IT * RPI * NW == BM && B_IT * RPI * NW == BN, "DMA split");
+  static_assert(S >= 2 && S * L < 64, "pipeline depth");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -253,26 +269,26 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
   // byte offset (at k = 0) of the chunk this lane fetches in each DMA instruction
   uint32_t a_off[A_IT], b_off[B_IT];
   {
-    const int sub = lane >> 3, pc = lane & 7;
+    const int sub = lane / CPR, pc = lane % CPR;
 #pragma unroll
     for (int j = 0; j < A_IT; ++j) {
-      const int row = (j * 4 + wave) * 8 + sub;
-      a_off[j] = (uint32_t)(m0 + row) * (uint32_t)K * 2u + (uint32_t)swz(row, pc) * 16u;
+      const int row = (j * NW + wave) * RPI + sub;
+      a_off[j] = (uint32_t)(m0 + row) * (uint32_t)K * 2u + (uint32_t)swz_k<BKT>(row, pc) * 16u;
     }
 #pragma unroll
     for (int j = 0; j < B_IT; ++j) {
-      const int row = (j * 4 + wave) * 8 + sub;
-      b_off[j] = (uint32_t)(n0 + row) * (uint32_t)K * 2u + (uint32_t)swz(row, pc) * 16u;
+      const int row = (j * NW + wave) * RPI + sub;
+      b_off[j] = (uint32_t)(n0 + row) * (uint32_t)K * 2u + (uint32_t)swz_k<BKT>(row, pc) * 16u;
     }
   }
   auto issue = [&](auto stage, int kt) {
     const uint32_t blk = lds_addr(stage_lds<STAGE_BYTES, decltype(stage)::value>());
-    const uint32_t koff = (uint32_t)kt * (BK * 2);
+    const uint32_t koff = (uint32_t)kt * (BKT * 2);
 #pragma unroll
-    for (int j = 0; j < A_IT; ++j) dma16(ra_src, a_off[j] + koff, blk + (uint32_t)(j * 4 + wave_u) * 1024u);
+    for (int j = 0; j < A_IT; ++j) dma16(ra_src, a_off[j] + koff, blk + (uint32_t)(j * NW + wave_u) * 1024u);
 #pragma unroll
     for (int j = 0; j < B_IT; ++j)
-      dma16(rb_src, b_off[j] + koff, blk + (uint32_t)(BM * 128 + (j * 4 + wave_u) * 1024));
+      dma16(rb_src, b_off[j] + koff, blk + (uint32_t)(BM * BKT * 2 + (j * NW + wave_u) * 1024));
   };
 
   f32x16 acc[TM][TN];
@@ -283,54 +299,64 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int KT = K / BK;
+  const int KT = K / BKT;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  // Fragments of step ks + 1 are read from LDS while the MFMAs of step ks run.
-  auto compute = [&](auto stage) {
+  bf16x8 af[2][TM], bw[2][TN];
+  auto read = [&](auto stage, int buf, int ks) {
     const uint4* Ac = stage_lds<STAGE_BYTES, decltype(stage)::value>();
-    const uint4* Bc = Ac + BM * 8;
-    bf16x8 af[2][TM], bw[2][TN];
-    auto read = [&](int buf, int ks) {
-      const int qd = ks * 2 + lhalf;
+    const uint4* Bc = Ac + BM * CPR;
+    const int qd = ks * 2 + lhalf;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WTM + i * 32 + lrow;
-        af[buf][i] = as_bf16x8(Ac[r * 8 + swz(r, qd)]);
-      }
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * WTM + i * 32 + lrow;
+      af[buf][i] = as_bf16x8(Ac[r * CPR + swz_k<BKT>(r, qd)]);
+    }
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = wn * WTN + j * 32 + lrow;
-        bw[buf][j] = as_bf16x8(Bc[r * 8 + swz(r, qd)]);
-      }
-    };
-    read(0, 0);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < BK / 16) read(cur ^ 1, ks + 1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(af[cur][i], bw[cur][j], acc[i][j]);
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn * WTN + j * 32 + lrow;
+      bw[buf][j] = as_bf16x8(Bc[r * CPR + swz_k<BKT>(r, qd)]);
     }
   };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(af[buf][i], bw[buf][j], acc[i][j]);
+  };
+  // wait until at most `later` stages of this wave's loads are in flight
+  // (the ones issued after the stage being waited for)
+  auto wait_stages = [&](int later) {
+    static_for<0, S>([&](auto c) {
+      if (later == decltype(c)::value) wait_vm<decltype(c)::value * L>();
+    });
+  };
 
-  static_for<0, S - 1>([&](auto s) {
+  static_for<0, S>([&](auto s) {
     if (decltype(s)::value < KT) issue(s, decltype(s)::value);
   });
+  wait_stages(min(S - 1, KT - 1));  // steps 1 .. S-1 may still be in flight
+  barrier_keep_loads();
+  read(std::integral_constant<int, 0>{}, 0, 0);
+
   for (int kt0 = 0; kt0 < KT; kt0 += S) {
     static_for<0, S>([&](auto s) {
       constexpr int st = decltype(s)::value;
+      constexpr int nx = (st + 1) % S;
       const int kt = kt0 + st;
       if (kt < KT) {
-        // this wave's loads of stage st are done once at most `later` stages are in flight
-        const int later = min(S - 2, KT - 1 - kt);
-        static_for<0, S - 1>([&](auto c) {
-          if (later == decltype(c)::value) wait_vm<decltype(c)::value * L>();
-        });
-        barrier_keep_loads();  // every wave's loads of stage st have landed
-        if (kt + S - 1 < KT) issue(std::integral_constant<int, (st + S - 1) % S>{}, kt + S - 1);
-        compute(s);
+#pragma unroll
+        for (int ks = 0; ks + 1 < KS; ++ks) {
+          read(s, (ks + 1) & 1, ks + 1);
+          mma(ks & 1);
+        }
+        if (kt + 1 < KT) {
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave is done reading step kt
+          wait_stages(min(S - 2, KT - 2 - kt));  // steps kt + 2 .. kt + S - 1 may be in flight
+          barrier_keep_loads();                  // step kt + 1 visible, step kt's buffer free
+          if (kt + S < KT) issue(s, kt + S);
+          read(std::integral_constant<int, nx>{}, KS & 1, 0);
+        }
+        mma((KS - 1) & 1);
       }
     });
   }
@@ -352,14 +378,21 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
   } else {
     // Each wave stages one 32-row block of its tile at a time (row stride WTN + 8
     // floats: the two lane halves land on disjoint banks), then every lane
-    // handles 4 consecutive columns of one row.  Waves 0-1 use the LDS of
-    // stage 0, waves 2-3 that of stage 1.
+    // handles 4 consecutive columns of one row.  The staging areas live in the
+    // (now idle) LDS of the pipeline stages.
     constexpr int LD = WTN + 8;
-    constexpr int LPR = WTN / 4;        // lanes per staged row
-    constexpr int RPP = 64 / LPR;       // rows per pass
-    static_assert(2 * 32 * LD * 4 <= STAGE_BYTES, "staging must fit in one stage");
-    float* stage = reinterpret_cast<float*>(wave < 2 ? stage_lds<STAGE_BYTES, 0>() : stage_lds<STAGE_BYTES, 1>()) +
-                   (wave & 1) * 32 * LD;
+    constexpr int LPR = WTN / 4;                   // lanes per staged row
+    constexpr int RPP = 64 / LPR;                  // rows per pass
+    constexpr int PASSES = (32 + RPP - 1) / RPP;
+    constexpr int WAVE_BYTES = 32 * LD * 4;
+    constexpr int WPB = STAGE_BYTES / WAVE_BYTES;  // waves per stage object
+    static_assert(LPR <= 64, "staging pass shape");
+    static_assert(WPB >= 1 && WPB * S >= NW, "staging must fit in the stage LDS");
+    float* stage = nullptr;
+    static_for<0, S>([&](auto s) {
+      if (wave / WPB == decltype(s)::value)
+        stage = reinterpret_cast<float*>(stage_lds<STAGE_BYTES, decltype(s)::value>()) + (wave % WPB) * 32 * LD;
+    });
     const int cl = (lane % LPR) * 4;
     const int n = n0 + wn * WTN + cl;
     const int nvalid = min(4, N - n);
@@ -371,10 +404,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
         for (int e = 0; e < 16; ++e) stage[((e >> 2) * 8 + lhalf * 4 + (e & 3)) * LD + j * 32 + lrow] = acc[i][j][e];
       __syncthreads();
 #pragma unroll
-      for (int pass = 0; pass < 32 / RPP; ++pass) {
+      for (int pass = 0; pass < PASSES; ++pass) {
         const int r = pass * RPP + lane / LPR;
         const int m = m0 + wm * WTM + i * 32 + r;
-        if (m < M && nvalid > 0) {
+        if (lane < RPP * LPR && r < 32 && m < M && nvalid > 0) {
           const float4 t = *reinterpret_cast<const float4*>(stage + r * LD + cl);
           float v[4] = {t.x, t.y, t.z, t.w};
           epi.store4(m, n, v, nvalid);
@@ -385,20 +418,37 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict
   }
 }
 
-template <int BM, int BN, int S, bool kStaged, class Epi>
+// Tile configuration: BM x BN tile, WGM x WGN waves, S pipeline stages.
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int S_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, S = S_;
+};
+
+template <class C, bool kStaged, class Epi>
 hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, S, kStaged, Epi>), dim3(tiles_m * tiles_n), dim3(256), 0, s, A, W, M,
-                     N, K, tiles_m, tiles_n, epi);
+  const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
+  if (K % C::BK != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_bf16_kernel<C::BM, C::BN, C::BK, C::WGM, C::WGN, C::S, kStaged, Epi>), dim3(tiles_m * tiles_n),
+                     dim3(64 * C::WGM * C::WGN), 0, s, A, W, M, N, K, tiles_m, tiles_n, epi);
   return hipGetLastError();
 }
 
+#ifndef GEMM_CFG_BIG
+#define GEMM_CFG_BIG Cfg<256, 256, 64, 2, 4, 2>
+#endif
+#ifndef GEMM_CFG_SMALL
+#define GEMM_CFG_SMALL Cfg<64, 128, 64, 2, 2, 2>
+#endif
+#ifndef GEMM_BIG_LIMIT
+#define GEMM_BIG_LIMIT (8L * 1024 * 1024 * 4)
+#endif
+
 template <bool kStaged, class Epi>
 hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
-  // Few tiles: a smaller tile keeps more CUs busy.
-  const long big_tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (big_tiles < 256) return run<64, 64, GEMM_STAGES_SMALL, kStaged>(A, W, M, N, K, epi, s);
-  return run<128, 128, GEMM_STAGES, kStaged>(A, W, M, N, K, epi, s);
+  // Small tiles keep several workgroups resident per CU, which hides the
+  // per-tile load latency; only very large products use the big tile.
+  if ((long)M * N >= GEMM_BIG_LIMIT) return run<GEMM_CFG_BIG, kStaged>(A, W, M, N, K, epi, s);
+  return run<GEMM_CFG_SMALL, kStaged>(A, W, M, N, K, epi, s);
 }
 
 }  // namespace
