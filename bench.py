@@ -123,12 +123,13 @@ def kernel_breakdown(cfg, batch, steps=20, warmup=5):
     w2, b2 = rnd(D, Hm), rnd(D, dtype=torch.float32)
     f = torch.empty((M, Hm), dtype=bf, device="cuda")
     vit.vit_op_qkv(h, wqkv, bqkv, batch, N, H, q, k, vt)
+    attn_work = torch.empty(max(vit.vit_op_attention_workspace(batch, N, H), 4), dtype=torch.uint8, device="cuda")
     ops = {
         "layernorm": (lambda: vit.vit_op_layernorm(x, M, D, gam, bet, 1e-6, h, 0), 2 * L, 0.0,
                       M * D * (4 + 2) + 8 * D, "hbm"),
         "qkv": (lambda: vit.vit_op_qkv(h, wqkv, bqkv, batch, N, H, q, k, vt), L, 2.0 * M * D * 3 * D,
                 M * D * 2 + 3 * D * D * 2 + 3 * M * D * 2, "mfma"),
-        "attention": (lambda: vit.vit_op_attention(q, k, vt, batch, N, H, o), L, 4.0 * batch * N * N * D,
+        "attention": (lambda: vit.vit_op_attention(q, k, vt, batch, N, H, o, attn_work), L, 4.0 * batch * N * N * D,
                       4 * M * D * 2, "mfma"),
         "out_proj": (lambda: vit.vit_op_linear(o, wo, bo, M, D, D, vit.EPI_RESIDUAL, ls, x), L,
                      2.0 * M * D * D, M * D * 2 + D * D * 2 + 2 * M * D * 4, "mfma"),

@@ -58,9 +58,15 @@ int vit_op_qkv(const void* h, const void* wqkv, const float* bqkv, int batch, in
  * with the softmax over keys (LibreYOLO diagram, "Encoder self-attention";
  * the logits stay fp32, model card "Build BF16, not FP16").
  *   q, k, vt as produced by vit_op_qkv; o [batch, tokens, heads*64] bf16
- *   (heads merged in channel order). */
+ *   (heads merged in channel order).
+ *   work, work_bytes: device scratch for fp32 partial results; with at least
+ *   vit_op_attention_workspace(batch, tokens, heads) bytes the last, partly
+ *   filled query tile of every head may be spread over key ranges (better
+ *   load balance on long sequences).  NULL or too small: not spread.  The
+ *   result is the same up to fp32 rounding of the merge. */
+size_t vit_op_attention_workspace(int batch, int tokens, int heads);
 int vit_op_attention(const void* q, const void* k, const void* vt, int batch, int tokens, int heads,
-                     void* o, void* stream);
+                     void* o, void* work, size_t work_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ __all__ = [
     "LibraryMissing", "VitError", "VitConfig", "VitSizes", "lib", "config_from_dict", "pack_params",
     "vit_config_preset", "vit_plan", "vit_create", "vit_forward", "vit_descriptor", "vit_patch_scores",
     "vit_destroy", "vit_last_error", "vit_op_layernorm", "vit_op_linear", "vit_op_qkv", "vit_op_attention",
+    "vit_op_attention_workspace",
     "Encoder", "EPI_BIAS_BF16", "EPI_GELU_BF16", "EPI_RESIDUAL", "EPI_BIAS_F32",
 ]
 
@@ -80,7 +81,8 @@ _SIGNATURES = {
     "vit_op_layernorm": (_I, [_P, _I, _I, _P, _P, ctypes.c_float, _P, _I, _P]),
     "vit_op_linear": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "vit_op_qkv": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
-    "vit_op_attention": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
+    "vit_op_attention": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, ctypes.c_size_t, _P]),
+    "vit_op_attention_workspace": (ctypes.c_size_t, [_I, _I, _I]),
 }
 
 
@@ -183,9 +185,14 @@ def vit_op_qkv(h, wqkv, bqkv, batch, tokens, heads, q, k, vt, stream=None):
                                                  _ptr(k), _ptr(vt), _stream(stream)))
 
 
-def vit_op_attention(q, k, vt, batch, tokens, heads, o, stream=None):
+def vit_op_attention_workspace(batch, tokens, heads) -> int:
+    return lib().vit_op_attention_workspace(batch, tokens, heads)
+
+
+def vit_op_attention(q, k, vt, batch, tokens, heads, o, work=None, stream=None):
+    nbytes = 0 if work is None else work.numel() * work.element_size()
     return _check("vit_op_attention", lib().vit_op_attention(_ptr(q), _ptr(k), _ptr(vt), batch, tokens, heads,
-                                                             _ptr(o), _stream(stream)))
+                                                             _ptr(o), _ptr(work), nbytes, _stream(stream)))
 
 
 # ------------------------------------------------------------------ marshalling helpers

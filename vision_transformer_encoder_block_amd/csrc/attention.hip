@@ -23,6 +23,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace vit {
 namespace {
 
@@ -36,20 +38,41 @@ __device__ __forceinline__ int vt_tok(int p) { return (p & ~12) | ((p & 4) << 1)
 // ds_read_b128 cover all 64 banks.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-__global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
-                                                        const bf16_t* __restrict__ Vt, bf16_t* __restrict__ O,
-                                                        int N, int H, int nv) {
+// One workgroup: NW waves x 32 query rows starting at q_first + 32 NW blockIdx.x
+// (full pass) or at q_first (partial pass), against the keys of
+// [key_first, key_end).  The full pass writes the normalised output; the
+// partial pass writes this key range's running max, sum and unnormalised
+// output per row, merged afterwards by combine_kernel.
+struct AttnArgs {
+  const bf16_t* Q;
+  const bf16_t* K;
+  const bf16_t* Vt;
+  bf16_t* O;
+  float* part;     // partial pass: [B, H, splits, rows, 66] (m, l, o[64])
+  int N, H, nv;
+  int q_first;     // first query row of the launch
+  int part_rows;   // partial pass: rows per (b, h) in `part`
+  int keys_per_split;
+};
+
+template <int NW, bool kPartial>
+__global__ __launch_bounds__(64 * NW) void attention_kernel(AttnArgs a) {
+  constexpr int CH = 512 / (64 * NW);  // 16-byte chunks per thread per K (or V^T) tile
   __shared__ uint4 Ks[2][KT * 8];
   __shared__ uint4 Vs[2][64 * 8];
 
+  const int N = a.N, H = a.H, nv = a.nv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * H + h;
-  const bf16_t* Qp = Q + bh * N * 64;
-  const bf16_t* Kp = K + bh * N * 64;
-  const bf16_t* Vp = Vt + bh * 64 * nv;
+  const bf16_t* Qp = a.Q + bh * N * 64;
+  const bf16_t* Kp = a.K + bh * N * 64;
+  const bf16_t* Vp = a.Vt + bh * 64 * nv;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const int qrow = blockIdx.x * QT + wave * 32 + lrow;
+  const int split = kPartial ? blockIdx.x : 0;
+  const int qrow = a.q_first + (kPartial ? 0 : blockIdx.x * 32 * NW) + wave * 32 + lrow;
+  const int key_first = kPartial ? split * a.keys_per_split : 0;
+  const int key_end = kPartial ? min(N, key_first + a.keys_per_split) : N;
 
   // rows past N read as zeros through the buffer range checks
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qp, (uint32_t)N * 128u);
@@ -59,25 +82,23 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(buf_load16(rq, (uint32_t)qrow * 128u + ks * 32 + lhalf * 16));
 
-  // cooperative tile loads: 512 chunks of K and 512 of V^T, 2 + 2 per thread
-  int k_row[2], k_q[2], k_dst[2], v_row[2], v_q[2], v_dst[2];
+  // cooperative tile loads: 512 chunks of K and 512 of V^T
+  int k_dst[CH], v_dst[CH], row_c[CH], q_c[CH];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int cid = tid + c * 256;
-    k_row[c] = cid >> 3;
-    k_q[c] = cid & 7;
-    k_dst[c] = k_row[c] * 8 + swz(k_row[c], k_q[c]);
-    v_row[c] = cid >> 3;  // channel d
-    v_q[c] = cid & 7;     // 8 stored token positions
-    v_dst[c] = v_row[c] * 8 + swz(v_row[c], v_q[c]);
+  for (int c = 0; c < CH; ++c) {
+    const int cid = tid + c * 64 * NW;
+    row_c[c] = cid >> 3;  // key row of K / channel row of V^T
+    q_c[c] = cid & 7;     // 16-byte chunk
+    k_dst[c] = row_c[c] * 8 + swz(row_c[c], q_c[c]);
+    v_dst[c] = k_dst[c];
   }
   auto load_tile = [&](int t, uint4* rk, uint4* rv) {
     const int k0 = t * KT;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      rk[c] = buf_load16(rk_src, (uint32_t)(k0 + k_row[c]) * 128u + k_q[c] * 16);
-      const int p0 = k0 + v_q[c] * 8;  // < nv: nv is a multiple of 64
-      uint4 u = buf_load16(rv_src, ((uint32_t)v_row[c] * nv + p0) * 2u);
+    for (int c = 0; c < CH; ++c) {
+      rk[c] = buf_load16(rk_src, (uint32_t)(k0 + row_c[c]) * 128u + q_c[c] * 16);
+      const int p0 = k0 + q_c[c] * 8;  // < nv: nv is a multiple of 64
+      uint4 u = buf_load16(rv_src, ((uint32_t)row_c[c] * nv + p0) * 2u);
       if (k0 + KT > N) {  // last tile: zero the positions of keys >= N
         uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -94,32 +115,45 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
 #pragma unroll
   for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = 0.f;
 
-  const int ntiles = (N + KT - 1) / KT;
-  uint4 rk[2], rv[2];
-  load_tile(0, rk, rv);
+  // key ranges start on a tile boundary; only the global last tile is ragged
+  const int t_first = key_first / KT;
+  const int t_end = (key_end + KT - 1) / KT;
+  uint4 rk[CH], rv[CH];
+  load_tile(t_first, rk, rv);
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < CH; ++c) {
     Ks[0][k_dst[c]] = rk[c];
     Vs[0][v_dst[c]] = rv[c];
   }
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1, rk, rv);
+  for (int t = t_first; t < t_end; ++t) {
+    const int cur = (t - t_first) & 1;
+    if (t + 1 < t_end) load_tile(t + 1, rk, rv);
 
-    // S^T for keys t*64 + kb*32 + [0, 32): element e <-> key 8*(e/4) + 4*lhalf + e%4
+    // S^T for keys t*64 + kb*32 + [0, 32): element e <-> key 8*(e/4) + 4*lhalf + e%4.
+    // All K fragments are read before the MFMAs, and the V fragments right
+    // after them, so the LDS latency of both hides under MFMA and softmax work.
+    bf16x8 kf[2][4], vf[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int r = kb * 32 + lrow;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[kb][ks] = as_bf16x8(Ks[cur][r * 8 + swz(r, ks * 2 + lhalf)]);
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int r = db * 32 + lrow;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) vf[db][ks] = as_bf16x8(Vs[cur][r * 8 + swz(r, ks * 2 + lhalf)]);
+    }
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-      const int r = kb * 32 + lrow;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int qd = ks * 2 + lhalf;
-        s[kb] = mfma32x32x16(as_bf16x8(Ks[cur][r * 8 + swz(r, qd)]), qf[ks], s[kb]);
-      }
+      for (int ks = 0; ks < 4; ++ks) s[kb] = mfma32x32x16(kf[kb][ks], qf[ks], s[kb]);
     }
     if ((t + 1) * KT > N) {
 #pragma unroll
@@ -173,18 +207,13 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
     }
     // O^T[d, q] += V^T[d, keys] P^T[keys, q]; d = db*32 + row of the MFMA
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      const int r = db * 32 + lrow;
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int qd = ks * 2 + lhalf;
-        o[db] = mfma32x32x16(as_bf16x8(Vs[cur][r * 8 + swz(r, qd)]), pf[ks], o[db]);
-      }
-    }
+      for (int ks = 0; ks < 4; ++ks) o[db] = mfma32x32x16(vf[db][ks], pf[ks], o[db]);
 
-    if (t + 1 < ntiles) {
+    if (t + 1 < t_end) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < CH; ++c) {
         Ks[cur ^ 1][k_dst[c]] = rk[c];
         Vs[cur ^ 1][v_dst[c]] = rv[c];
       }
@@ -192,30 +221,146 @@ __global__ __launch_bounds__(256) void attention_kernel(const bf16_t* __restrict
     __syncthreads();
   }
 
-  const float l = half_swap_sum(l_run);
-  const float inv = 1.0f / l;
-  if (qrow < N) {
-    bf16_t* op = O + ((size_t)b * N + qrow) * (size_t)(H * 64) + h * 64;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = db * 32 + i * 8 + lhalf * 4;
-        uint2 u = make_uint2(pack_bf16x2(o[db][i * 4 + 0] * inv, o[db][i * 4 + 1] * inv),
-                             pack_bf16x2(o[db][i * 4 + 2] * inv, o[db][i * 4 + 3] * inv));
-        *reinterpret_cast<uint2*>(op + d) = u;
+  if constexpr (kPartial) {
+    // per row: max, sum (both halves) and the unnormalised output
+    const float l = half_swap_sum(l_run);
+    const int row_t = qrow - a.q_first;
+    if (qrow < N) {
+      float* pp = a.part + (((size_t)bh * gridDim.x + split) * a.part_rows + row_t) * 66;
+      if (lhalf == 0) {
+        pp[0] = m_run;
+        pp[1] = l;
       }
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = db * 32 + i * 8 + lhalf * 4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pp[2 + d + j] = o[db][i * 4 + j];
+        }
+    }
+  } else {
+    const float l = half_swap_sum(l_run);
+    const float inv = 1.0f / l;
+    if (qrow < N) {
+      bf16_t* op = a.O + ((size_t)b * N + qrow) * (size_t)(H * 64) + h * 64;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = db * 32 + i * 8 + lhalf * 4;
+          uint2 u = make_uint2(pack_bf16x2(o[db][i * 4 + 0] * inv, o[db][i * 4 + 1] * inv),
+                               pack_bf16x2(o[db][i * 4 + 2] * inv, o[db][i * 4 + 3] * inv));
+          *reinterpret_cast<uint2*>(op + d) = u;
+        }
+    }
   }
+}
+
+// Merge the key-range partials of the tail rows: M = max m_i,
+// O = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.  One thread per (row, channel).
+__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part, int splits, int rows, int q_first,
+                                                     int N, int H, bf16_t* __restrict__ O) {
+  const int d = threadIdx.x;
+  const int row_t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const size_t bh = (size_t)b * H + h;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part[((bh * splits + s) * rows + row_t) * 66]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* pp = part + ((bh * splits + s) * rows + row_t) * 66;
+    const float w = __builtin_amdgcn_exp2f(pp[0] - M);
+    L += w * pp[1];
+    acc += w * pp[2 + d];
+  }
+  O[((size_t)b * N + q_first + row_t) * (size_t)(H * 64) + h * 64 + d] = f2bf(acc / L);
+}
+
+// Tail split: the last, partly filled query tile of every head can form an
+// extra round of workgroups (e.g. 4101 tokens x 16 heads = 528 tiles on 256
+// CUs).  When that is so, its rows are instead processed against key ranges by
+// small workgroups (about one per CU) and merged by combine_kernel.
+constexpr int kMaxSplits = 16;
+
+struct TailPlan {
+  int full_rows = 0;   // rows covered by the full-tile pass
+  int tail_rows = 0;   // rows handled by the split pass (< 128)
+  int waves = 0;       // waves per split workgroup (32 rows each)
+  int splits = 0;
+  int keys_per_split = 0;
+};
+
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || n <= 0)
+      n = 256;
+    cus = n;
+  }
+  return cus;
+}
+
+TailPlan plan_tail(int batch, int heads, int tokens) {
+  TailPlan p;
+  p.full_rows = tokens;
+  const int full = tokens / QT, tail = tokens - full * QT;
+  if (full == 0 || tail == 0) return p;
+  const long units = (long)batch * heads;
+  const int cus = device_cus();
+  const long rounds_all = (units * (full + 1) + cus - 1) / cus;
+  const long rounds_full = (units * full + cus - 1) / cus;
+  if (rounds_full >= rounds_all) return p;
+  p.full_rows = full * QT;
+  p.tail_rows = tail;
+  p.waves = tail <= 32 ? 1 : (tail <= 64 ? 2 : 4);
+  const int max_splits = (tokens + KT - 1) / KT;
+  const int want = (int)std::max<long>(1, std::min<long>(std::min(max_splits, kMaxSplits), (cus + units - 1) / units));
+  p.keys_per_split = ((tokens + want - 1) / want + KT - 1) / KT * KT;
+  p.splits = (tokens + p.keys_per_split - 1) / p.keys_per_split;
+  return p;
 }
 
 }  // namespace
 
+// Upper bound of the split-pass partials for any device (pure host function).
+size_t attention_workspace_bytes(int batch, int tokens, int heads) {
+  const int full = tokens / QT, tail = tokens - full * QT;
+  if (full == 0 || tail == 0) return 0;
+  const int splits = std::min(kMaxSplits, (tokens + KT - 1) / KT);
+  return (size_t)batch * heads * splits * tail * 66 * sizeof(float);
+}
+
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
-                            int heads, int nv, uint16_t* o, hipStream_t s) {
+                            int heads, int nv, uint16_t* o, float* work, size_t work_bytes, hipStream_t s) {
   if (batch <= 0 || tokens <= 0 || heads <= 0 || nv < tokens || nv % 64 != 0) return hipErrorInvalidValue;
   if ((size_t)nv * 128 >= (1ull << 32)) return hipErrorInvalidValue;
-  dim3 grid((tokens + QT - 1) / QT, heads, batch);
-  hipLaunchKernelGGL(attention_kernel, grid, dim3(256), 0, s, q, k, vt, o, tokens, heads, nv);
+  TailPlan p = plan_tail(batch, heads, tokens);
+  if (p.tail_rows && (work == nullptr || work_bytes < attention_workspace_bytes(batch, tokens, heads))) {
+    p.full_rows = tokens;  // no workspace: the last tile stays in the main pass
+    p.tail_rows = 0;
+  }
+  AttnArgs a{q, k, vt, o, work, tokens, heads, nv, 0, 0, 0};
+  dim3 grid((p.full_rows + QT - 1) / QT, heads, batch);
+  hipLaunchKernelGGL((attention_kernel<4, false>), grid, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.tail_rows == 0) return e;
+  a.q_first = p.full_rows;
+  a.part_rows = p.tail_rows;
+  a.keys_per_split = p.keys_per_split;
+  const dim3 pgrid(p.splits, heads, batch);
+  if (p.waves == 1)
+    hipLaunchKernelGGL((attention_kernel<1, true>), pgrid, dim3(64), 0, s, a);
+  else if (p.waves == 2)
+    hipLaunchKernelGGL((attention_kernel<2, true>), pgrid, dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL((attention_kernel<4, true>), pgrid, dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3(p.tail_rows, heads, batch), dim3(64), 0, s, (const float*)work, p.splits,
+                     p.tail_rows, p.full_rows, tokens, heads, o);
   return hipGetLastError();
 }
 

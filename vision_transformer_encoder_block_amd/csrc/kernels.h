@@ -72,9 +72,11 @@ hipError_t launch_assemble(float* x, int batch, int tokens, int dim, const float
 hipError_t launch_pos_resample(const float* pos_in, int gh, int gw, float* pos_out, int th, int tw, int dim,
                                hipStream_t s);
 
-// Attention core (see vit_op_attention).
+// Attention core (see vit_op_attention).  `work` (fp32 partials of the tail
+// split) may be null, in which case the split is not used.
+size_t attention_workspace_bytes(int batch, int tokens, int heads);
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
-                            int heads, int nv, uint16_t* o, hipStream_t s);
+                            int heads, int nv, uint16_t* o, float* work, size_t work_bytes, hipStream_t s);
 
 // fp32 -> bf16 (nearest even) of n values.
 hipError_t launch_to_bf16(const float* x, size_t n, uint16_t* y, hipStream_t s);

@@ -80,7 +80,8 @@ struct WeightLayout {
 };
 
 struct WorkLayout {
-  size_t x, h, q, k, vt, o, f, cols, crops, feats, clsb, cos, corners, total;
+  size_t x, h, q, k, vt, o, f, cols, attn, crops, feats, clsb, cos, corners, total;
+  size_t attn_bytes;
   int ldc_cos;
 };
 
@@ -232,6 +233,9 @@ int build_plan(const vit_config* c, Plan& pl) {
   s.o = take(rows * D * 2);
   s.f = take(rows * Hm * 2);
   s.cols = take(prows * pl.kpad * 2);
+  s.attn_bytes = std::max(vit::attention_workspace_bytes(c->max_batch, pl.main.N, pl.heads),
+                          pl.nwin ? vit::attention_workspace_bytes(pl.nwin, pl.win.N, pl.heads) : (size_t)0);
+  s.attn = take(std::max<size_t>(s.attn_bytes, 4));
   s.ldc_cos = round_up(std::max(c->max_classes, 1), 4);
   if (c->max_classes > 0) {
     const size_t frows = std::max((size_t)pl.main.P, prow_win);
@@ -270,6 +274,7 @@ struct vit_model {
   std::vector<BlockW> blocks;
   float* x = nullptr;
   uint16_t *h = nullptr, *q = nullptr, *k = nullptr, *vt = nullptr, *o = nullptr, *f = nullptr, *cols = nullptr;
+  float* attn = nullptr;
   float *crops = nullptr, *cos = nullptr;
   uint16_t *feats = nullptr, *clsb = nullptr;
   int* corners = nullptr;
@@ -312,7 +317,8 @@ int run_encoder(vit_model* m, const Geom& g, const float* images, int batch, flo
     eq.heads = pl.heads;
     eq.nv = g.nv;
     VIT_HIP(vit::launch_gemm(m->h, w.wqkv, M, 3 * D, D, eq, st), "qkv");
-    VIT_HIP(vit::launch_attention(m->q, m->k, m->vt, batch, N, pl.heads, g.nv, m->o, st), "attention");
+    VIT_HIP(vit::launch_attention(m->q, m->k, m->vt, batch, N, pl.heads, g.nv, m->o, m->attn, pl.ws.attn_bytes, st),
+            "attention");
     vit::EpiParams eo;
     eo.kind = vit::EPI_RESIDUAL;
     eo.bias = w.bo;
@@ -497,6 +503,7 @@ int vit_create(const vit_config* cfg, const float* host_params, size_t host_floa
   m->o = (uint16_t*)(S + ws.o);
   m->f = (uint16_t*)(S + ws.f);
   m->cols = (uint16_t*)(S + ws.cols);
+  m->attn = (float*)(S + ws.attn);
   if (pl.cfg.max_classes > 0) {
     m->crops = pl.nwin ? (float*)(S + ws.crops) : nullptr;
     m->feats = (uint16_t*)(S + ws.feats);
@@ -638,12 +645,17 @@ int vit_op_qkv(const void* h, const void* wqkv, const float* bqkv, int batch, in
   return VIT_OK;
 }
 
+size_t vit_op_attention_workspace(int batch, int tokens, int heads) {
+  if (batch < 1 || tokens < 1 || heads < 1) return 0;
+  return vit::attention_workspace_bytes(batch, tokens, heads);
+}
+
 int vit_op_attention(const void* q, const void* k, const void* vt, int batch, int tokens, int heads, void* o,
-                     void* stream) {
+                     void* work, size_t work_bytes, void* stream) {
   if (!q || !k || !vt || !o) return fail(VIT_ERR_ARG, "NULL pointer");
   if (batch < 1 || tokens < 1 || heads < 1 || heads > 64) return fail(VIT_ERR_SHAPE, "bad batch/tokens/heads");
   VIT_HIP(vit::launch_attention((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, batch, tokens, heads,
-                                round_up(tokens, 64), (uint16_t*)o, (hipStream_t)stream),
+                                round_up(tokens, 64), (uint16_t*)o, (float*)work, work_bytes, (hipStream_t)stream),
           "attention");
   return VIT_OK;
 }
