@@ -188,7 +188,7 @@ def test_vitl16_1024_b4_batch_invariance(vitl):
 
 # ------------------------------------------------------------------ zero-shot scoring
 
-COS_TOL = 5e-3
+COS_TOL = 2.5e-3  # bf16 feature rounding bound 2^-9 (Cauchy-Schwarz) + final-LN error
 
 
 def check_labels(got, score, tol):

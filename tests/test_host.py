@@ -124,7 +124,7 @@ def test_create_and_calls_validate_before_touching_the_device(L):
     assert lib.vit_op_linear(fake, fake, fake, 4, 4, 63, 0, None, fake, None) == -2
     assert lib.vit_op_layernorm(fake, 4, 100, fake, fake, ctypes.c_float(1e-6), fake, 0, None) == -2
     assert lib.vit_op_attention(None, fake, fake, 1, 4, 1, fake, None, 0, None) == -1
-    assert vit.vit_op_attention_workspace(1, 100, 6) == 0           # no full 128-row tile: never split
-    assert vit.vit_op_attention_workspace(1, 446, 6) == 6 * 7 * 62 * 66 * 4
-    assert vit.vit_op_attention_workspace(1, 4101, 16) == 16 * 16 * 5 * 66 * 4
+    assert vit.vit_op_attention_workspace(1, 446, 6) == 0            # short sequences are never split
+    assert vit.vit_op_attention_workspace(2, 1370, 6) == 2 * 6 * 11 * 90 * 66 * 4   # 11 ranges of 128 keys
+    assert vit.vit_op_attention_workspace(1, 4101, 16) == 16 * 13 * 5 * 66 * 4      # 13 ranges of 320 keys
     assert lib.vit_destroy(None) == 0

@@ -277,11 +277,15 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
   O[((size_t)b * N + q_first + row_t) * (size_t)(H * 64) + h * 64 + d] = f2bf(acc / L);
 }
 
-// Tail split: the last, partly filled query tile of every head can form an
-// extra round of workgroups (e.g. 4101 tokens x 16 heads = 528 tiles on 256
-// CUs).  When that is so, its rows are instead processed against key ranges by
-// small workgroups (about one per CU) and merged by combine_kernel.
+// Tail split: on long sequences the last, partly filled query tile of every
+// head would run as a full-length workgroup that mostly idles and, on many
+// shapes, forms an extra round of workgroups (e.g. 4101 tokens x 16 heads =
+// 528 tiles on 256 CUs).  Its rows are instead processed against up to 16 key
+// ranges by small workgroups and merged by combine_kernel.  The decision and
+// the number of ranges depend on the sequence length only, so an image gives
+// bit-identical results at every batch size.
 constexpr int kMaxSplits = 16;
+constexpr int kSplitMinTokens = 1024;
 
 struct TailPlan {
   int full_rows = 0;   // rows covered by the full-tile pass
@@ -291,33 +295,15 @@ struct TailPlan {
   int keys_per_split = 0;
 };
 
-int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || n <= 0)
-      n = 256;
-    cus = n;
-  }
-  return cus;
-}
-
-TailPlan plan_tail(int batch, int heads, int tokens) {
+TailPlan plan_tail(int tokens) {
   TailPlan p;
   p.full_rows = tokens;
   const int full = tokens / QT, tail = tokens - full * QT;
-  if (full == 0 || tail == 0) return p;
-  const long units = (long)batch * heads;
-  const int cus = device_cus();
-  const long rounds_all = (units * (full + 1) + cus - 1) / cus;
-  const long rounds_full = (units * full + cus - 1) / cus;
-  if (rounds_full >= rounds_all) return p;
+  if (tokens < kSplitMinTokens || tail == 0) return p;
   p.full_rows = full * QT;
   p.tail_rows = tail;
   p.waves = tail <= 32 ? 1 : (tail <= 64 ? 2 : 4);
-  const int max_splits = (tokens + KT - 1) / KT;
-  const int want = (int)std::max<long>(1, std::min<long>(std::min(max_splits, kMaxSplits), (cus + units - 1) / units));
+  const int want = std::min(kMaxSplits, (tokens + KT - 1) / KT);
   p.keys_per_split = ((tokens + want - 1) / want + KT - 1) / KT * KT;
   p.splits = (tokens + p.keys_per_split - 1) / p.keys_per_split;
   return p;
@@ -325,19 +311,17 @@ TailPlan plan_tail(int batch, int heads, int tokens) {
 
 }  // namespace
 
-// Upper bound of the split-pass partials for any device (pure host function).
+// Bytes of the split-pass partials (pure host function).
 size_t attention_workspace_bytes(int batch, int tokens, int heads) {
-  const int full = tokens / QT, tail = tokens - full * QT;
-  if (full == 0 || tail == 0) return 0;
-  const int splits = std::min(kMaxSplits, (tokens + KT - 1) / KT);
-  return (size_t)batch * heads * splits * tail * 66 * sizeof(float);
+  const TailPlan p = plan_tail(tokens);
+  return p.tail_rows ? (size_t)batch * heads * p.splits * p.tail_rows * 66 * sizeof(float) : 0;
 }
 
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
                             int heads, int nv, uint16_t* o, float* work, size_t work_bytes, hipStream_t s) {
   if (batch <= 0 || tokens <= 0 || heads <= 0 || nv < tokens || nv % 64 != 0) return hipErrorInvalidValue;
   if ((size_t)nv * 128 >= (1ull << 32)) return hipErrorInvalidValue;
-  TailPlan p = plan_tail(batch, heads, tokens);
+  TailPlan p = plan_tail(tokens);
   if (p.tail_rows && (work == nullptr || work_bytes < attention_workspace_bytes(batch, tokens, heads))) {
     p.full_rows = tokens;  // no workspace: the last tile stays in the main pass
     p.tail_rows = 0;
