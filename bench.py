@@ -209,6 +209,67 @@ def cpu_baseline(budget_s=12.0, max_images=32):
                 sample=f"{done} ViT-S/16@336 images (float64 NumPy oracle, batches of {chunk}), {dt:.1f} s")
 
 
+def copy_calibration(mib=256, reps=3):
+    """A plain device copy of known size, so HBM counters can be scaled."""
+    import torch
+    src = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return mib
+
+
+# op -> (kernel-name substring, grid size at ViT-S/16@336 b32 or None)
+PMC_OPS = {
+    "fc1": ("EpiGeluBf16", None),
+    "attention": ("attention_kernel", None),
+    "layernorm": ("layernorm_kernel", None),
+}
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_mib=256):
+    """Per-dispatch HBM bytes of the block kernels from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE in KiB), scaled by the same counters on a plain copy
+    of known size; written to profiles/hbm_traffic.json with the source digest."""
+    import csv
+
+    def load(path, counter):
+        rows = {}
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name") != counter:
+                continue
+            rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return rows
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+
+    def avg(table, sub):
+        vals = [v for k, vs in table.items() if sub in k for v in vs]
+        return sum(vals) / len(vals) if vals else None
+
+    def copy_avg(table):
+        vals = [v for k, vs in table.items() if ("copy" in k.lower() or "elementwise" in k.lower()) for v in vs]
+        vals = sorted(vals)[-3:]  # the three large calibration copies
+        return sum(vals) / len(vals) if vals else None
+
+    expect_kib = copy_mib * 1024.0
+    cf, cw = copy_avg(fetch), copy_avg(write)
+    scale_f = expect_kib / cf if cf else None
+    scale_w = expect_kib / cw if cw else None
+    out = {"source_digest": _source_digest(), "copy_mib": copy_mib, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "scale_fetch": scale_f, "scale_write": scale_w, "ops": {}}
+    for op, (sub, _) in PMC_OPS.items():
+        f, w = avg(fetch, sub), avg(write, sub)
+        if f is None or w is None or scale_f is None or scale_w is None:
+            continue
+        out["ops"][op] = {"kernel_substring": sub, "fetch_kib": f, "write_kib": w,
+                          "bytes_per_launch": (f * scale_f + w * scale_w) * 1024.0}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
 KERNEL_NAMES = {
     "qkv": "gemm_bf16_kernel<EpiQKV>",
     "attention": "attention_kernel",
@@ -226,7 +287,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-large", action="store_true", help="skip the ViT-L/16 @1024 b1 line")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (for scaling HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: turn two rocprofv3 --pmc CSVs into profiles/hbm_traffic.json")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the encoder path is single-GPU (images are independent, "
               "so several GPUs would each run their own batch); run with --gpus 1", file=sys.stderr)
@@ -234,6 +302,8 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
 
+    if args.copy_calibration:
+        copy_calibration()
     log("ViT-S/16 @336 b32 ...")
     cfg, enc, small = bench_workload("vits16_336", 32, args.steps, args.warmup)
     enc.close()
