@@ -187,7 +187,7 @@ def traffic_for(op):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
-def cpu_baseline(budget_s=12.0, max_images=32):
+def cpu_baseline(budget_s=15.0, max_images=128):
     """The oracle (float64 NumPy), untuned, on ViT-S/16 @336 images until the budget is spent."""
     import synth
     from oracle import vit_oracle as O
