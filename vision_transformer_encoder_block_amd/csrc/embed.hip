@@ -8,9 +8,12 @@
 namespace vit {
 namespace {
 
-// One thread writes 8 consecutive columns (16 bytes) of one patch row.
+// One thread writes 8 consecutive columns (16 bytes) of one patch row.  The
+// (c, ky, kx) of the first column is decoded once and then stepped; when the
+// 8 columns lie in one image row (vec4: p a multiple of 8, W a multiple of 4
+// and img 16-byte aligned, checked on the host) they are two float4 loads.
 __global__ __launch_bounds__(256) void patchify_kernel(const float* __restrict__ img, int batch, int H, int W, int p,
-                                                       int kpad, bf16_t* __restrict__ out) {
+                                                       int kpad, bool vec4, bf16_t* __restrict__ out) {
   const int gw = W / p, gh = H / p;
   const int chunks = kpad / 8;
   const size_t total = (size_t)batch * gh * gw * chunks;
@@ -22,18 +25,34 @@ __global__ __launch_bounds__(256) void patchify_kernel(const float* __restrict__
   const int gy = (int)((prow / gw) % gh);
   const int b = (int)(prow / ((size_t)gw * gh));
   const int kvalid = 3 * p * p;
+  const int k0 = ch * 8;
   float v[8];
+  if (k0 >= kvalid) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int k = ch * 8 + e;
-    float x = 0.f;
-    if (k < kvalid) {
-      const int c = k / (p * p);
-      const int r = k - c * p * p;
-      const int ky = r / p, kx = r - ky * p;
-      x = img[(((size_t)b * 3 + c) * H + gy * p + ky) * W + gx * p + kx];
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  } else {
+    int c = k0 / (p * p);
+    int r = k0 - c * p * p;
+    int ky = r / p, kx = r - ky * p;
+    const float* base = img + (size_t)b * 3 * H * W + (size_t)(gy * p) * W + gx * p;
+    if (vec4 && k0 + 8 <= kvalid) {
+      const float4* src = reinterpret_cast<const float4*>(base + ((size_t)c * H + ky) * W + kx);
+      const float4 lo = src[0], hi = src[1];
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = (k0 + e < kvalid) ? base[((size_t)c * H + ky) * W + kx] : 0.f;
+        if (++kx == p) {
+          kx = 0;
+          if (++ky == p) {
+            ky = 0;
+            ++c;
+          }
+        }
+      }
     }
-    v[e] = x;
   }
   uint4 u = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                        pack_bf16x2(v[6], v[7]));
@@ -114,8 +133,9 @@ hipError_t launch_patchify(const float* img, int batch, int H, int W, int p, int
                            hipStream_t s) {
   if (kpad % 8 != 0 || kpad < 3 * p * p) return hipErrorInvalidValue;
   const size_t total = (size_t)batch * (H / p) * (W / p) * (kpad / 8);
+  const bool vec4 = (p % 8) == 0 && (W % 4) == 0 && (reinterpret_cast<uintptr_t>(img) % 16) == 0;
   hipLaunchKernelGGL(patchify_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, img, batch, H, W, p,
-                     kpad, out);
+                     kpad, vec4, out);
   return hipGetLastError();
 }
 

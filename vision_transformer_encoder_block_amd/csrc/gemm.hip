@@ -84,6 +84,9 @@ struct EpiBiasBf16 {
       for (int i = 0; i < nvalid; ++i) p[i] = f2bf(v[i]);
     }
   }
+  struct Col { float b; };
+  __device__ Col col(int n) const { return {bias ? bias[n] : 0.f}; }
+  __device__ void store(int m, int n, float v, const Col& c) const { out[(size_t)m * ldc + n] = f2bf(v + c.b); }
 };
 
 struct EpiGeluBf16 {
@@ -104,6 +107,9 @@ struct EpiGeluBf16 {
       for (int i = 0; i < nvalid; ++i) p[i] = f2bf(gelu_erf(v[i] + bias[n + i]));
     }
   }
+  struct Col { float b; };
+  __device__ Col col(int n) const { return {bias[n]}; }
+  __device__ void store(int m, int n, float v, const Col& c) const { out[(size_t)m * ldc + n] = f2bf(gelu_erf(v + c.b)); }
 };
 
 struct EpiResidual {
@@ -127,6 +133,12 @@ struct EpiResidual {
       for (int i = 0; i < nvalid; ++i) p[i] = p[i] + ls[n + i] * (v[i] + bias[n + i]);
     }
   }
+  struct Col { float b, s; };
+  __device__ Col col(int n) const { return {bias[n], ls[n]}; }
+  __device__ void store(int m, int n, float v, const Col& c) const {
+    float* p = out + (size_t)m * ldc + n;
+    *p = *p + c.s * (v + c.b);
+  }
 };
 
 struct EpiBiasF32 {
@@ -143,6 +155,9 @@ struct EpiBiasF32 {
       for (int i = 0; i < nvalid; ++i) p[i] = v[i];
     }
   }
+  struct Col { float b; };
+  __device__ Col col(int n) const { return {bias ? bias[n] : 0.f}; }
+  __device__ void store(int m, int n, float v, const Col& c) const { out[(size_t)m * ldc + n] = v + c.b; }
 };
 
 // Q and K columns (n < 2D) of the fused projection: head-major rows of 64.
@@ -166,6 +181,18 @@ struct EpiQK {
     float o[4] = {(v[0] + bb.x) * s, (v[1] + bb.y) * s, (v[2] + bb.z) * s, (v[3] + bb.w) * s};
     *reinterpret_cast<uint2*>((which ? k : q) + row * 64 + d) = pack4_bf16(o);
   }
+  struct Col { float b, s; int which, head, d; };
+  __device__ Col col(int n) const {
+    const int which = n >= D;
+    const int c = n - which * D;
+    return {bias[n], which ? 1.f : qscale, which, c >> 6, c & 63};
+  }
+  __device__ void store(int m, int n, float v, const Col& c) const {
+    const int b = (int)fdiv((uint32_t)m, divN);
+    const int tok = m - b * N;
+    const size_t row = ((size_t)b * heads + c.head) * N + tok;
+    (c.which ? k : q)[row * 64 + c.d] = f2bf((v + c.b) * c.s);
+  }
 };
 
 struct EpiPatch {
@@ -184,6 +211,14 @@ struct EpiPatch {
     *reinterpret_cast<float4*>(out + row * D + n) =
         make_float4(v[0] + bb.x + pp.x, v[1] + bb.y + pp.y, v[2] + bb.z + pp.z, v[3] + bb.w + pp.w);
   }
+  struct Col { float b; };
+  __device__ Col col(int n) const { return {bias[n]}; }
+  __device__ void store(int m, int n, float v, const Col& c) const {
+    const int b = (int)fdiv((uint32_t)m, divP);
+    const int i = m - b * patches;
+    const size_t row = (size_t)b * tokens + 1 + regs + i;
+    out[row * D + n] = v + c.b + pos[(size_t)(1 + i) * D + n];
+  }
 };
 
 // V columns, computed transposed (A = wv rows, W = token rows): element (m, n)
@@ -194,11 +229,14 @@ struct EpiVt {
   bf16_t* vt;
   int N, heads, nv;
   FastDiv divN;
-  __device__ void store(int m, int n, float v) const {
+  struct Col { int b, col; };  // image and vt column of token row n
+  __device__ Col col(int n) const {
     const int b = (int)fdiv((uint32_t)n, divN);
-    const int tok = n - b * N;
+    return {b, vt_pos(n - b * N)};
+  }
+  __device__ void store(int m, int n, float v, const Col& c) const {
     const int head = m >> 6, d = m & 63;
-    vt[(((size_t)b * heads + head) * 64 + d) * nv + vt_pos(tok)] = f2bf(v + bias[m]);
+    vt[(((size_t)c.b * heads + head) * 64 + d) * nv + c.col] = f2bf(v + bias[m]);
   }
 };
 
@@ -372,7 +410,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int m = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
-          if (m < M && n < N) epi.store(m, n, acc[i][j][e]);
+          if (m < M && n < N) epi.store(m, n, acc[i][j][e], epi.col(n));
         }
     }
   } else {
@@ -433,22 +471,20 @@ hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi&
   return hipGetLastError();
 }
 
-#ifndef GEMM_CFG_BIG
-#define GEMM_CFG_BIG Cfg<256, 256, 64, 2, 4, 2>
-#endif
-#ifndef GEMM_CFG_SMALL
-#define GEMM_CFG_SMALL Cfg<64, 128, 64, 2, 2, 2>
-#endif
-#ifndef GEMM_BIG_LIMIT
-#define GEMM_BIG_LIMIT (8L * 1024 * 1024 * 4)
-#endif
+// Tile shapes measured on MI355X over the encoder's GEMMs (M = 4101..16404,
+// N = 384..4096, K = 384..4096): 128 x 128 is best or equal on most; 64 x 128
+// wins on short-K products with few tiles (more resident workgroups per CU);
+// 256 x 256 wins only on very large products.
+using CfgMid = Cfg<128, 128, 64, 2, 2, 2>;
+using CfgSmall = Cfg<64, 128, 64, 2, 2, 2>;
+using CfgBig = Cfg<256, 256, 64, 2, 4, 2>;
 
 template <bool kStaged, class Epi>
 hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
-  // Small tiles keep several workgroups resident per CU, which hides the
-  // per-tile load latency; only very large products use the big tile.
-  if ((long)M * N >= GEMM_BIG_LIMIT) return run<GEMM_CFG_BIG, kStaged>(A, W, M, N, K, epi, s);
-  return run<GEMM_CFG_SMALL, kStaged>(A, W, M, N, K, epi, s);
+  const long mid_tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
+  if ((long)M * N >= 32L * 1024 * 1024) return run<CfgBig, kStaged>(A, W, M, N, K, epi, s);
+  if (K <= 512 && mid_tiles < 512) return run<CfgSmall, kStaged>(A, W, M, N, K, epi, s);
+  return run<CfgMid, kStaged>(A, W, M, N, K, epi, s);
 }
 
 }  // namespace
