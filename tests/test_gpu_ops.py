@@ -84,6 +84,28 @@ def test_linear(M, N, K, epi):
     assert not bad.any(), (np.argwhere(bad)[:5], np.abs(got - ref).max())
 
 
+def test_gelu_epilogue_wide_range():
+    """GELU over pre-activations spanning [-8, 8] (every step of 1/16, exact in
+    bf16), so the clamped ends of the epilogue's Phi lookup are exercised:
+    a = x in column 0, w = 1 in column 0, so acc = x exactly."""
+    say("gelu epilogue wide range")
+    x = np.arange(-128, 129, dtype=np.float64) / 16.0
+    M, N, K = x.size, 64, 64
+    a = np.zeros((M, K))
+    a[:, 0] = x
+    w = np.zeros((N, K))
+    w[:, 0] = 1.0
+    a_d, a_r = bf16_dev(a)
+    w_d, _ = bf16_dev(w)
+    assert np.array_equal(a_r[:, 0], x)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    vit.vit_op_linear(a_d, w_d, f32_dev(np.zeros(N, np.float32)), M, N, K, vit.EPI_GELU_BF16,
+                      f32_dev(np.ones(N, np.float32)), out)
+    ref = O.gelu(np.repeat(x[:, None], N, 1))
+    got = host(out)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6), np.abs(got - ref).max()
+
+
 # ------------------------------------------------------------------ QKV head split
 
 @pytest.mark.parametrize("batch,tokens,heads", [(1, 5, 1), (2, 201, 6), (1, 446, 6), (3, 70, 2)])

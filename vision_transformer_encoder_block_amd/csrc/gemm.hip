@@ -10,7 +10,11 @@
 // 16-byte chunks of a row are XOR-swizzled so that the 16 rows read by 16
 // consecutive lanes of one ds_read_b128 hit distinct banks.  The epilogue
 // stages each wave's accumulators through LDS so that every lane writes 4
-// consecutive columns of one row (coalesced 8- or 16-byte stores).  Workgroup
+// consecutive columns of one row (coalesced 8- or 16-byte stores); all of its
+// reads (LDS, bias, residual) are issued before its first store, because
+// loads and stores share one completion counter and a load waited for after
+// a store would wait for the store too.  V columns of the fused Q/K/V
+// projection leave through a transposing variant of the staging.  Workgroup
 // ids are remapped so that each XCD (8 per chip, own L2) owns a contiguous
 // range of tiles, grouped along M.  Tile shapes were chosen by measurement on
 // MI355X: small tiles with several workgroups resident per CU beat large tiles
@@ -18,6 +22,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <cmath>
+#include <mutex>
 #include <type_traits>
 
 namespace vit {
@@ -66,27 +72,76 @@ __device__ __forceinline__ uint2 pack4_bf16(const float (&v)[4]) {
   return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
+// Columns n .. n + nvalid - 1 (nvalid <= 4; nothing read for nvalid <= 0).
+// `vec` is uniform over the launch: N % 4 == 0 and the pointers are aligned,
+// so every group a lane touches is whole and one vector access serves it
+// (a uniform branch: no divergent control flow around the loads).
+__device__ __forceinline__ float4 load4(const float* p, int nvalid, bool vec) {
+  if (vec) return *reinterpret_cast<const float4*>(p);
+  float t[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 4; ++i)
+    if (i < nvalid) t[i] = p[i];
+  return make_float4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void store4_bf16(bf16_t* p, const float (&v)[4], int nvalid, bool vec) {
+  if (vec) {
+    *reinterpret_cast<uint2*>(p) = pack4_bf16(v);
+  } else {
+    for (int i = 0; i < nvalid; ++i) p[i] = f2bf(v[i]);
+  }
+}
+__device__ __forceinline__ void store4_f32(float* p, const float (&v)[4], int nvalid, bool vec) {
+  if (vec) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    for (int i = 0; i < nvalid; ++i) p[i] = v[i];
+  }
+}
+
+// ---------------------------------------------------------------- GELU
+// GELU(x) = x * Phi(x) with Phi, the standard normal CDF, read from a table at
+// the points x_i = -6 + i / 64 (i = 0 .. 768) and linearly interpolated: the
+// interpolation error is at most h^2/8 * max|Phi''| = 7.4e-6 (h = 1/64,
+// max|Phi''| = phi(1)), and outside [-6, 6] Phi is 0 or 1 to within 1e-9.
+// Entry i holds (Phi(x_i), Phi(x_{i+1}) - Phi(x_i)); the table is built on
+// the host from erfc in double precision and copied once per device.
+constexpr int kPhiPoints = 769;
+__device__ float2 g_phi_table[kPhiPoints];
+
+__device__ __forceinline__ float gelu_table(float x, const float2* tab) {
+  // t in [0, 768]; NaN converts to index 0 and propagates through f
+  const float t = __builtin_amdgcn_fmed3f(fmaf(x, 64.f, 384.f), 0.f, 768.f);
+  const float2 e = tab[(int)t];
+  return x * fmaf(__builtin_amdgcn_fractf(t), e.y, e.x);
+}
+
 // ---------------------------------------------------------------- epilogues
-// store4(m, n, v, nvalid): columns n .. n + nvalid - 1 (nvalid <= 4) of row m.
-// `vec` is true when row starts and n are aligned for a 4-wide vector store.
+// Staged epilogues: every lane owns 4 consecutive columns n .. n + 3 (nvalid
+// of them inside the matrix) of several rows m of the tile.
+//   col4(n, nvalid)   column constants (bias, LayerScale), read once per tile
+//   pre(m, n, nvalid) row data read before any store of the pass group
+//   finish4(v, col, row) the output values (all passes before any store)
+//   write4(m, n, v, nvalid[, col]) the stores
+// Output and parameter pointers may alias as far as the compiler knows, so
+// reads placed after a store would wait for it; this split keeps all reads
+// ahead of all stores.  `vec` (host-checked alignment) selects vector accesses.
+struct NoRow {};
 
 struct EpiBiasBf16 {
   const float* bias;
   bf16_t* out;
   int ldc;
   bool vec;
-  __device__ void store4(int m, int n, float (&v)[4], int nvalid) const {
-    bf16_t* p = out + (size_t)m * ldc + n;
-    for (int i = 0; i < 4; ++i) v[i] += (bias && i < nvalid) ? bias[n + i] : 0.f;
-    if (vec && nvalid == 4) {
-      *reinterpret_cast<uint2*>(p) = pack4_bf16(v);
-    } else {
-      for (int i = 0; i < nvalid; ++i) p[i] = f2bf(v[i]);
-    }
+  using Col = float4;
+  using Row = NoRow;
+  __device__ Col col4(int n, int nvalid) const { return bias ? load4(bias + n, nvalid, vec) : make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ Row pre(int, int, int) const { return {}; }
+  __device__ void finish4(float (&v)[4], const Col& b, const Row&) const {
+    v[0] += b.x, v[1] += b.y, v[2] += b.z, v[3] += b.w;
   }
-  struct Col { float b; };
-  __device__ Col col(int n) const { return {bias ? bias[n] : 0.f}; }
-  __device__ void store(int m, int n, float v, const Col& c) const { out[(size_t)m * ldc + n] = f2bf(v + c.b); }
+  __device__ void write4(int m, int n, const float (&v)[4], int nvalid) const {
+    store4_bf16(out + (size_t)m * ldc + n, v, nvalid, vec);
+  }
 };
 
 struct EpiGeluBf16 {
@@ -94,22 +149,30 @@ struct EpiGeluBf16 {
   bf16_t* out;
   int ldc;
   bool vec;
-  __device__ void store4(int m, int n, float (&v)[4], int nvalid) const {
-    bf16_t* p = out + (size_t)m * ldc + n;
-    if (vec && nvalid == 4) {
-      const float4 b = *reinterpret_cast<const float4*>(bias + n);
-      v[0] = gelu_erf(v[0] + b.x);
-      v[1] = gelu_erf(v[1] + b.y);
-      v[2] = gelu_erf(v[2] + b.z);
-      v[3] = gelu_erf(v[3] + b.w);
-      *reinterpret_cast<uint2*>(p) = pack4_bf16(v);
-    } else {
-      for (int i = 0; i < nvalid; ++i) p[i] = f2bf(gelu_erf(v[i] + bias[n + i]));
-    }
+  const float2* phi;  // device copy of the Phi table
+  using Col = float4;
+  using Row = NoRow;
+  __device__ static float2* lds_phi() {
+    __shared__ float2 t[kPhiPoints];
+    return t;
   }
-  struct Col { float b; };
-  __device__ Col col(int n) const { return {bias[n]}; }
-  __device__ void store(int m, int n, float v, const Col& c) const { out[(size_t)m * ldc + n] = f2bf(gelu_erf(v + c.b)); }
+  // copies the table to LDS at kernel start (published by the main loop's barriers)
+  __device__ void prologue(int tid, int nthreads) const {
+    float2* t = lds_phi();
+    for (int i = tid; i < kPhiPoints; i += nthreads) t[i] = phi[i];
+  }
+  __device__ Col col4(int n, int nvalid) const { return load4(bias + n, nvalid, vec); }
+  __device__ Row pre(int, int, int) const { return {}; }
+  __device__ void finish4(float (&v)[4], const Col& b, const Row&) const {
+    const float2* t = lds_phi();
+    v[0] = gelu_table(v[0] + b.x, t);
+    v[1] = gelu_table(v[1] + b.y, t);
+    v[2] = gelu_table(v[2] + b.z, t);
+    v[3] = gelu_table(v[3] + b.w, t);
+  }
+  __device__ void write4(int m, int n, const float (&v)[4], int nvalid) const {
+    store4_bf16(out + (size_t)m * ldc + n, v, nvalid, vec);
+  }
 };
 
 struct EpiResidual {
@@ -118,26 +181,18 @@ struct EpiResidual {
   float* out;
   int ldc;
   bool vec;
-  __device__ void store4(int m, int n, float (&v)[4], int nvalid) const {
-    float* p = out + (size_t)m * ldc + n;
-    if (vec && nvalid == 4) {
-      const float4 b = *reinterpret_cast<const float4*>(bias + n);
-      const float4 s = *reinterpret_cast<const float4*>(ls + n);
-      float4 r = *reinterpret_cast<float4*>(p);
-      r.x += s.x * (v[0] + b.x);
-      r.y += s.y * (v[1] + b.y);
-      r.z += s.z * (v[2] + b.z);
-      r.w += s.w * (v[3] + b.w);
-      *reinterpret_cast<float4*>(p) = r;
-    } else {
-      for (int i = 0; i < nvalid; ++i) p[i] = p[i] + ls[n + i] * (v[i] + bias[n + i]);
-    }
+  struct Col { float4 b, s; };
+  using Row = float4;  // current residual
+  __device__ Col col4(int n, int nvalid) const { return {load4(bias + n, nvalid, vec), load4(ls + n, nvalid, vec)}; }
+  __device__ Row pre(int m, int n, int nvalid) const { return load4(out + (size_t)m * ldc + n, nvalid, vec); }
+  __device__ void finish4(float (&v)[4], const Col& c, const Row& r) const {
+    v[0] = r.x + c.s.x * (v[0] + c.b.x);
+    v[1] = r.y + c.s.y * (v[1] + c.b.y);
+    v[2] = r.z + c.s.z * (v[2] + c.b.z);
+    v[3] = r.w + c.s.w * (v[3] + c.b.w);
   }
-  struct Col { float b, s; };
-  __device__ Col col(int n) const { return {bias[n], ls[n]}; }
-  __device__ void store(int m, int n, float v, const Col& c) const {
-    float* p = out + (size_t)m * ldc + n;
-    *p = *p + c.s * (v + c.b);
+  __device__ void write4(int m, int n, const float (&v)[4], int nvalid) const {
+    store4_f32(out + (size_t)m * ldc + n, v, nvalid, vec);
   }
 };
 
@@ -146,21 +201,20 @@ struct EpiBiasF32 {
   float* out;
   int ldc;
   bool vec;
-  __device__ void store4(int m, int n, float (&v)[4], int nvalid) const {
-    float* p = out + (size_t)m * ldc + n;
-    for (int i = 0; i < 4; ++i) v[i] += (bias && i < nvalid) ? bias[n + i] : 0.f;
-    if (vec && nvalid == 4) {
-      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-      for (int i = 0; i < nvalid; ++i) p[i] = v[i];
-    }
+  using Col = float4;
+  using Row = NoRow;
+  __device__ Col col4(int n, int nvalid) const { return bias ? load4(bias + n, nvalid, vec) : make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ Row pre(int, int, int) const { return {}; }
+  __device__ void finish4(float (&v)[4], const Col& b, const Row&) const {
+    v[0] += b.x, v[1] += b.y, v[2] += b.z, v[3] += b.w;
   }
-  struct Col { float b; };
-  __device__ Col col(int n) const { return {bias ? bias[n] : 0.f}; }
-  __device__ void store(int m, int n, float v, const Col& c) const { out[(size_t)m * ldc + n] = v + c.b; }
+  __device__ void write4(int m, int n, const float (&v)[4], int nvalid) const {
+    store4_f32(out + (size_t)m * ldc + n, v, nvalid, vec);
+  }
 };
 
 // Q and K columns (n < 2D) of the fused projection: head-major rows of 64.
+// D % 64 == 0, so the 4 columns of a lane never straddle a head.
 struct EpiQK {
   const float* bias;
   bf16_t* q;
@@ -168,75 +222,97 @@ struct EpiQK {
   int D, N, heads;
   FastDiv divN;
   float qscale;
-  bool vec;  // always true: D % 64 == 0 and n % 4 == 0
-  __device__ void store4(int m, int n, float (&v)[4], int) const {
+  bool vec;
+  struct Col { float4 b; float s; bf16_t* dst; int d; };
+  using Row = NoRow;
+  __device__ Col col4(int n, int nvalid) const {
     const int which = n >= D;
     const int c = n - which * D;
-    const int head = c >> 6, d = c & 63;
+    return {load4(bias + n, nvalid, vec), which ? 1.f : qscale, (which ? k : q) + (size_t)(c >> 6) * N * 64, c & 63};
+  }
+  __device__ Row pre(int, int, int) const { return {}; }
+  __device__ void finish4(float (&v)[4], const Col& c, const Row&) const {
+    v[0] = (v[0] + c.b.x) * c.s;
+    v[1] = (v[1] + c.b.y) * c.s;
+    v[2] = (v[2] + c.b.z) * c.s;
+    v[3] = (v[3] + c.b.w) * c.s;
+  }
+  __device__ void write4(int m, int, const float (&v)[4], int nvalid, const Col& c) const {
     const int b = (int)fdiv((uint32_t)m, divN);
     const int tok = m - b * N;
-    const size_t row = ((size_t)b * heads + head) * N + tok;
-    const float4 bb = *reinterpret_cast<const float4*>(bias + n);
-    const float s = which ? 1.f : qscale;
-    float o[4] = {(v[0] + bb.x) * s, (v[1] + bb.y) * s, (v[2] + bb.z) * s, (v[3] + bb.w) * s};
-    *reinterpret_cast<uint2*>((which ? k : q) + row * 64 + d) = pack4_bf16(o);
-  }
-  struct Col { float b, s; int which, head, d; };
-  __device__ Col col(int n) const {
-    const int which = n >= D;
-    const int c = n - which * D;
-    return {bias[n], which ? 1.f : qscale, which, c >> 6, c & 63};
-  }
-  __device__ void store(int m, int n, float v, const Col& c) const {
-    const int b = (int)fdiv((uint32_t)m, divN);
-    const int tok = m - b * N;
-    const size_t row = ((size_t)b * heads + c.head) * N + tok;
-    (c.which ? k : q)[row * 64 + c.d] = f2bf((v + c.b) * c.s);
+    store4_bf16(c.dst + ((size_t)b * heads * N + tok) * 64 + c.d, v, nvalid, vec);
   }
 };
 
+// All three projections in one GEMM (N = 3D).  Tiles of Q and K columns go
+// through the staged row path of EpiQK; tiles of V columns (n >= 2D: tile
+// uniform because 2D is a multiple of the tile width) are transposed through
+// LDS: each lane takes one token and half-waves take channel pairs, so 32
+// lanes write 32 consecutive vt columns of one channel row.
+struct EpiQKV : EpiQK {
+  bf16_t* vt;
+  int nv;
+  __device__ bool tile_transposed(int n0) const { return n0 >= 2 * D; }
+  __device__ float tbias(int n) const { return bias[min(n, 3 * D - 1)]; }
+  // value v of V channel ch (0 <= ch < D) of token row m
+  struct TRow { bf16_t* base; bool ok; };
+  __device__ TRow trow(int m, int M) const {
+    const int b = (int)fdiv((uint32_t)m, divN);
+    const int tok = m - b * N;
+    return {vt + (size_t)b * heads * 64 * nv + vt_pos(tok), m < M};
+  }
+  __device__ void tstore(const TRow& r, int ch, float v) const {
+    if (r.ok && ch < D) r.base[(size_t)ch * nv] = f2bf(v);
+  }
+};
+
+// write4 with or without the column constants
+template <class E>
+__device__ __forceinline__ auto write4_any(const E& e, int m, int n, const float (&v)[4], int nvalid,
+                                           const typename E::Col& c, int) -> decltype(e.write4(m, n, v, nvalid, c)) {
+  return e.write4(m, n, v, nvalid, c);
+}
+template <class E>
+__device__ __forceinline__ void write4_any(const E& e, int m, int n, const float (&v)[4], int nvalid,
+                                           const typename E::Col&, long) {
+  e.write4(m, n, v, nvalid);
+}
+
+template <class E, class = void>
+struct HasPrologue : std::false_type {};
+template <class E>
+struct HasPrologue<E, std::void_t<decltype(&E::prologue)>> : std::true_type {};
+template <class E, class = void>
+struct HasTransposed : std::false_type {};
+template <class E>
+struct HasTransposed<E, std::void_t<decltype(&E::tile_transposed)>> : std::true_type {};
+
+// Patch rows of the embedding GEMM: row m = b * patches + i goes to residual
+// row b * tokens + 1 + regs + i with its position embedding pos[1 + i] added.
 struct EpiPatch {
   const float* bias;
   const float* pos;
   float* out;
   int D, tokens, patches, regs;
   FastDiv divP;
-  bool vec;  // always true: D % 64 == 0
-  __device__ void store4(int m, int n, float (&v)[4], int) const {
+  bool vec;
+  using Col = float4;
+  using Row = float4;  // position embedding of the patch
+  __device__ Col col4(int n, int nvalid) const { return load4(bias + n, nvalid, vec); }
+  __device__ Row pre(int m, int n, int nvalid) const {
     const int b = (int)fdiv((uint32_t)m, divP);
-    const int i = m - b * patches;
-    const size_t row = (size_t)b * tokens + 1 + regs + i;
-    const float4 bb = *reinterpret_cast<const float4*>(bias + n);
-    const float4 pp = *reinterpret_cast<const float4*>(pos + (size_t)(1 + i) * D + n);
-    *reinterpret_cast<float4*>(out + row * D + n) =
-        make_float4(v[0] + bb.x + pp.x, v[1] + bb.y + pp.y, v[2] + bb.z + pp.z, v[3] + bb.w + pp.w);
+    return load4(pos + (size_t)(1 + m - b * patches) * D + n, nvalid, vec);
   }
-  struct Col { float b; };
-  __device__ Col col(int n) const { return {bias[n]}; }
-  __device__ void store(int m, int n, float v, const Col& c) const {
+  __device__ void finish4(float (&v)[4], const Col& bb, const Row& pp) const {
+    v[0] += bb.x + pp.x;
+    v[1] += bb.y + pp.y;
+    v[2] += bb.z + pp.z;
+    v[3] += bb.w + pp.w;
+  }
+  __device__ void write4(int m, int n, const float (&v)[4], int nvalid) const {
     const int b = (int)fdiv((uint32_t)m, divP);
-    const int i = m - b * patches;
-    const size_t row = (size_t)b * tokens + 1 + regs + i;
-    out[row * D + n] = v + c.b + pos[(size_t)(1 + i) * D + n];
-  }
-};
-
-// V columns, computed transposed (A = wv rows, W = token rows): element (m, n)
-// is channel m of token row n, stored in vt.  Written straight from the
-// accumulators: the 32 lanes of a row hold 32 consecutive tokens.
-struct EpiVt {
-  const float* bias;  // bv
-  bf16_t* vt;
-  int N, heads, nv;
-  FastDiv divN;
-  struct Col { int b, col; };  // image and vt column of token row n
-  __device__ Col col(int n) const {
-    const int b = (int)fdiv((uint32_t)n, divN);
-    return {b, vt_pos(n - b * N)};
-  }
-  __device__ void store(int m, int n, float v, const Col& c) const {
-    const int head = m >> 6, d = m & 63;
-    vt[(((size_t)c.b * heads + head) * 64 + d) * nv + c.col] = f2bf(v + bias[m]);
+    const size_t row = (size_t)b * tokens + 1 + regs + (m - b * patches);
+    store4_f32(out + row * D + n, v, nvalid, vec);
   }
 };
 
@@ -276,7 +352,7 @@ __device__ __forceinline__ int swz_k(int r, int c) {
   else return c ^ (r & 15);
 }
 
-template <int BM, int BN, int BKT, int WGM, int WGN, int S, bool kStaged, class Epi>
+template <int BM, int BN, int BKT, int WGM, int WGN, int S, class Epi>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t* __restrict__ A,
                                                                   const bf16_t* __restrict__ W, int M, int N, int K,
                                                                   int tiles_m, int tiles_n, Epi epi) {
@@ -300,6 +376,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+
+  if constexpr (HasPrologue<Epi>::value) epi.prologue(tid, 64 * NW);
 
   const int32x4 ra_src = make_rsrc_words(A, (uint32_t)((size_t)M * K * 2));
   const int32x4 rb_src = make_rsrc_words(W, (uint32_t)((size_t)N * K * 2));
@@ -401,23 +479,49 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   __syncthreads();
 
   // accumulator element e of block (i, j): row 8*(e/4) + 4*lhalf + e%4, column lrow
-  if constexpr (!kStaged) {
+  if constexpr (HasTransposed<Epi>::value) {
+    if (epi.tile_transposed(n0)) {
+      // Stage 32 rows (tokens) x WTN columns (channels) with the bias added,
+      // row stride WTN + 2 floats: the transposed reads below (lane -> row,
+      // half-wave -> column parity) then hit 64 distinct banks.
+      constexpr int LDT = WTN + 2;
+      constexpr int WAVE_BYTES = 32 * LDT * 4;
+      constexpr int WPB = STAGE_BYTES / WAVE_BYTES;
+      static_assert(WPB >= 1 && WPB * S >= NW, "staging must fit in the stage LDS");
+      float* stage = nullptr;
+      static_for<0, S>([&](auto s) {
+        if (wave / WPB == decltype(s)::value)
+          stage = reinterpret_cast<float*>(stage_lds<STAGE_BYTES, decltype(s)::value>()) + (wave % WPB) * 32 * LDT;
+      });
+      const int nw0 = n0 + wn * WTN;
+      float bcol[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * WTN + j * 32 + lrow;
+      for (int j = 0; j < TN; ++j) bcol[j] = epi.tbias(nw0 + j * 32 + lrow);
+      const int ch0 = nw0 - 2 * epi.D;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
-          if (m < M && n < N) epi.store(m, n, acc[i][j][e], epi.col(n));
-        }
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            stage[((e >> 2) * 8 + lhalf * 4 + (e & 3)) * LDT + j * 32 + lrow] = acc[i][j][e] + bcol[j];
+        __syncthreads();
+        const auto tr = epi.trow(m0 + wm * WTM + i * 32 + lrow, M);
+        float tv[WTN / 2];
+#pragma unroll
+        for (int c2 = 0; c2 < WTN / 2; ++c2) tv[c2] = stage[lrow * LDT + 2 * c2 + lhalf];
+#pragma unroll
+        for (int c2 = 0; c2 < WTN / 2; ++c2) epi.tstore(tr, ch0 + 2 * c2 + lhalf, tv[c2]);
+        __syncthreads();
+      }
+      return;
     }
-  } else {
+  }
+  {
     // Each wave stages one 32-row block of its tile at a time (row stride WTN + 8
     // floats: the two lane halves land on disjoint banks), then every lane
-    // handles 4 consecutive columns of one row.  The staging areas live in the
-    // (now idle) LDS of the pipeline stages.
+    // handles 4 consecutive columns of PASSES rows.  The staging areas live in
+    // the (now idle) LDS of the pipeline stages.
     constexpr int LD = WTN + 8;
     constexpr int LPR = WTN / 4;                   // lanes per staged row
     constexpr int RPP = 64 / LPR;                  // rows per pass
@@ -434,6 +538,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
     const int cl = (lane % LPR) * 4;
     const int n = n0 + wn * WTN + cl;
     const int nvalid = min(4, N - n);
+    const bool lane_ok = lane < RPP * LPR && nvalid > 0;
+    // Reads are issued for every lane at in-range addresses (idle lanes read
+    // the tile's first columns or the last row) so that no branch surrounds them.
+    const int n_rd = lane_ok ? n : n0;
+    const int nvalid_rd = lane_ok ? nvalid : min(4, N - n0);
+    const typename Epi::Col cc = epi.col4(n_rd, nvalid_rd);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -441,15 +551,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
 #pragma unroll
         for (int e = 0; e < 16; ++e) stage[((e >> 2) * 8 + lhalf * 4 + (e & 3)) * LD + j * 32 + lrow] = acc[i][j][e];
       __syncthreads();
+      float v[PASSES][4];
+      typename Epi::Row rw[PASSES];
+      const int mb = m0 + wm * WTM + i * 32 + lane / LPR;
+#pragma unroll
+      for (int pass = 0; pass < PASSES; ++pass) {
+        const int r = min(pass * RPP + lane / LPR, 31);
+        const float4 t = *reinterpret_cast<const float4*>(stage + r * LD + cl);
+        v[pass][0] = t.x;
+        v[pass][1] = t.y;
+        v[pass][2] = t.z;
+        v[pass][3] = t.w;
+        rw[pass] = epi.pre(min(mb + pass * RPP, M - 1), n_rd, nvalid_rd);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): every read of this block is in
+#pragma unroll
+      for (int pass = 0; pass < PASSES; ++pass) epi.finish4(v[pass], cc, rw[pass]);
 #pragma unroll
       for (int pass = 0; pass < PASSES; ++pass) {
         const int r = pass * RPP + lane / LPR;
-        const int m = m0 + wm * WTM + i * 32 + r;
-        if (lane < RPP * LPR && r < 32 && m < M && nvalid > 0) {
-          const float4 t = *reinterpret_cast<const float4*>(stage + r * LD + cl);
-          float v[4] = {t.x, t.y, t.z, t.w};
-          epi.store4(m, n, v, nvalid);
-        }
+        if (lane_ok && r < 32 && mb + pass * RPP < M) write4_any(epi, mb + pass * RPP, n, v[pass], nvalid, cc, 0);
       }
       __syncthreads();
     }
@@ -462,11 +583,11 @@ struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, S = S_;
 };
 
-template <class C, bool kStaged, class Epi>
+template <class C, class Epi>
 hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
   if (K % C::BK != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<C::BM, C::BN, C::BK, C::WGM, C::WGN, C::S, kStaged, Epi>), dim3(tiles_m * tiles_n),
+  hipLaunchKernelGGL((gemm_bf16_kernel<C::BM, C::BN, C::BK, C::WGM, C::WGN, C::S, Epi>), dim3(tiles_m * tiles_n),
                      dim3(64 * C::WGM * C::WGN), 0, s, A, W, M, N, K, tiles_m, tiles_n, epi);
   return hipGetLastError();
 }
@@ -479,45 +600,93 @@ using CfgMid = Cfg<128, 128, 64, 2, 2, 2>;
 using CfgSmall = Cfg<64, 128, 64, 2, 2, 2>;
 using CfgBig = Cfg<256, 256, 64, 2, 4, 2>;
 
-template <bool kStaged, class Epi>
+template <class Epi>
 hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   const long mid_tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if ((long)M * N >= 32L * 1024 * 1024) return run<CfgBig, kStaged>(A, W, M, N, K, epi, s);
-  if (K <= 512 && mid_tiles < 512) return run<CfgSmall, kStaged>(A, W, M, N, K, epi, s);
-  return run<CfgMid, kStaged>(A, W, M, N, K, epi, s);
+  if ((long)M * N >= 32L * 1024 * 1024) return run<CfgBig>(A, W, M, N, K, epi, s);
+  if (K <= 512 && mid_tiles < 512) return run<CfgSmall>(A, W, M, N, K, epi, s);
+  return run<CfgMid>(A, W, M, N, K, epi, s);
+}
+
+// Phi table of the GELU epilogue: built once per device (synchronous copy to
+// the device symbol); returns the device address or nullptr on failure.
+const float2* phi_table_device() {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static const float2* addr[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    float2 host[kPhiPoints];
+    double prev = 0.5 * std::erfc(6.0 / std::sqrt(2.0));  // Phi(-6)
+    for (int i = 0; i < kPhiPoints; ++i) {
+      const double x1 = -6.0 + (i + 1) / 64.0;
+      const double next = i + 1 < kPhiPoints ? 0.5 * std::erfc(-x1 / std::sqrt(2.0)) : prev;
+      host[i] = make_float2((float)prev, (float)(next - prev));
+      prev = next;
+    }
+    void* p = nullptr;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_phi_table), host, sizeof(host)) != hipSuccess) return nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_phi_table)) != hipSuccess) return nullptr;
+    addr[dev] = static_cast<const float2*>(p);
+  }
+  return addr[dev];
+}
+
+// Fused Q/K/V: the V tiles must not straddle the K|V boundary at 2D.
+hipError_t dispatch_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, const EpiQKV& epi, hipStream_t s) {
+  const long mid_tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
+  if ((long)M * N >= 32L * 1024 * 1024 && (2 * epi.D) % CfgBig::BN == 0) return run<CfgBig>(A, W, M, N, K, epi, s);
+  if (K <= 512 && mid_tiles < 512) return run<CfgSmall>(A, W, M, N, K, epi, s);
+  return run<CfgMid>(A, W, M, N, K, epi, s);
 }
 
 }  // namespace
+
+hipError_t prepare_gemm() { return phi_table_device() ? hipSuccess : hipErrorInvalidValue; }
 
 hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, int M, int N, int K, const EpiParams& ep,
                        hipStream_t s) {
   if (M <= 0 || N <= 0 || K <= 0 || K % BK != 0) return hipErrorInvalidValue;
   if ((size_t)(M + 128) * K * 2 >= (1ull << 32) || (size_t)(N + 128) * K * 2 >= (1ull << 32))
     return hipErrorInvalidValue;  // 32-bit buffer offsets
-  const bool vec = ep.ldc % 4 == 0;
+  auto al = [](const void* p, size_t n) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % n == 0; };
+  const bool par16 = N % 4 == 0 && al(ep.bias, 16) && al(ep.ls, 16);
   switch (ep.kind) {
-    case EPI_BIAS_BF16:
-      return dispatch<true>(A, W, M, N, K, EpiBiasBf16{ep.bias, (bf16_t*)ep.out, ep.ldc, vec}, s);
-    case EPI_GELU_BF16:
-      return dispatch<true>(A, W, M, N, K, EpiGeluBf16{ep.bias, (bf16_t*)ep.out, ep.ldc, vec}, s);
-    case EPI_RESIDUAL:
-      return dispatch<true>(A, W, M, N, K, EpiResidual{ep.bias, ep.ls, (float*)ep.out, ep.ldc, vec}, s);
-    case EPI_BIAS_F32:
-      return dispatch<true>(A, W, M, N, K, EpiBiasF32{ep.bias, (float*)ep.out, ep.ldc, vec}, s);
+    case EPI_BIAS_BF16: {
+      const bool vec = ep.ldc % 4 == 0 && par16 && al(ep.out, 8);
+      return dispatch(A, W, M, N, K, EpiBiasBf16{ep.bias, (bf16_t*)ep.out, ep.ldc, vec}, s);
+    }
+    case EPI_GELU_BF16: {
+      const bool vec = ep.ldc % 4 == 0 && par16 && al(ep.out, 8);
+      const float2* phi = phi_table_device();
+      if (!phi) return hipErrorInvalidValue;
+      return dispatch(A, W, M, N, K, EpiGeluBf16{ep.bias, (bf16_t*)ep.out, ep.ldc, vec, phi}, s);
+    }
+    case EPI_RESIDUAL: {
+      const bool vec = ep.ldc % 4 == 0 && par16 && al(ep.out, 16);
+      return dispatch(A, W, M, N, K, EpiResidual{ep.bias, ep.ls, (float*)ep.out, ep.ldc, vec}, s);
+    }
+    case EPI_BIAS_F32: {
+      const bool vec = ep.ldc % 4 == 0 && par16 && al(ep.out, 16);
+      return dispatch(A, W, M, N, K, EpiBiasF32{ep.bias, (float*)ep.out, ep.ldc, vec}, s);
+    }
     case EPI_QKV: {
-      // N = 3D: Q and K columns as one GEMM, V columns as a transposed GEMM.
       const int D = N / 3;
       const FastDiv dn = make_fastdiv(ep.tokens);
-      EpiQK eqk{ep.bias, ep.q, ep.k, D, ep.tokens, ep.heads, dn, kLog2e * 0.125f, true};
-      hipError_t e = dispatch<true>(A, W, M, 2 * D, K, eqk, s);
-      if (e != hipSuccess) return e;
-      EpiVt ev{ep.bias + 2 * D, ep.vt, ep.tokens, ep.heads, ep.nv, dn};
-      return dispatch<false>(W + (size_t)2 * D * K, A, D, M, K, ev, s);
+      const bool vec = par16 && al(ep.q, 8) && al(ep.k, 8);
+      EpiQKV e;
+      static_cast<EpiQK&>(e) = EpiQK{ep.bias, ep.q, ep.k, D, ep.tokens, ep.heads, dn, kLog2e * 0.125f, vec};
+      e.vt = ep.vt;
+      e.nv = ep.nv;
+      return dispatch_qkv(A, W, M, N, K, e, s);
     }
     case EPI_PATCH: {
+      const bool vec = par16 && al(ep.pos, 16) && al(ep.out, 16);
       EpiPatch e{ep.bias, ep.pos, (float*)ep.out, ep.ldc, ep.tokens, ep.patches, ep.regs, make_fastdiv(ep.patches),
-                 true};
-      return dispatch<true>(A, W, M, N, K, e, s);
+                 vec};
+      return dispatch(A, W, M, N, K, e, s);
     }
   }
   return hipErrorInvalidValue;

@@ -36,6 +36,11 @@ struct EpiParams {
   int regs = 0;
 };
 
+// One-time per-device set-up of the GEMM epilogues (the GELU Phi table; a
+// synchronous copy).  launch_gemm does it on first use; encoders call it at
+// creation so that no later launch copies.
+hipError_t prepare_gemm();
+
 hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, int M, int N, int K, const EpiParams& ep,
                        hipStream_t s);
 

@@ -410,6 +410,7 @@ int vit_create(const vit_config* cfg, const float* host_params, size_t host_floa
   if (((uintptr_t)d_weights | (uintptr_t)d_workspace) % kAlign)
     return fail(VIT_ERR_ARG, "device buffers must be 256-byte aligned");
   hipStream_t st = (hipStream_t)stream;
+  if (vit::prepare_gemm() != hipSuccess) return fail(VIT_ERR_HIP, "GEMM tables could not be set up");
 
   const size_t D = pl.D, Hm = pl.Hm, R = pl.R, p = pl.p;
   const WeightLayout& wl = pl.wl;
