@@ -122,7 +122,7 @@ int vit_create(const vit_config* cfg, const float* host_params, size_t host_floa
 
 /* Encoder forward for `batch` (1..max_batch) images.
  *   d_images  device fp32 [batch,3,img_h,img_w]
- *   d_tokens  device fp32 [batch,N,D]: final LayerNorm of every token
+ *   d_tokens  device fp32 [batch,N,D], 16-byte aligned: final LayerNorm of every token
  *             (row 0 CLS, rows 1..R registers, then patches in raster order)
  *   d_taps    NULL, or device fp32 [batch, taps, D, H/p, W/p]: after each
  *             block selected by tap_mask, the final LayerNorm (backbone `norm`

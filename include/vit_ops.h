@@ -20,14 +20,16 @@ extern "C" {
 /* LayerNorm over the last axis (LibreYOLO DINOv2 diagram, "Encoder block":
  * LayerNorm eps 1e-6): y = (x - mean) / sqrt(var + eps) * g + b, biased var.
  *   x [rows, dim] fp32; g, b [dim]; y [rows, dim], bf16 if out_fp32 == 0 else fp32.
- *   dim must be a multiple of 64 and <= 4096. */
+ *   dim must be a multiple of 64 and <= 4096; x, g, b, y 16-byte aligned. */
 int vit_op_layernorm(const float* x, int rows, int dim, const float* g, const float* b, float eps,
                      void* y, int out_fp32, void* stream);
 
 /* Epilogues of vit_op_linear. */
 enum vit_epilogue {
   VIT_EPI_BIAS_BF16 = 0,   /* c_bf16[m,n] = bf16(acc + bias[n]) */
-  VIT_EPI_GELU_BF16 = 1,   /* c_bf16[m,n] = bf16(GELU(acc + bias[n])), exact erf GELU */
+  VIT_EPI_GELU_BF16 = 1,   /* c_bf16[m,n] = bf16(GELU(acc + bias[n])), GELU(z) = z Phi(z) with the
+                              normal CDF Phi linearly interpolated between points 1/64 apart
+                              (|error of Phi| <= 7.4e-6; Phi = 0 / 1 beyond -6 / 6) */
   VIT_EPI_RESIDUAL = 2,    /* c_f32[m,n] += ls[n] * (acc + bias[n])  (LayerScale + residual) */
   VIT_EPI_BIAS_F32 = 3     /* c_f32[m,n] = acc + bias[n]  (bias may be NULL: 0) */
 };

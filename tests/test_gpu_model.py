@@ -265,3 +265,37 @@ def test_two_runs_are_bitwise_equal(vits336):
     b = host(enc.forward(xd))
     enc.close()
     np.testing.assert_array_equal(a, b)
+
+
+def test_graph_replay_matches_eager():
+    """The forward (with taps and the descriptor) captured as a HIP graph and
+    replayed on new inputs, with eager work and synchronisations between the
+    replays, reproduces the eager results bit for bit on every replay
+    (DINOv2-S/14 @518, 1370 tokens: the attention tail split is in the graph)."""
+    cfg = synth.preset("vits14_518")
+    say("graph replay, DINOv2-S/14 @518 b2 with taps")
+    P = synth.make_params(cfg)
+    xs = [synth.make_images(cfg, 2, seed=s) for s in (11, 12, 13)]
+    enc = vit.Encoder(cfg, P, max_batch=2)
+    eager = []
+    for x in xs:
+        tok, taps = enc.forward(f32_dev(x), with_taps=True)
+        desc = enc.descriptor(tok)
+        eager.append((host(tok), host(taps), host(desc)))
+    xd = f32_dev(xs[0])
+    tok = torch.empty((2, enc.tokens, cfg["dim"]), dtype=torch.float32, device="cuda")
+    taps = torch.empty_like(enc.forward(xd, with_taps=True)[1])
+    desc = torch.empty((2, cfg["dim"]), dtype=torch.float32, device="cuda")
+    g = vit.EncoderGraph(enc, xd, tok, desc_out=desc, taps_out=taps)
+    for rep, i in enumerate((1, 0, 2, 2, 1)):
+        xd.copy_(torch.from_numpy(xs[i]))
+        side = enc.forward(f32_dev(xs[(i + 1) % 3]))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(tok), eager[i][0], err_msg=f"replay {rep}")
+        np.testing.assert_array_equal(host(taps), eager[i][1], err_msg=f"replay {rep}")
+        np.testing.assert_array_equal(host(desc), eager[i][2], err_msg=f"replay {rep}")
+        del side
+    enc.close()
+

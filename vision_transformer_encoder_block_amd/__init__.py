@@ -23,7 +23,7 @@ __all__ = [
     "vit_config_preset", "vit_plan", "vit_create", "vit_forward", "vit_descriptor", "vit_patch_scores",
     "vit_destroy", "vit_last_error", "vit_op_layernorm", "vit_op_linear", "vit_op_qkv", "vit_op_attention",
     "vit_op_attention_workspace",
-    "Encoder", "EPI_BIAS_BF16", "EPI_GELU_BF16", "EPI_RESIDUAL", "EPI_BIAS_F32",
+    "Encoder", "EncoderGraph", "EPI_BIAS_BF16", "EPI_GELU_BF16", "EPI_RESIDUAL", "EPI_BIAS_F32",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvit.so")
@@ -289,3 +289,33 @@ class Encoder:
             self.close()
         except Exception:
             pass
+
+
+class EncoderGraph:
+    """One ``Encoder.forward`` (and optionally ``descriptor``) over fixed device
+    buffers, recorded once as a HIP graph; ``replay()`` enqueues the whole
+    forward as a single graph launch on the current stream.  New inputs are
+    written into ``images`` in place between replays.  The forward enqueues
+    kernels only (no allocation, copy, memset or host synchronisation), which
+    is what makes it capturable."""
+
+    def __init__(self, enc: Encoder, images, tokens_out, desc_out=None, taps_out=None):
+        import torch
+        self.enc, self.images, self.tokens, self.desc, self.taps = enc, images, tokens_out, desc_out, taps_out
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # one eager run before capture
+            self._record()
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._record()
+
+    def _record(self):
+        self.enc.forward(self.images, with_taps=self.taps is not None, tokens_out=self.tokens, taps_out=self.taps)
+        if self.desc is not None:
+            self.enc.descriptor(self.tokens, desc_out=self.desc)
+
+    def replay(self):
+        self.graph.replay()
+

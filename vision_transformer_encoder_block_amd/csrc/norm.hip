@@ -1,8 +1,8 @@
 // Row normalisations for gfx950: LayerNorm (bf16 or fp32 out), LayerNormed
 // channel-first taps, LayerNorm + L2 patch features, and the L2-normalised CLS
-// descriptor.  One wave64 per row; lane l holds columns l, l + 64, ... so every
-// load and store instruction of a wave touches one contiguous 256-byte run.
-// Mean and variance use two passes over the row held in registers.
+// descriptor.  A LayerNorm row is spread over 16, 32 or 64 lanes with 16-byte
+// accesses (several rows per wave for narrow rows); mean and variance use two
+// passes over the row held in registers.
 #include "common.h"
 #include "kernels.h"
 
@@ -13,69 +13,104 @@ namespace {
 
 constexpr int MAXV = 64;  // columns per lane: dim <= 4096
 
-template <int V>
-__device__ __forceinline__ void ln_row(const float* __restrict__ xr, const float* __restrict__ g,
-                                       const float* __restrict__ b, float eps, int dim, int lane, float (&y)[V]) {
+// Sum over the LPR lanes of a lane group (LPR a power of two <= 64).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// LayerNorm of one row held by a group of LPR lanes as V4 float4 groups each
+// (lane sl of the group holds columns 4 (sl + LPR i) .. + 3).  Every lane of
+// the wave must call it (the group sums shuffle); all LayerNorms of the
+// library go through it, so they agree bit for bit on the same row.
+template <int V4, int LPR>
+__device__ __forceinline__ void ln_vec(const float* __restrict__ xrow, const float* __restrict__ g,
+                                       const float* __restrict__ b, float eps, int dim, int sl, float4 (&v)[V4]) {
+  const float4* xr = reinterpret_cast<const float4*>(xrow);
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    y[i] = xr[lane + 64 * i];
-    s += y[i];
+  for (int i = 0; i < V4; ++i) {
+    v[i] = xr[sl + LPR * i];
+    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   }
-  const float mean = wave_sum(s) / (float)dim;
-  float v = 0.f;
+  const float mean = group_sum<LPR>(s) / (float)dim;
+  float q = 0.f;
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    y[i] -= mean;
-    v += y[i] * y[i];
+  for (int i = 0; i < V4; ++i) {
+    v[i].x -= mean, v[i].y -= mean, v[i].z -= mean, v[i].w -= mean;
+    q += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
   }
-  const float rstd = rsqrtf(wave_sum(v) / (float)dim + eps);
+  const float rstd = rsqrtf(group_sum<LPR>(q) / (float)dim + eps);
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int c = lane + 64 * i;
-    y[i] = y[i] * rstd * g[c] + b[c];
+  for (int i = 0; i < V4; ++i) {
+    const int c4 = sl + LPR * i;
+    const float4 gg = reinterpret_cast<const float4*>(g)[c4];
+    const float4 bb = reinterpret_cast<const float4*>(b)[c4];
+    v[i] = make_float4(v[i].x * rstd * gg.x + bb.x, v[i].y * rstd * gg.y + bb.y, v[i].z * rstd * gg.z + bb.z,
+                       v[i].w * rstd * gg.w + bb.w);
   }
 }
 
-template <int V, bool F32>
+// Lane group shape for dim = 64 V: the widest group that divides the row into float4s.
+template <int V>
+struct LnShape {
+  static constexpr int LPR = V % 4 == 0 ? 64 : (V % 2 == 0 ? 32 : 16);
+  static constexpr int V4 = 16 * V / LPR;
+  static constexpr int RPW = 64 / LPR;  // rows per wave
+};
+
+// Block LayerNorm: 64 / LPR rows per wave, 16-byte loads, 8-byte bf16 stores.
+template <int V4, int LPR, bool F32>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, int rows, int dim,
                                                         const float* __restrict__ g, const float* __restrict__ b,
                                                         float eps, void* __restrict__ y) {
+  constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int sl = lane % LPR;
+  const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  float4 v[V4];
+  // lanes past the last row normalise it again (the group sums need every lane)
+  ln_vec<V4, LPR>(x + (size_t)min(row, rows - 1) * dim, g, b, eps, dim, sl, v);
   if (row >= rows) return;
-  float v[V];
-  ln_row<V>(x + (size_t)row * dim, g, b, eps, dim, lane, v);
-  if (F32) {
-    float* yr = reinterpret_cast<float*>(y) + (size_t)row * dim;
 #pragma unroll
-    for (int i = 0; i < V; ++i) yr[lane + 64 * i] = v[i];
-  } else {
-    bf16_t* yr = reinterpret_cast<bf16_t*>(y) + (size_t)row * dim;
-#pragma unroll
-    for (int i = 0; i < V; ++i) yr[lane + 64 * i] = f2bf(v[i]);
+  for (int i = 0; i < V4; ++i) {
+    const size_t at = (size_t)row * (dim / 4) + sl + LPR * i;
+    if (F32) {
+      reinterpret_cast<float4*>(y)[at] = v[i];
+    } else {
+      reinterpret_cast<uint2*>(y)[at] = make_uint2(pack_bf16x2(v[i].x, v[i].y), pack_bf16x2(v[i].z, v[i].w));
+    }
   }
 }
 
 // Taps: rt (<= 32) patch rows per workgroup are normalised into LDS, then
 // written channel-first so that consecutive lanes store consecutive patches.
-template <int V>
+template <int V4, int LPR>
 __global__ __launch_bounds__(256) void tap_kernel(const float* __restrict__ x, int tokens, int first_patch,
                                                   int patches, int dim, const float* __restrict__ g,
                                                   const float* __restrict__ b, float eps, float* __restrict__ taps,
                                                   size_t tap_stride, int rt) {
+  constexpr int RPW = 64 / LPR;
   extern __shared__ float tile[];  // [rt][dim + 1]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sl = lane % LPR;
   const int bimg = blockIdx.y;
   const int p0 = blockIdx.x * rt;
   const int ld = dim + 1;
-  for (int r = wave; r < rt; r += 4) {
+  for (int r0 = wave * RPW; r0 < rt; r0 += 4 * RPW) {  // uniform over the wave
+    const int r = r0 + lane / LPR;
     const int i = p0 + r;
-    if (i >= patches) break;
-    float v[V];
-    ln_row<V>(x + ((size_t)bimg * tokens + first_patch + i) * dim, g, b, eps, dim, lane, v);
+    float4 v[V4];
+    ln_vec<V4, LPR>(x + ((size_t)bimg * tokens + first_patch + min(i, patches - 1)) * dim, g, b, eps, dim, sl, v);
+    if (r < rt && i < patches) {
 #pragma unroll
-    for (int k = 0; k < V; ++k) tile[r * ld + lane + 64 * k] = v[k];
+      for (int k = 0; k < V4; ++k) {
+        float* t = tile + r * ld + 4 * (sl + LPR * k);
+        t[0] = v[k].x, t[1] = v[k].y, t[2] = v[k].z, t[3] = v[k].w;
+      }
+    }
   }
   __syncthreads();
   float* out = taps + (size_t)bimg * tap_stride;
@@ -86,24 +121,29 @@ __global__ __launch_bounds__(256) void tap_kernel(const float* __restrict__ x, i
   }
 }
 
-template <int V>
+template <int V4, int LPR>
 __global__ __launch_bounds__(256) void ln_l2_kernel(const float* __restrict__ x, int batch, int tokens,
                                                     int first_patch, int patches, int dim,
                                                     const float* __restrict__ g, const float* __restrict__ b,
                                                     float eps, bf16_t* __restrict__ feats) {
+  constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= batch * patches) return;
-  const int bimg = row / patches, i = row - bimg * patches;
-  float v[V];
-  ln_row<V>(x + ((size_t)bimg * tokens + first_patch + i) * dim, g, b, eps, dim, lane, v);
+  const int sl = lane % LPR;
+  const int rows = batch * patches;
+  const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const int rc = min(row, rows - 1);
+  const int bimg = rc / patches, i = rc - bimg * patches;
+  float4 v[V4];
+  ln_vec<V4, LPR>(x + ((size_t)bimg * tokens + first_patch + i) * dim, g, b, eps, dim, sl, v);
   float s = 0.f;
 #pragma unroll
-  for (int k = 0; k < V; ++k) s += v[k] * v[k];
-  const float inv = 1.0f / fmaxf(sqrtf(wave_sum(s)), 1e-12f);
-  bf16_t* fr = feats + (size_t)row * dim;
+  for (int k = 0; k < V4; ++k) s += (v[k].x * v[k].x + v[k].y * v[k].y) + (v[k].z * v[k].z + v[k].w * v[k].w);
+  const float inv = 1.0f / fmaxf(sqrtf(group_sum<LPR>(s)), 1e-12f);
+  if (row >= rows) return;
 #pragma unroll
-  for (int k = 0; k < V; ++k) fr[lane + 64 * k] = f2bf(v[k] * inv);
+  for (int k = 0; k < V4; ++k)
+    reinterpret_cast<uint2*>(feats)[(size_t)row * (dim / 4) + sl + LPR * k] =
+        make_uint2(pack_bf16x2(v[k].x * inv, v[k].y * inv), pack_bf16x2(v[k].z * inv, v[k].w * inv));
 }
 
 __global__ __launch_bounds__(64) void descriptor_kernel(const float* __restrict__ x, size_t row_stride, int dim,
@@ -148,11 +188,12 @@ template <int V>
 struct LnLaunch {
   static hipError_t go(const float* x, int rows, int dim, const float* g, const float* b, float eps, void* y,
                        bool f32, hipStream_t s) {
-    const dim3 grid((rows + 3) / 4);
+    using L = LnShape<V>;
+    const dim3 grid((rows + 4 * L::RPW - 1) / (4 * L::RPW));
     if (f32)
-      hipLaunchKernelGGL((layernorm_kernel<V, true>), grid, dim3(256), 0, s, x, rows, dim, g, b, eps, y);
+      hipLaunchKernelGGL((layernorm_kernel<L::V4, L::LPR, true>), grid, dim3(256), 0, s, x, rows, dim, g, b, eps, y);
     else
-      hipLaunchKernelGGL((layernorm_kernel<V, false>), grid, dim3(256), 0, s, x, rows, dim, g, b, eps, y);
+      hipLaunchKernelGGL((layernorm_kernel<L::V4, L::LPR, false>), grid, dim3(256), 0, s, x, rows, dim, g, b, eps, y);
     return hipGetLastError();
   }
 };
@@ -161,11 +202,12 @@ template <int V>
 struct TapLaunch {
   static hipError_t go(const float* x, int batch, int tokens, int first_patch, int patches, int dim,
                        const float* g, const float* b, float eps, float* taps, size_t tap_stride, hipStream_t s) {
+    using L = LnShape<V>;
     const int rt = (int)std::min<size_t>(32, 65536 / ((size_t)(dim + 1) * sizeof(float)));
     const size_t lds = (size_t)rt * (dim + 1) * sizeof(float);
     const dim3 grid((patches + rt - 1) / rt, batch);
-    hipLaunchKernelGGL((tap_kernel<V>), grid, dim3(256), lds, s, x, tokens, first_patch, patches, dim, g, b, eps,
-                       taps, tap_stride, rt);
+    hipLaunchKernelGGL((tap_kernel<L::V4, L::LPR>), grid, dim3(256), lds, s, x, tokens, first_patch, patches, dim, g,
+                       b, eps, taps, tap_stride, rt);
     return hipGetLastError();
   }
 };
@@ -174,9 +216,10 @@ template <int V>
 struct LnL2Launch {
   static hipError_t go(const float* x, int batch, int tokens, int first_patch, int patches, int dim,
                        const float* g, const float* b, float eps, uint16_t* feats, hipStream_t s) {
-    const dim3 grid((batch * patches + 3) / 4);
-    hipLaunchKernelGGL((ln_l2_kernel<V>), grid, dim3(256), 0, s, x, batch, tokens, first_patch, patches, dim, g, b,
-                       eps, feats);
+    using L = LnShape<V>;
+    const dim3 grid((batch * patches + 4 * L::RPW - 1) / (4 * L::RPW));
+    hipLaunchKernelGGL((ln_l2_kernel<L::V4, L::LPR>), grid, dim3(256), 0, s, x, batch, tokens, first_patch, patches,
+                       dim, g, b, eps, feats);
     return hipGetLastError();
   }
 };
@@ -186,18 +229,22 @@ struct LnL2Launch {
 hipError_t launch_layernorm(const float* x, int rows, int dim, const float* g, const float* b, float eps, void* y,
                             bool out_f32, hipStream_t s) {
   if (rows <= 0 || dim <= 0 || dim % 64 != 0 || dim > 64 * MAXV) return hipErrorInvalidValue;
+  // float4 access of x, g, b and y
+  if (((uintptr_t)x | (uintptr_t)g | (uintptr_t)b | (uintptr_t)y) % 16 != 0) return hipErrorInvalidValue;
   return by_width<LnLaunch>(dim, x, rows, dim, g, b, eps, y, out_f32, s);
 }
 
 hipError_t launch_tap(const float* x, int batch, int tokens, int first_patch, int patches, int dim, const float* g,
                       const float* b, float eps, float* taps, size_t tap_stride, hipStream_t s) {
-  if (dim % 64 != 0 || patches <= 0) return hipErrorInvalidValue;
+  if (dim % 64 != 0 || patches <= 0 || dim > 64 * MAXV) return hipErrorInvalidValue;
+  if (((uintptr_t)x | (uintptr_t)g | (uintptr_t)b) % 16 != 0) return hipErrorInvalidValue;
   return by_width<TapLaunch>(dim, x, batch, tokens, first_patch, patches, dim, g, b, eps, taps, tap_stride, s);
 }
 
 hipError_t launch_ln_l2(const float* x, int batch, int tokens, int first_patch, int patches, int dim, const float* g,
                         const float* b, float eps, uint16_t* feats, hipStream_t s) {
-  if (dim % 64 != 0 || patches <= 0) return hipErrorInvalidValue;
+  if (dim % 64 != 0 || patches <= 0 || dim > 64 * MAXV) return hipErrorInvalidValue;
+  if (((uintptr_t)x | (uintptr_t)g | (uintptr_t)b | (uintptr_t)feats) % 16 != 0) return hipErrorInvalidValue;
   return by_width<LnL2Launch>(dim, x, batch, tokens, first_patch, patches, dim, g, b, eps, feats, s);
 }
 

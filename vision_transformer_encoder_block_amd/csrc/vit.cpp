@@ -545,6 +545,7 @@ int vit_create(const vit_config* cfg, const float* host_params, size_t host_floa
 int vit_forward(vit_model* m, const float* d_images, int batch, float* d_tokens, float* d_taps, void* stream) {
   if (!m || !d_images || !d_tokens) return fail(VIT_ERR_ARG, "NULL model, image or token pointer");
   if (batch < 1 || batch > m->pl.cfg.max_batch) return fail(VIT_ERR_SIZE, "batch must be in [1, max_batch]");
+  if ((uintptr_t)d_tokens % 16) return fail(VIT_ERR_ARG, "d_tokens must be 16-byte aligned");
   return run_encoder(m, m->pl.main, d_images, batch, d_tokens, d_taps, false, (hipStream_t)stream);
 }
 
