@@ -59,8 +59,9 @@ int vit_op_qkv(const void* h, const void* wqkv, const float* bqkv, int batch, in
 /* Multi-head attention core, O = softmax(Q K^T / sqrt(64)) V per (batch, head)
  * with the softmax over keys (LibreYOLO diagram, "Encoder self-attention";
  * the logits stay fp32, model card "Build BF16, not FP16").
- *   q, k, vt as produced by vit_op_qkv; o [batch, tokens, heads*64] bf16
- *   (heads merged in channel order).
+ *   q, k, vt as produced by vit_op_qkv (the columns >= tokens of vt are
+ *   ignored, whatever they hold); o [batch, tokens, heads*64] bf16 (heads
+ *   merged in channel order).
  *   work, work_bytes: device scratch for fp32 partial results; with at least
  *   vit_op_attention_workspace(batch, tokens, heads) bytes the last, partly
  *   filled query tile of every head may be spread over key ranges (better

@@ -133,8 +133,8 @@ def test_qkv_split(batch, tokens, heads):
     cols = vt_position(np.arange(tokens))
     gv_t = gv[:, :, :, cols]
     assert np.all(np.abs(gv_t - ref_v) <= 2 ** -8 * np.abs(ref_v) + acc[:, :, 2].transpose(0, 2, 3, 1))
-    untouched = np.setdiff1d(np.arange(nv), cols)
-    assert np.all(gv[:, :, :, untouched] == 0)
+    pad = np.setdiff1d(np.arange(nv), cols)
+    assert np.all(gv[:, :, :, pad] == 0)  # not written
 
 
 # ------------------------------------------------------------------ attention core

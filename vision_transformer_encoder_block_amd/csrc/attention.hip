@@ -38,8 +38,8 @@ __device__ __forceinline__ int vt_tok(int p) { return (p & ~12) | ((p & 4) << 1)
 // ds_read_b128 cover all 64 banks.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// One workgroup: NW waves x 32 query rows starting at q_first + 32 NW blockIdx.x
-// (full pass) or at q_first (partial pass), against the keys of
+// One workgroup: NW waves x 32 query rows starting at q_first + 32 NW qt (full
+// pass, qt from full_coords) or at q_first (partial pass), against the keys of
 // [key_first, key_end).  The full pass writes the normalised output; the
 // partial pass writes this key range's running max, sum and unnormalised
 // output per row, merged afterwards by combine_kernel.
@@ -53,83 +53,156 @@ struct AttnArgs {
   int q_first;     // first query row of the launch
   int part_rows;   // partial pass: rows per (b, h) in `part`
   int keys_per_split;
+  int qtiles;      // full pass: query tiles per (b, h); the grid is 1-D
+  int B;
 };
 
+// Full pass: workgroup id -> (query tile, head, image).  Workgroups are handed
+// to the 8 XCDs round-robin by id; the ids are renumbered so that each XCD
+// gets a contiguous run of (image, head) pairs and all query tiles of a pair
+// meet the same K and V^T in that XCD's L2.
+__device__ __forceinline__ void full_coords(int bid, int qtiles, int H, int B, int& qt, int& h, int& b) {
+  constexpr int XCD = 8;
+  const int n = qtiles * H * B;
+  const int per = (n + XCD - 1) / XCD;
+  int tall = n % XCD;
+  if (tall == 0) tall = XCD;
+  const int xcd = bid % XCD, local = bid / XCD;
+  const int pid = xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+  qt = pid % qtiles;
+  const int bh = pid / qtiles;
+  h = bh % H;
+  b = bh / H;
+}
+
+// At most 168 VGPRs (3 waves per SIMD): three 4-wave workgroups per CU keep
+// e.g. a ViT-S/16 @336 batch of 32 (768 workgroups) resident in one round.
 template <int NW, bool kPartial>
-__global__ __launch_bounds__(64 * NW) void attention_kernel(AttnArgs a) {
-  constexpr int CH = 512 / (64 * NW);  // 16-byte chunks per thread per K (or V^T) tile
-  __shared__ uint4 Ks[2][KT * 8];
-  __shared__ uint4 Vs[2][64 * 8];
+__global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a) {
+  constexpr int S = 3;         // K / V^T tile stages in LDS
+  constexpr int IPW = 8 / NW;  // DMA instructions per wave per K (or V^T) tile
+  constexpr int L = 2 * IPW;   // ... per tile of both
+  static_assert(S * L < 64, "vmcnt range");
+  __shared__ uint4 KV[S][2][KT * 8];  // [stage][K | V^T][16-byte chunk]
 
   const int N = a.N, H = a.H, nv = a.nv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.y, b = blockIdx.z;
+  int qt = 0, h, b;
+  if constexpr (kPartial) {
+    h = blockIdx.y, b = blockIdx.z;
+  } else {
+    full_coords(blockIdx.x, a.qtiles, H, a.B, qt, h, b);
+  }
   const size_t bh = (size_t)b * H + h;
   const bf16_t* Qp = a.Q + bh * N * 64;
   const bf16_t* Kp = a.K + bh * N * 64;
   const bf16_t* Vp = a.Vt + bh * 64 * nv;
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int split = kPartial ? blockIdx.x : 0;
-  const int qrow = a.q_first + (kPartial ? 0 : blockIdx.x * 32 * NW) + wave * 32 + lrow;
+  const int qrow = a.q_first + qt * 32 * NW + wave * 32 + lrow;
   const int key_first = kPartial ? split * a.keys_per_split : 0;
   const int key_end = kPartial ? min(N, key_first + a.keys_per_split) : N;
 
   // rows past N read as zeros through the buffer range checks
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qp, (uint32_t)N * 128u);
-  const __amdgpu_buffer_rsrc_t rk_src = make_rsrc(Kp, (uint32_t)N * 128u);
-  const __amdgpu_buffer_rsrc_t rv_src = make_rsrc(Vp, (uint32_t)nv * 128u);
+  const int32x4 rk_w = make_rsrc_words(Kp, (uint32_t)N * 128u);
+  const int32x4 rv_w = make_rsrc_words(Vp, (uint32_t)nv * 128u);
   bf16x8 qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(buf_load16(rq, (uint32_t)qrow * 128u + ks * 32 + lhalf * 16));
 
-  // cooperative tile loads: 512 chunks of K and 512 of V^T
-  int k_dst[CH], v_dst[CH], row_c[CH], q_c[CH];
+  // K and V^T tiles (64 rows of 8 chunks of 16 bytes) arrive by direct-to-LDS
+  // buffer loads: each wave instruction fills 8 rows (1 KB); the lane at slot
+  // (row, p) fetches the logical chunk p ^ ((row >> 1) & 7), which is where the
+  // swizzled reads below look for it.  K rows past N come back as zeros; the
+  // V^T columns of keys >= N (padding of unspecified content) are zeroed in
+  // LDS once the ragged last tile has landed, so they meet p = 0 as zeros.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t kv_base = lds_addr(&KV[0][0][0]);
+  uint32_t k_off[IPW], v_off[IPW];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int cid = tid + c * 64 * NW;
-    row_c[c] = cid >> 3;  // key row of K / channel row of V^T
-    q_c[c] = cid & 7;     // 16-byte chunk
-    k_dst[c] = row_c[c] * 8 + swz(row_c[c], q_c[c]);
-    v_dst[c] = k_dst[c];
+  for (int j = 0; j < IPW; ++j) {
+    const int row = (j * NW + wave) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    k_off[j] = (uint32_t)row * 128u + c * 16u;
+    v_off[j] = (uint32_t)row * (uint32_t)nv * 2u + c * 16u;
   }
-  auto load_tile = [&](int t, uint4* rk, uint4* rv) {
+  auto issue = [&](int t, int stage) {
+    const uint32_t k0 = (uint32_t)t * KT;
+    const uint32_t kb = kv_base + (uint32_t)stage * (2 * KT * 8 * 16);
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) dma16(rk_w, k_off[j] + k0 * 128u, kb + (uint32_t)(j * NW + wave_u) * 1024u);
+#pragma unroll
+    for (int j = 0; j < IPW; ++j)
+      dma16(rv_w, v_off[j] + k0 * 2u, kb + KT * 8 * 16 + (uint32_t)(j * NW + wave_u) * 1024u);
+  };
+  // wait until at most `later` tiles of this wave's loads are in flight
+  auto wait_tiles = [&](int later) {
+    if (later <= 0) wait_vm<0>();
+    else if (later == 1) wait_vm<L>();
+    else wait_vm<2 * L>();
+  };
+  static_assert(S <= 3, "wait_tiles covers up to two tiles in flight");
+  // Zero the V^T entries of keys >= N in the stage holding tile t (called by
+  // every thread after the barrier that publishes it; a barrier follows).
+  auto fix_last = [&](int t, int stage) {
+    uint4* vs = KV[stage][1];
     const int k0 = t * KT;
+    for (int cid = tid; cid < 64 * 8; cid += 64 * NW) {
+      const int r = cid >> 3, c = cid & 7;
+      const int p0 = k0 + c * 8;
+      uint4& u = vs[r * 8 + swz(r, c)];
+      uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      rk[c] = buf_load16(rk_src, (uint32_t)(k0 + row_c[c]) * 128u + q_c[c] * 16);
-      const int p0 = k0 + q_c[c] * 8;  // < nv: nv is a multiple of 64
-      uint4 u = buf_load16(rv_src, ((uint32_t)row_c[c] * nv + p0) * 2u);
-      if (k0 + KT > N) {  // last tile: zero the positions of keys >= N
-        uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (vt_tok(p0 + e) >= N) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-        u = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-      rv[c] = u;
+      for (int e = 0; e < 8; ++e)
+        if (vt_tok(p0 + e) >= N) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+      u = make_uint4(w[0], w[1], w[2], w[3]);
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = 0.f, l_run = 0.f;
   f32x16 o[2];
 #pragma unroll
   for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = 0.f;
+  // Fifth MFMA k-step of S^T: ones (keys) x -m_run (queries) subtracts the
+  // reference max inside the accumulation.  -m_run is split into three bf16
+  // parts (8 + 8 + 8 significant bits cover fp32's 24, so the split is exact);
+  // they sit in k-slots 0..2, held by the lower lane half.
+  bf16x8 ones, mneg;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ones[e] = (__bf16)((lhalf == 0 && e < 3) ? 1.f : 0.f);
+    mneg[e] = (__bf16)0.f;
+  }
+  auto set_mneg = [&](float m) {
+    const float n = -m;
+    const __bf16 h0 = (__bf16)n;
+    const float r1 = n - (float)h0;
+    const __bf16 h1 = (__bf16)r1;
+    const __bf16 h2 = (__bf16)(r1 - (float)h1);
+    mneg[0] = lhalf == 0 ? h0 : (__bf16)0.f;
+    mneg[1] = lhalf == 0 ? h1 : (__bf16)0.f;
+    mneg[2] = lhalf == 0 ? h2 : (__bf16)0.f;
+  };
 
   // key ranges start on a tile boundary; only the global last tile is ragged
   const int t_first = key_first / KT;
-  const int t_end = (key_end + KT - 1) / KT;
-  uint4 rk[CH], rv[CH];
-  load_tile(t_first, rk, rv);
+  const int nt = (key_end + KT - 1) / KT - t_first;
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    Ks[0][k_dst[c]] = rk[c];
-    Vs[0][v_dst[c]] = rv[c];
+  for (int i = 0; i < S - 1; ++i)
+    if (i < nt) issue(t_first + i, i);
+  wait_tiles(min(S - 2, nt - 1));  // tile t_first is in
+  barrier_keep_loads();
+  if ((t_first + 1) * KT > N) {
+    fix_last(t_first, 0);
+    __syncthreads();
   }
-  __syncthreads();
 
-  for (int t = t_first; t < t_end; ++t) {
-    const int cur = (t - t_first) & 1;
-    if (t + 1 < t_end) load_tile(t + 1, rk, rv);
+  for (int i = 0; i < nt; ++i) {
+    const int t = t_first + i;
+    const int stage = i % S;
+    const uint4* Ks = KV[stage][0];
+    const uint4* Vs = KV[stage][1];
 
     // S^T for keys t*64 + kb*32 + [0, 32): element e <-> key 8*(e/4) + 4*lhalf + e%4.
     // All K fragments are read before the MFMAs, and the V fragments right
@@ -139,14 +212,15 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       const int r = kb * 32 + lrow;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[kb][ks] = as_bf16x8(Ks[cur][r * 8 + swz(r, ks * 2 + lhalf)]);
+      for (int ks = 0; ks < 4; ++ks) kf[kb][ks] = as_bf16x8(Ks[r * 8 + swz(r, ks * 2 + lhalf)]);
     }
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int r = db * 32 + lrow;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) vf[db][ks] = as_bf16x8(Vs[cur][r * 8 + swz(r, ks * 2 + lhalf)]);
+      for (int ks = 0; ks < 4; ++ks) vf[db][ks] = as_bf16x8(Vs[r * 8 + swz(r, ks * 2 + lhalf)]);
     }
+    // s = S^T - m_run (the first tile of the range runs with m_run = 0)
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -154,6 +228,7 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(AttnArgs a) {
       for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) s[kb] = mfma32x32x16(kf[kb][ks], qf[ks], s[kb]);
+      s[kb] = mfma32x32x16(ones, mneg, s[kb]);
     }
     if ((t + 1) * KT > N) {
 #pragma unroll
@@ -164,61 +239,70 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(AttnArgs a) {
           if (key >= N) s[kb][e] = -INFINITY;
         }
     }
-    float mt = s[0][0];
+    // tile max of this lane's 32 logits as a tree (short dependency chain)
+    float mx[8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = (kb == 0); e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
+    for (int i = 0; i < 8; ++i) mx[i] = fmaxf(fmaxf(s[i >> 2][(i & 3) * 4], s[i >> 2][(i & 3) * 4 + 1]),
+                                          fmaxf(s[i >> 2][(i & 3) * 4 + 2], s[i >> 2][(i & 3) * 4 + 3]));
+    float mt = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])), fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
     mt = half_swap_max(mt);
     // Lazy rescaling: the reference max m_run only moves (and O, l are only
     // rescaled) when some query's tile max exceeds it by more than 8, so
-    // p = exp2(s - m_run) <= 2^8.  Tile 0 always moves it (m_run = -inf, and
-    // tile 0 holds key 0).  Numerator and denominator share m_run, so the
-    // final O / l is unchanged.
-    const bool grow = mt > m_run + 8.0f;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+    // p = 2^(s - m_run) <= 2^8; the first tile of the range always sets it.
+    // Numerator and denominator share m_run, so the final O / l is unchanged.
+    float shift = 0.f;
+    if (t == t_first || __builtin_amdgcn_ballot_w64(mt > 8.0f)) {
+      shift = t == t_first ? mt : fmaxf(mt, 0.f);
+      const float alpha = t == t_first ? 0.f : __builtin_amdgcn_exp2f(-shift);
       l_run *= alpha;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         o[0][e] *= alpha;
         o[1][e] *= alpha;
       }
+      m_run += shift;
+      set_mneg(m_run);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] -= shift;
     }
-    const float m_use = m_run;
-    // probabilities, packed as the B operand of the 4 key steps of P V
+    // probabilities, packed as the B operand of the 4 key steps of P V; their
+    // sum as a tree of pairwise adds
     bf16x8 pf[4];
+    float ps[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(s[kb][half * 8 + e] - m_use);
-          l_run += p[e];
-        }
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[kb][half * 8 + e]);
+        ps[kb * 2 + half] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         uint4 u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                              pack_bf16x2(p[6], p[7]));
         pf[kb * 2 + half] = as_bf16x8(u);
       }
     }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     // O^T[d, q] += V^T[d, keys] P^T[keys, q]; d = db*32 + row of the MFMA
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) o[db] = mfma32x32x16(vf[db][ks], pf[ks], o[db]);
 
-    if (t + 1 < t_end) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        Ks[cur ^ 1][k_dst[c]] = rk[c];
-        Vs[cur ^ 1][v_dst[c]] = rv[c];
+    if (i + 1 < nt) {
+      // refill the stage read in the previous step (every wave passed the
+      // barrier after it), then wait for this wave's part of tile i + 1 and
+      // publish it; the barrier also retires this step's stage
+      if (i + S - 1 < nt) issue(t + S - 1, (i + S - 1) % S);
+      wait_tiles(min(S - 2, nt - 2 - i));
+      barrier_keep_loads();
+      if ((t + 2) * KT > N) {
+        fix_last(t + 1, (i + 1) % S);
+        __syncthreads();
       }
     }
-    __syncthreads();
   }
 
   if constexpr (kPartial) {
@@ -326,9 +410,9 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
     p.full_rows = tokens;  // no workspace: the last tile stays in the main pass
     p.tail_rows = 0;
   }
-  AttnArgs a{q, k, vt, o, work, tokens, heads, nv, 0, 0, 0};
-  dim3 grid((p.full_rows + QT - 1) / QT, heads, batch);
-  hipLaunchKernelGGL((attention_kernel<4, false>), grid, dim3(256), 0, s, a);
+  const int qtiles = (p.full_rows + QT - 1) / QT;
+  AttnArgs a{q, k, vt, o, work, tokens, heads, nv, 0, 0, 0, qtiles, batch};
+  hipLaunchKernelGGL((attention_kernel<4, false>), dim3(qtiles * heads * batch), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.tail_rows == 0) return e;
   a.q_first = p.full_rows;

@@ -348,7 +348,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 // read by 16 consecutive lanes of one ds_read_b128 hit distinct 4-bank groups.
 template <int BKT>
 __device__ __forceinline__ int swz_k(int r, int c) {
-  if constexpr (BKT == 64) return c ^ ((r >> 1) & 7);
+  if constexpr (BKT == 32) return c ^ ((r >> 2) & 3);
+  else if constexpr (BKT == 64) return c ^ ((r >> 1) & 7);
   else return c ^ (r & 15);
 }
 
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   constexpr int L = A_IT + B_IT;
   constexpr int KS = BKT / 16;                      // MFMA k-steps per stage
   constexpr int STAGE_BYTES = (BM + BN) * BKT * 2;
-  static_assert(BKT == 64 || BKT == 128, "BK");
+  static_assert(BKT == 32 || BKT == 64 || BKT == 128, "BK");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(A_IT * RPI * NW == BM && B_IT * RPI * NW == BN, "DMA split");
   static_assert(S >= 2 && S * L < 64, "pipeline depth");
