@@ -110,23 +110,4 @@ __device__ __forceinline__ float half_swap_max(float v) {
   return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 
-// GELU in its erf form, x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), with erf from
-// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
-// erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
-// t = 1 / (1 + p z), z >= 0, absolute error <= 1.5e-7 (odd extension for z < 0).
-// One exp and one reciprocal per value instead of a library erf.
-__device__ __forceinline__ float erf_as(float z) {
-  const float a = fabsf(z);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, a, 1.0f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  poly *= t;
-  const float e = __builtin_amdgcn_exp2f(-a * a * 1.4426950408889634f);
-  const float r = fmaf(-poly, e, 1.0f);
-  return copysignf(r, z);
-}
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f)); }
-
 }  // namespace vit
