@@ -22,6 +22,8 @@ Sources (web pages; sections named as they appear there):
 * DINOv2 ONNX/TensorRT article (gitcode blog): DinoVisionTransformer class
   diagram (patch_embed, cls_token, pos_embed, register_tokens, blocks, norm),
   ``forward_features(x)["x_norm_clstoken"]``, model size table.
+* DINOv2 ONNX/TensorRT deployment article: the FastAPI service's frame
+  preprocessing (cv2 decode, BGR to RGB, cv2.resize, /255).
 * dino.txt zero-shot segmentation article (hotelren): ViT-L/16 patch tokens
   after 2 extra attention blocks, per-patch L2 normalisation and cosine against
   class embeddings, whole mode (bilinear upsample, align_corners=False, argmax)
@@ -35,7 +37,9 @@ GELU is the exact erf form; the descriptor's L2 epsilon is 1e-12; taps use the
 backbone's final LayerNorm parameters; the extra dino.txt blocks are ordinary
 pre-LN blocks followed by the single final LayerNorm; bicubic resampling uses
 the cubic-convolution kernel with a = -0.75 and half-pixel centres; slide
-windows are full size with the last one moved back to end at the border.
+windows are full size with the last one moved back to end at the border;
+frame preprocessing resamples the 8-bit values bilinearly without rounding
+them back to 8 bits.
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (library routines in float64, brute force on tiny
@@ -351,6 +355,38 @@ def bilinear_resize(x: np.ndarray, out_h: int, out_w: int) -> np.ndarray:
     x = np.asarray(x, F64)
     rows = x[:, y0, :] * (1.0 - ly)[None, :, None] + x[:, y1, :] * ly[None, :, None]
     return rows[:, :, x0] * (1.0 - lx)[None, None, :] + rows[:, :, x1] * lx[None, None, :]
+
+
+# ---------------------------------------------------------------------------
+# frame preprocessing (the step right before the encoder)
+
+IMAGENET_MEAN = (0.485, 0.456, 0.406)  # RGB; model card, "Model I/O"
+IMAGENET_STD = (0.229, 0.224, 0.225)
+
+
+def preprocess(frames: np.ndarray, out_h: int, out_w: int, bgr: bool = False) -> np.ndarray:
+    """8-bit HWC frames [B, h, w, 3] -> ImageNet-normalised CHW images [B, 3, out_h, out_w].
+
+    The deployment article's service decodes a frame (BGR), converts it to RGB
+    and resizes it with cv2's default bilinear interpolation (half-pixel
+    centres, edges clamped); the model card fixes the input as ImageNet-
+    normalised RGB CHW with mean (0.485, 0.456, 0.406) and std (0.229, 0.224,
+    0.225), with the 8-bit values scaled by 1/255.  Reading: the resize is the
+    exact bilinear resampling of the 8-bit values, without rounding back to 8
+    bits in between.
+    """
+    f = np.asarray(frames)
+    if f.ndim != 4 or f.shape[-1] != 3 or f.dtype != np.uint8:
+        raise ValueError("frames must be uint8 [B, h, w, 3]")
+    if bgr:
+        f = f[..., ::-1]
+    mean = np.asarray(IMAGENET_MEAN, F64)[:, None, None]
+    std = np.asarray(IMAGENET_STD, F64)[:, None, None]
+    out = np.empty((f.shape[0], 3, out_h, out_w), dtype=F64)
+    for i in range(f.shape[0]):
+        chw = np.asarray(f[i], F64).transpose(2, 0, 1)
+        out[i] = (bilinear_resize(chw, out_h, out_w) / 255.0 - mean) / std
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -267,6 +267,21 @@ def test_two_runs_are_bitwise_equal(vits336):
     np.testing.assert_array_equal(a, b)
 
 
+def test_position_table_resampled_to_the_image_grid():
+    """One weight set at another resolution: a ViT-S/16 whose position table is
+    stored for 224 x 224 (14 x 14 patches) runs on 336 x 336 images; the library
+    resamples the table bicubically to 21 x 21 at creation (LibreYOLO diagram,
+    "Bicubic interpolation"), the oracle with its own resample_pos."""
+    cfg = synth.preset("vits16_224", img_h=336, img_w=336, pos_grid=(14, 14), depth=4)
+    say("ViT-S/16 with a 14x14 position table at 336x336, b2")
+    P = synth.make_params(cfg)
+    assert P["pos"].shape[0] == 1 + 14 * 14
+    x = synth.make_images(cfg, 2)
+    pos = O.resample_pos(P["pos"], (14, 14), (21, 21))
+    ref = O.forward(x, P, cfg, pos=pos)
+    gate(*run_gpu(cfg, P, x)[:2], ref)
+
+
 def test_graph_replay_matches_eager():
     """The forward (with taps and the descriptor) captured as a HIP graph and
     replayed on new inputs, with eager work and synchronisations between the

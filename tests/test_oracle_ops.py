@@ -274,3 +274,49 @@ def test_sdpa_matches_torch_with_scale():
         ref = F.scaled_dot_product_attention(t64(q)[None], t64(k)[None], t64(v)[None], scale=scale)[0].numpy()
         np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
         assert smax == pytest.approx(np.abs(q @ k.T).max() * scale)
+
+
+# --------------------------------------------------------------------- frame preprocessing
+
+def _facts():
+    import json, os
+    return json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")))
+
+
+def test_preprocess_constants_are_the_cards():
+    f = _facts()["imagenet_normalisation"]
+    assert tuple(O.IMAGENET_MEAN) == tuple(f["mean"]) and tuple(O.IMAGENET_STD) == tuple(f["std"])
+
+
+@pytest.mark.parametrize("frame,out", [((2, 37, 53), (45, 31)), ((1, 72, 128), (33, 33)), ((1, 20, 20), (64, 48))])
+def test_preprocess_matches_torch(frame, out):
+    """Resize + normalise against torch's bilinear interpolate (align_corners=False)
+    on the 0..1-scaled frame, a routine the oracle does not use."""
+    f = RNG.integers(0, 256, size=frame + (3,), dtype=np.uint8)
+    got = O.preprocess(f, *out)
+    t = torch.from_numpy(f.astype(np.float64)).permute(0, 3, 1, 2) / 255.0
+    r = F.interpolate(t, size=out, mode="bilinear", align_corners=False)
+    mean = torch.tensor([0.485, 0.456, 0.406], dtype=torch.float64)[None, :, None, None]
+    std = torch.tensor([0.229, 0.224, 0.225], dtype=torch.float64)[None, :, None, None]
+    np.testing.assert_allclose(got, ((r - mean) / std).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_preprocess_special_cases():
+    # same size: no resampling, only the per-channel normalisation
+    f = RNG.integers(0, 256, size=(1, 6, 9, 3), dtype=np.uint8)
+    got = O.preprocess(f, 6, 9)
+    for c, (m, s) in enumerate(zip((0.485, 0.456, 0.406), (0.229, 0.224, 0.225))):
+        np.testing.assert_allclose(got[0, c], (f[0, :, :, c] / 255.0 - m) / s, rtol=0, atol=1e-14)
+    # BGR input is the RGB result of the channel-reversed frame
+    np.testing.assert_array_equal(O.preprocess(f, 4, 5, bgr=True), O.preprocess(f[..., ::-1].copy(), 4, 5))
+    # a horizontal ramp v = 2x halved: output column j samples x = 2j + 0.5, i.e. v = 4j + 1
+    ramp = np.zeros((1, 4, 128, 3), dtype=np.uint8)
+    ramp[0, :, :, :] = (2 * np.arange(128, dtype=np.uint8))[None, :, None]
+    got = O.preprocess(ramp, 4, 64)
+    want = ((4 * np.arange(64) + 1) / 255.0 - 0.485) / 0.229
+    np.testing.assert_allclose(got[0, 0, 2], want, rtol=0, atol=1e-12)
+    # a 2-pixel row doubled: edge pixels replicate, the inner samples weigh 3:1
+    two = np.array([[[[40, 40, 40], [200, 200, 200]]]], dtype=np.uint8)
+    got = O.preprocess(two, 1, 4)[0, 1, 0] * 0.224 + 0.456
+    np.testing.assert_allclose(got * 255.0, [40, 80, 160, 200], rtol=0, atol=1e-9)
+
