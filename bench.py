@@ -99,6 +99,25 @@ def bench_workload(name, batch, steps, warmup):
     return cfg, enc, res
 
 
+def bench_preprocess(batch=32, src=(720, 1280), dst=(336, 336), steps=50, warmup=10):
+    """Frame preprocessing (8-bit BGR HWC -> normalised CHW) at the live-camera
+    frame size of the model card into the ViT-S/16 @336 input, HBM-bound:
+    algorithmic bytes = frames read once + fp32 images written."""
+    import torch
+    import vision_transformer_encoder_block_amd as vit
+    g = torch.Generator(device="cuda").manual_seed(5000)
+    frames = torch.randint(0, 256, (batch,) + src + (3,), dtype=torch.uint8, device="cuda", generator=g)
+    out = torch.empty((batch, 3) + dst, dtype=torch.float32, device="cuda")
+    ms, _ = time_gpu(lambda: vit.vit_op_preprocess(frames, batch, src[0], src[1], True, out, dst[0], dst[1]),
+                     steps, warmup)
+    nbytes = batch * (src[0] * src[1] * 3 + 3 * dst[0] * dst[1] * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"{batch} BGR frames {src[1]}x{src[0]} -> {dst[1]}x{dst[0]} ImageNet-normalised",
+            "frames_per_s": batch / (ms * 1e-3), "us_per_batch": ms * 1e3, "bytes_per_batch": nbytes,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS}}
+
+
 def kernel_breakdown(cfg, batch, steps=20, warmup=5):
     """Average duration of each block kernel at the workload's shapes (HIP events
     on the launch stream), through the per-op C ABI entry points."""
@@ -320,6 +339,9 @@ def main():
         cfg_l, enc_l, large = bench_workload("vitl16_1024", 1, args.steps, args.warmup)
         enc_l.close()
         log(json.dumps(large))
+    log("frame preprocessing ...")
+    pre = bench_preprocess()
+    log(json.dumps(pre))
     log("kernel breakdown ...")
     bd = kernel_breakdown(cfg, 32)
     for n, b in bd.items():
@@ -351,6 +373,7 @@ def main():
         out["vitl16_1024_b1"] = {"images_per_s": large["images_per_s"], "ms_per_step": large["ms_per_step"],
                                  "eager_images_per_s": large["eager_images_per_s"],
                                  "tflops": large["tflops"], "pct_bf16_peak": 100 * large["frac_bf16_peak"]}
+    out["preprocess"] = pre
     if not args.no_cpu:
         log("CPU oracle baseline ...")
         out["cpu_baseline"] = cpu_baseline()

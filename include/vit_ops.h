@@ -17,6 +17,21 @@
 extern "C" {
 #endif
 
+/* Frame preprocessing, the step right before the encoder: 8-bit HWC frames
+ * to the ImageNet-normalised RGB CHW input of the model card ("Model I/O":
+ * mean (0.485, 0.456, 0.406), std (0.229, 0.224, 0.225)), resized like the
+ * deployment article's service (cv2.resize default: bilinear, half-pixel
+ * centres, edge pixels replicated) and scaled by 1/255.
+ *   frames [batch, src_h, src_w, 3] uint8, rows packed (stride src_w * 3);
+ *   bgr != 0: channels stored B, G, R (cv2 decode order), else R, G, B.
+ *   images [batch, 3, dst_h, dst_w] fp32 (the d_images of vit_forward).
+ *   The resampled values are not rounded back to 8 bits.
+ *   batch and dst_h at most 65535; all sizes >= 1.  Device pointers, caller-
+ *   owned; enqueue only.  VIT_ERR_ARG for NULL pointers, VIT_ERR_SHAPE for
+ *   sizes out of range. */
+int vit_op_preprocess(const void* frames, int batch, int src_h, int src_w, int bgr, float* images, int dst_h,
+                      int dst_w, void* stream);
+
 /* LayerNorm over the last axis (LibreYOLO DINOv2 diagram, "Encoder block":
  * LayerNorm eps 1e-6): y = (x - mean) / sqrt(var + eps) * g + b, biased var.
  *   x [rows, dim] fp32; g, b [dim]; y [rows, dim], bf16 if out_fp32 == 0 else fp32.

@@ -188,3 +188,20 @@ def test_attention_large_logits_stay_finite():
         assert smax > 1e6
         np.testing.assert_array_equal(ref, np.broadcast_to(v[0, h, 3], ref.shape))
         np.testing.assert_allclose(got[0, :, h], ref, atol=2 ** -8 * np.abs(ref).max() + 1e-6)
+
+
+# ------------------------------------------------------------------ frame preprocessing
+
+@pytest.mark.parametrize("batch,src,dst,bgr", [(2, (720, 1280), (336, 336), True), (1, (37, 53), (45, 31), False),
+                                               (3, (100, 150), (224, 224), False), (1, (518, 518), (518, 518), True),
+                                               (1, (1, 1), (3, 2), False)])
+def test_preprocess(batch, src, dst, bgr):
+    say(f"preprocess batch={batch} {src} -> {dst} bgr={bgr}")
+    frames = RNG.integers(0, 256, size=(batch,) + src + (3,), dtype=np.uint8)
+    fd = torch.from_numpy(frames).cuda()
+    out = torch.empty((batch, 3) + dst, dtype=torch.float32, device="cuda")
+    vit.vit_op_preprocess(fd, batch, src[0], src[1], bgr, out, dst[0], dst[1])
+    ref = O.preprocess(frames, *dst, bgr=bgr)
+    # fp32 weights and sums on values <= 255, then /255/std (std >= 0.224)
+    np.testing.assert_allclose(host(out), ref, rtol=0, atol=2e-5)
+

@@ -1,7 +1,8 @@
-// Input side of the encoder on gfx950: im2col of the fp32 images into the
-// bf16 patch matrix (the A operand of the patch-embedding GEMM), CLS/register
-// rows of the token sequence, bicubic resampling of the position table, the
-// slide-mode window crops and a plain fp32 -> bf16 conversion.
+// Input side of the encoder on gfx950: 8-bit frame preprocessing (resize +
+// ImageNet normalisation), im2col of the fp32 images into the bf16 patch
+// matrix (the A operand of the patch-embedding GEMM), CLS/register rows of the
+// token sequence, bicubic resampling of the position table, the slide-mode
+// window crops and a plain fp32 -> bf16 conversion.
 #include "common.h"
 #include "kernels.h"
 
@@ -122,6 +123,55 @@ __global__ __launch_bounds__(256) void crops_kernel(const float* __restrict__ im
   }
 }
 
+// Source index and weight of output position i along an axis (n_in -> n_out):
+// the centre (i + 1/2) n_in / n_out - 1/2 is the exact rational
+// ((2i + 1) n_in - n_out) / (2 n_out), split into its integer part and an
+// exactly computed remainder, so the weight carries only the rounding of one
+// division (a float coordinate near 700 would carry an ulp of 6e-5).
+// Negative centres clamp to 0; indices past the edge clamp to n_in - 1.
+__device__ __forceinline__ void bilinear_tap(int i, int n_in, int n_out, int& i0, int& i1, float& w) {
+  const long long num = (long long)(2 * i + 1) * n_in - n_out;
+  const long long den = 2LL * n_out;
+  if (num <= 0) {
+    i0 = 0;
+    w = 0.f;
+  } else {
+    const long long q = num / den;
+    i0 = (int)q;
+    w = (float)(num - q * den) / (float)den;
+  }
+  i0 = min(i0, n_in - 1);
+  i1 = min(i0 + 1, n_in - 1);
+}
+
+// Frame preprocessing: one thread per output pixel of one row.  Bilinear
+// sample (half-pixel centres, coordinates clamped at the edges) of the three
+// 8-bit channels, scaled by 1/255 and normalised with the ImageNet mean/std
+// (RGB order), written to three planes.  bgr: the frame stores B, G, R.
+__global__ __launch_bounds__(256) void preprocess_kernel(const uint8_t* __restrict__ frames, int sh, int sw,
+                                                         float* __restrict__ out, int dh, int dw, bool bgr) {
+  const int x = blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= dw) return;
+  const int y = blockIdx.y, b = blockIdx.z;
+  int y0, y1, x0, x1;
+  float ly, lx;
+  bilinear_tap(y, sh, dh, y0, y1, ly);
+  bilinear_tap(x, sw, dw, x0, x1, lx);
+  const uint8_t* f = frames + (size_t)b * sh * sw * 3;
+  const uint8_t* r0 = f + (size_t)y0 * sw * 3;
+  const uint8_t* r1 = f + (size_t)y1 * sw * 3;
+  constexpr float kMean[3] = {0.485f, 0.456f, 0.406f};
+  constexpr float kInvStd[3] = {1.f / 0.229f, 1.f / 0.224f, 1.f / 0.225f};
+#pragma unroll
+  for (int oc = 0; oc < 3; ++oc) {
+    const int c = bgr ? 2 - oc : oc;
+    const float top = (1.f - lx) * (float)r0[x0 * 3 + c] + lx * (float)r0[x1 * 3 + c];
+    const float bot = (1.f - lx) * (float)r1[x0 * 3 + c] + lx * (float)r1[x1 * 3 + c];
+    const float v = (1.f - ly) * top + ly * bot;
+    out[(((size_t)b * 3 + oc) * dh + y) * dw + x] = (v * (1.f / 255.f) - kMean[oc]) * kInvStd[oc];
+  }
+}
+
 __global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ x, size_t n, bf16_t* __restrict__ y) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) y[i] = f2bf(x[i]);
@@ -156,6 +206,15 @@ hipError_t launch_pos_resample(const float* pos_in, int gh, int gw, float* pos_o
 hipError_t launch_crops(const float* img, int H, int W, const int* corners_dev, int nwin, int side, float* out,
                         hipStream_t s) {
   hipLaunchKernelGGL(crops_kernel, dim3(64, 3, nwin), dim3(256), 0, s, img, H, W, corners_dev, side, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_preprocess(const uint8_t* frames, int batch, int sh, int sw, bool bgr, float* out, int dh, int dw,
+                             hipStream_t s) {
+  if (batch < 1 || sh < 1 || sw < 1 || dh < 1 || dw < 1 || batch > 65535 || dh > 65535)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(preprocess_kernel, dim3((unsigned)((dw + 255) / 256), dh, batch), dim3(256), 0, s, frames, sh, sw,
+                     out, dh, dw, bgr);
   return hipGetLastError();
 }
 

@@ -63,6 +63,11 @@ hipError_t launch_ln_l2(const float* x, int batch, int tokens, int first_patch, 
 hipError_t launch_descriptor(const float* x, int batch, size_t row_stride, int dim, float* desc,
                              hipStream_t s);
 
+// 8-bit HWC frames [batch, sh, sw, 3] -> ImageNet-normalised fp32 CHW
+// [batch, 3, dh, dw] (bilinear, half-pixel centres; bgr: channel order B, G, R).
+hipError_t launch_preprocess(const uint8_t* frames, int batch, int sh, int sw, bool bgr, float* out, int dh, int dw,
+                             hipStream_t s);
+
 // im2col of fp32 images [batch, 3, H, W] into bf16 [batch * gh * gw, kpad]
 // with columns in (c, ky, kx) order, zero beyond 3 p^2.
 hipError_t launch_patchify(const float* img, int batch, int H, int W, int p, int kpad, uint16_t* out,

@@ -601,6 +601,19 @@ int vit_destroy(vit_model* m) {
 
 // ------------------------------------------------------------------ per-op entry points
 
+int vit_op_preprocess(const void* frames, int batch, int src_h, int src_w, int bgr, float* images, int dst_h,
+                      int dst_w, void* stream) {
+  if (!frames || !images) return fail(VIT_ERR_ARG, "NULL pointer");
+  if (batch < 1 || src_h < 1 || src_w < 1 || dst_h < 1 || dst_w < 1 || batch > 65535 || dst_h > 65535)
+    return fail(VIT_ERR_SHAPE, "sizes must be >= 1, batch and dst_h <= 65535");
+  if ((size_t)src_h * src_w * 3 >= (1ull << 31) || (size_t)dst_h * dst_w >= (1ull << 31))
+    return fail(VIT_ERR_SHAPE, "frame or image too large");
+  VIT_HIP(vit::launch_preprocess((const uint8_t*)frames, batch, src_h, src_w, bgr != 0, images, dst_h, dst_w,
+                                 (hipStream_t)stream),
+          "preprocess");
+  return VIT_OK;
+}
+
 int vit_op_layernorm(const float* x, int rows, int dim, const float* g, const float* b, float eps, void* y,
                      int out_fp32, void* stream) {
   if (!x || !g || !b || !y) return fail(VIT_ERR_ARG, "NULL pointer");
