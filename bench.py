@@ -149,19 +149,24 @@ def kernel_breakdown(cfg, batch, steps=20, warmup=5):
     f = torch.empty((M, Hm), dtype=bf, device="cuda")
     vit.vit_op_qkv(h, wqkv, bqkv, batch, N, H, q, k, vt)
     attn_work = torch.empty(max(vit.vit_op_attention_workspace(batch, N, H), 4), dtype=torch.uint8, device="cuda")
+    # D = 384: the residual GEMMs also apply the LayerNorm after them (as the
+    # forward does), leaving the first block's LN1 and the final norm standalone
+    fused = D == 384
     ops = {
-        "layernorm": (lambda: vit.vit_op_layernorm(x, M, D, gam, bet, 1e-6, h, 0), 2 * L, 0.0,
+        "layernorm": (lambda: vit.vit_op_layernorm(x, M, D, gam, bet, 1e-6, h, 0), 2 if fused else 2 * L, 0.0,
                       M * D * (4 + 2) + 8 * D, "hbm"),
         "qkv": (lambda: vit.vit_op_qkv(h, wqkv, bqkv, batch, N, H, q, k, vt), L, 2.0 * M * D * 3 * D,
                 M * D * 2 + 3 * D * D * 2 + 3 * M * D * 2, "mfma"),
         "attention": (lambda: vit.vit_op_attention(q, k, vt, batch, N, H, o, attn_work), L, 4.0 * batch * N * N * D,
                       4 * M * D * 2, "mfma"),
-        "out_proj": (lambda: vit.vit_op_linear(o, wo, bo, M, D, D, vit.EPI_RESIDUAL, ls, x), L,
-                     2.0 * M * D * D, M * D * 2 + D * D * 2 + 2 * M * D * 4, "mfma"),
+        "out_proj": ((lambda: vit.vit_op_linear_residual_ln(o, wo, bo, ls, M, D, D, x, gam, bet, 1e-6, h)) if fused
+                     else (lambda: vit.vit_op_linear(o, wo, bo, M, D, D, vit.EPI_RESIDUAL, ls, x)), L,
+                     2.0 * M * D * D, M * D * 2 + D * D * 2 + 2 * M * D * 4 + (M * D * 2 if fused else 0), "mfma"),
         "fc1": (lambda: vit.vit_op_linear(h, w1, b1, M, Hm, D, vit.EPI_GELU_BF16, None, f), L,
                 2.0 * M * D * Hm, M * D * 2 + Hm * D * 2 + M * Hm * 2, "mfma"),
-        "fc2": (lambda: vit.vit_op_linear(f, w2, b2, M, D, Hm, vit.EPI_RESIDUAL, ls, x), L,
-                2.0 * M * Hm * D, M * Hm * 2 + D * Hm * 2 + 2 * M * D * 4, "mfma"),
+        "fc2": ((lambda: vit.vit_op_linear_residual_ln(f, w2, b2, ls, M, D, Hm, x, gam, bet, 1e-6, h)) if fused
+                else (lambda: vit.vit_op_linear(f, w2, b2, M, D, Hm, vit.EPI_RESIDUAL, ls, x)), L,
+                2.0 * M * Hm * D, M * Hm * 2 + D * Hm * 2 + 2 * M * D * 4 + (M * D * 2 if fused else 0), "mfma"),
     }
     out = {}
     for name, (fn, per_step, flops, nbytes, bound) in ops.items():
@@ -298,10 +303,10 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib=256):
 KERNEL_NAMES = {
     "qkv": "gemm_bf16_kernel<EpiQKV>",
     "attention": "attention_kernel",
-    "out_proj": "gemm_bf16_kernel<EpiResidual> (out-proj)",
+    "out_proj": "gemm_bf16_kernel<EpiResidualLN> (out-proj + LN2)",
     "fc1": "gemm_bf16_kernel<EpiGeluBf16>",
-    "fc2": "gemm_bf16_kernel<EpiResidual> (fc2)",
-    "layernorm": "layernorm_kernel<6,false>",
+    "fc2": "gemm_bf16_kernel<EpiResidualLN> (fc2 + next LN1)",
+    "layernorm": "layernorm_kernel<3,32,false>",
 }
 
 

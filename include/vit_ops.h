@@ -57,6 +57,19 @@ enum vit_epilogue {
 int vit_op_linear(const void* a, const void* w, const float* bias, int M, int N, int K,
                   int epilogue, const float* ls, void* c, void* stream);
 
+/* Residual update and the LayerNorm after it, in one GEMM whose tiles span
+ * whole rows (LibreYOLO DINOv2 diagram, "Encoder block": the output Linear
+ * (or the second MLP Linear), LayerScale, residual add, then the next block
+ * step's LayerNorm, eps inside the square root):
+ *   x[m, :] += ls * (a[m, :] w^T + bias);   h[m, :] = LayerNorm(x[m, :]; g, b, eps)
+ *   a [M, K] bf16, w [N, K] bf16, bias, ls, g, b [N] fp32, x [M, N] fp32
+ *   (updated in place), h [M, N] bf16.  N must be 384 (VIT_ERR_UNSUPPORTED
+ *   otherwise), K a positive multiple of 64; float vectors and x 16-byte
+ *   aligned, h 8-byte aligned.  x and h equal, bit for bit, vit_op_linear
+ *   with VIT_EPI_RESIDUAL followed by vit_op_layernorm. */
+int vit_op_linear_residual_ln(const void* a, const void* w, const float* bias, const float* ls, int M, int N, int K,
+                              float* x, const float* g, const float* b, float eps, void* h, void* stream);
+
 /* Fused Q/K/V projection with the head split of the attention kernel
  * (LibreYOLO diagram, "Encoder self-attention": Linear Q/K/V, reshape heads).
  *   h [batch*tokens, D] bf16 (LayerNorm output), wqkv [3D, D] bf16 (rows: the

@@ -106,6 +106,37 @@ def test_gelu_epilogue_wide_range():
     assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6), np.abs(got - ref).max()
 
 
+@pytest.mark.parametrize("M,K", [(1, 64), (130, 384), (446, 1536), (14272, 384)])
+def test_linear_residual_ln(M, K):
+    """Residual update + the LayerNorm after it in one kernel: against the
+    oracle, and bit for bit against the two separate entry points."""
+    say(f"linear + residual + layernorm M={M} K={K}")
+    N = 384
+    a_d, a = bf16_dev(RNG.standard_normal((M, K)) * 0.7)
+    w_d, w = bf16_dev(RNG.standard_normal((N, K)) * 0.05)
+    bias = (0.1 * RNG.standard_normal(N)).astype(np.float32)
+    ls = (0.5 + RNG.standard_normal(N)).astype(np.float32)
+    g = (1.0 + 0.1 * RNG.standard_normal(N)).astype(np.float32)
+    b = (0.1 * RNG.standard_normal(N)).astype(np.float32)
+    r0 = RNG.standard_normal((M, N)).astype(np.float32)
+    x = f32_dev(r0)
+    h = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    vit.vit_op_linear_residual_ln(a_d, w_d, f32_dev(bias), f32_dev(ls), M, N, K, x, f32_dev(g), f32_dev(b), 1e-6, h)
+    z = O.linear(a, w, bias)
+    ref_x = r0 + ls * z
+    tol_x = np.abs(ls) * K * U24 * (np.abs(a) @ np.abs(w).T) + 4 * U24 * (np.abs(r0) + np.abs(ls * z)) + 1e-7
+    gx = host(x)
+    assert np.all(np.abs(gx - ref_x) <= tol_x), np.abs(gx - ref_x).max()
+    ref_h = O.layer_norm(gx.astype(np.float64), g, b, 1e-6)
+    assert np.all(np.abs(host(h) - ref_h) <= 2.0 ** -8 * np.abs(ref_h) + 2e-5 * (1 + np.abs(ref_h)))
+    # the unfused pair on the same inputs
+    x2 = f32_dev(r0)
+    h2 = torch.empty_like(h)
+    vit.vit_op_linear(a_d, w_d, f32_dev(bias), M, N, K, vit.EPI_RESIDUAL, f32_dev(ls), x2)
+    vit.vit_op_layernorm(x2, M, N, f32_dev(g), f32_dev(b), 1e-6, h2, 0)
+    assert torch.equal(x, x2) and torch.equal(h.view(torch.int16), h2.view(torch.int16))
+
+
 # ------------------------------------------------------------------ QKV head split
 
 @pytest.mark.parametrize("batch,tokens,heads", [(1, 5, 1), (2, 201, 6), (1, 446, 6), (3, 70, 2)])

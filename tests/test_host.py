@@ -127,6 +127,10 @@ def test_create_and_calls_validate_before_touching_the_device(L):
     assert vit.vit_op_attention_workspace(1, 446, 6) == 0            # short sequences are never split
     assert vit.vit_op_attention_workspace(2, 1370, 6) == 2 * 6 * 11 * 90 * 66 * 4   # 11 ranges of 128 keys
     assert vit.vit_op_attention_workspace(1, 4101, 16) == 16 * 13 * 5 * 66 * 4      # 13 ranges of 320 keys
+    f = ctypes.c_float(1e-6)
+    assert lib.vit_op_linear_residual_ln(fake, fake, fake, fake, 4, 384, 64, fake, fake, fake, f, None, None) == -1
+    assert lib.vit_op_linear_residual_ln(fake, fake, fake, fake, 4, 384, 60, fake, fake, fake, f, fake, None) == -2
+    assert lib.vit_op_linear_residual_ln(fake, fake, fake, fake, 4, 512, 64, fake, fake, fake, f, fake, None) == -5
     assert lib.vit_op_preprocess(None, 1, 8, 8, 0, fake, 4, 4, None) == -1
     assert lib.vit_op_preprocess(fake, 1, 8, 8, 0, None, 4, 4, None) == -1
     assert lib.vit_op_preprocess(fake, 0, 8, 8, 0, fake, 4, 4, None) == -2

@@ -22,7 +22,7 @@ __all__ = [
     "LibraryMissing", "VitError", "VitConfig", "VitSizes", "lib", "config_from_dict", "pack_params",
     "vit_config_preset", "vit_plan", "vit_create", "vit_forward", "vit_descriptor", "vit_patch_scores",
     "vit_destroy", "vit_last_error", "vit_op_layernorm", "vit_op_linear", "vit_op_qkv", "vit_op_attention",
-    "vit_op_attention_workspace", "vit_op_preprocess",
+    "vit_op_attention_workspace", "vit_op_preprocess", "vit_op_linear_residual_ln",
     "Encoder", "EncoderGraph", "EPI_BIAS_BF16", "EPI_GELU_BF16", "EPI_RESIDUAL", "EPI_BIAS_F32",
 ]
 
@@ -84,6 +84,7 @@ _SIGNATURES = {
     "vit_op_attention": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, ctypes.c_size_t, _P]),
     "vit_op_attention_workspace": (ctypes.c_size_t, [_I, _I, _I]),
     "vit_op_preprocess": (_I, [_P, _I, _I, _I, _I, _P, _I, _I, _P]),
+    "vit_op_linear_residual_ln": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P, _P, ctypes.c_float, _P, _P]),
 }
 
 
@@ -169,6 +170,12 @@ def vit_patch_scores(handle, d_image, d_class_emb, classes, mode, d_labels, d_co
 
 def vit_destroy(handle):
     return _check("vit_destroy", lib().vit_destroy(handle))
+
+
+def vit_op_linear_residual_ln(a, w, bias, ls, M, N, K, x, g, b, eps, h, stream=None):
+    return _check("vit_op_linear_residual_ln",
+                  lib().vit_op_linear_residual_ln(_ptr(a), _ptr(w), _ptr(bias), _ptr(ls), M, N, K, _ptr(x), _ptr(g),
+                                                  _ptr(b), eps, _ptr(h), _stream(stream)))
 
 
 def vit_op_preprocess(frames, batch, src_h, src_w, bgr, images, dst_h, dst_w, stream=None):

@@ -110,4 +110,36 @@ __device__ __forceinline__ float half_swap_max(float v) {
   return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 
+// Sum over the LPR lanes of a lane group (LPR a power of two <= 64).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// LayerNorm (two-pass mean and biased variance, eps inside the square root,
+// then the affine g, b) of one row of `dim` values held by a group of LPR
+// lanes as V4 float4 groups each, in place; gg, bb are this lane's groups of
+// g and b.  Every lane of the wave must call it (the group sums shuffle).
+template <int V4, int LPR>
+__device__ __forceinline__ void ln_group_normalize(float4 (&v)[V4], const float4 (&gg)[V4], const float4 (&bb)[V4],
+                                                   float eps, int dim) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < V4; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  const float mean = group_sum<LPR>(s) / (float)dim;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    v[i].x -= mean, v[i].y -= mean, v[i].z -= mean, v[i].w -= mean;
+    q += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
+  }
+  const float rstd = rsqrtf(group_sum<LPR>(q) / (float)dim + eps);
+#pragma unroll
+  for (int i = 0; i < V4; ++i)
+    v[i] = make_float4(v[i].x * rstd * gg[i].x + bb[i].x, v[i].y * rstd * gg[i].y + bb[i].y,
+                       v[i].z * rstd * gg[i].z + bb[i].z, v[i].w * rstd * gg[i].w + bb[i].w);
+}
+
 }  // namespace vit

@@ -283,9 +283,28 @@ struct HasPrologue : std::false_type {};
 template <class E>
 struct HasPrologue<E, std::void_t<decltype(&E::prologue)>> : std::true_type {};
 template <class E, class = void>
+struct HasRowLN : std::false_type {};
+template <class E>
+struct HasRowLN<E, std::void_t<decltype(E::kD)>> : std::true_type {};
+template <class E, class = void>
 struct HasTransposed : std::false_type {};
 template <class E>
 struct HasTransposed<E, std::void_t<decltype(&E::tile_transposed)>> : std::true_type {};
+
+// Residual update followed by the next LayerNorm, for a tile that spans whole
+// rows (N = kD): out[m, :] += ls * (acc + bias), then h[m, :] = LN(out[m, :])
+// in bf16.  The arithmetic of both steps is that of EpiResidual and of the
+// standalone LayerNorm kernel, so x and h are bit-identical to the unfused pair.
+struct EpiResidualLN {
+  static constexpr int kD = 384;
+  const float* bias;
+  const float* ls;
+  float* out;  // residual x [M, kD] fp32
+  const float* g;
+  const float* b;
+  float eps;
+  bf16_t* h;   // [M, kD] bf16
+};
 
 // Patch rows of the embedding GEMM: row m = b * patches + i goes to residual
 // row b * tokens + 1 + regs + i with its position embedding pos[1 + i] added.
@@ -480,6 +499,71 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   __syncthreads();
 
   // accumulator element e of block (i, j): row 8*(e/4) + 4*lhalf + e%4, column lrow
+  if constexpr (HasRowLN<Epi>::value) {
+    // Whole rows: stage acc + bias of the 64 x kD tile (rows 0..31 in stage 0,
+    // 32..63 in stage 1; row stride kD + 4 floats), then every wave finishes 8
+    // rows, two at a time (32 lanes x 3 float4 per row, the lane groups of the
+    // standalone LayerNorm).  All reads come before the first store.
+    constexpr int D = Epi::kD;
+    static_assert(BN == D && BM == 64 && WGM == 2 && TM == 1 && NW == 8, "row tile shape");
+    constexpr int LDR = D + 4;
+    static_assert(32 * LDR * 4 <= STAGE_BYTES, "half a tile per stage");
+    constexpr int LPR = 32, V4 = D / (4 * LPR), PASSES = BM / (NW * 2);
+    float* half0 = reinterpret_cast<float*>(stage_lds<STAGE_BYTES, 0>());
+    float* half1 = reinterpret_cast<float*>(stage_lds<STAGE_BYTES, 1>());
+    {
+      float* mine = wm == 0 ? half0 : half1;
+      float bcol[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bcol[j] = epi.bias[wn * WTN + j * 32 + lrow];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          mine[((e >> 2) * 8 + lhalf * 4 + (e & 3)) * LDR + wn * WTN + j * 32 + lrow] = acc[0][j][e] + bcol[j];
+    }
+    __syncthreads();
+    const int sl = lane & 31;
+    float4 sv[V4], gv[V4], bv[V4];
+#pragma unroll
+    for (int i = 0; i < V4; ++i) {
+      sv[i] = reinterpret_cast<const float4*>(epi.ls)[sl + LPR * i];
+      gv[i] = reinterpret_cast<const float4*>(epi.g)[sl + LPR * i];
+      bv[i] = reinterpret_cast<const float4*>(epi.b)[sl + LPR * i];
+    }
+    float4 v[PASSES][V4], xo[PASSES][V4];
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int r = wave * (2 * PASSES) + pass * 2 + (lane >> 5);
+      const int mc = min(m0 + r, M - 1);
+      const float* src = (r < 32 ? half0 : half1) + (r & 31) * LDR;
+#pragma unroll
+      for (int i = 0; i < V4; ++i) {
+        v[pass][i] = *reinterpret_cast<const float4*>(src + 4 * (sl + LPR * i));
+        xo[pass][i] = reinterpret_cast<const float4*>(epi.out + (size_t)mc * D)[sl + LPR * i];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int m = m0 + wave * (2 * PASSES) + pass * 2 + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < V4; ++i) {
+        float4& t = v[pass][i];
+        t = make_float4(xo[pass][i].x + sv[i].x * t.x, xo[pass][i].y + sv[i].y * t.y,
+                        xo[pass][i].z + sv[i].z * t.z, xo[pass][i].w + sv[i].w * t.w);
+        if (m < M) reinterpret_cast<float4*>(epi.out + (size_t)m * D)[sl + LPR * i] = t;
+      }
+      ln_group_normalize<V4, LPR>(v[pass], gv, bv, epi.eps, D);
+      if (m < M) {
+#pragma unroll
+        for (int i = 0; i < V4; ++i)
+          reinterpret_cast<uint2*>(epi.h + (size_t)m * D)[sl + LPR * i] =
+              make_uint2(pack_bf16x2(v[pass][i].x, v[pass][i].y), pack_bf16x2(v[pass][i].z, v[pass][i].w));
+      }
+    }
+    return;
+  }
   if constexpr (HasTransposed<Epi>::value) {
     if (epi.tile_transposed(n0)) {
       // Stage 32 rows (tokens) x WTN columns (channels) with the bias added,
@@ -518,7 +602,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
       return;
     }
   }
-  {
+  if constexpr (!HasRowLN<Epi>::value) {
     // Each wave stages one 32-row block of its tile at a time (row stride WTN + 8
     // floats: the two lane halves land on disjoint banks), then every lane
     // handles 4 consecutive columns of PASSES rows.  The staging areas live in
@@ -643,6 +727,8 @@ hipError_t dispatch_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, c
   return run<CfgMid>(A, W, M, N, K, epi, s);
 }
 
+using CfgRowLN = Cfg<64, EpiResidualLN::kD, 64, 2, 4, 2>;
+
 }  // namespace
 
 hipError_t prepare_gemm() { return phi_table_device() ? hipSuccess : hipErrorInvalidValue; }
@@ -682,6 +768,15 @@ hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, int M, int N, int K
       e.vt = ep.vt;
       e.nv = ep.nv;
       return dispatch_qkv(A, W, M, N, K, e, s);
+    }
+    case EPI_RESIDUAL_LN: {
+      if (N != EpiResidualLN::kD || ep.ldc != N) return hipErrorInvalidValue;
+      auto al16 = [&](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+      if (!al16(ep.bias) || !al16(ep.ls) || !al16(ep.out) || !al16(ep.ln_g) || !al16(ep.ln_b) || !ep.h ||
+          reinterpret_cast<uintptr_t>(ep.h) % 8 != 0)
+        return hipErrorInvalidValue;
+      EpiResidualLN e{ep.bias, ep.ls, (float*)ep.out, ep.ln_g, ep.ln_b, ep.eps, (bf16_t*)ep.h};
+      return run<CfgRowLN>(A, W, M, N, K, e, s);
     }
     case EPI_PATCH: {
       const bool vec = par16 && al(ep.pos, 16) && al(ep.out, 16);

@@ -15,6 +15,7 @@ enum EpiKind {
   EPI_BIAS_F32 = 3,    // out_f32[m,n] = acc + bias[n]
   EPI_QKV = 4,         // head split into q (scaled), k, vt (transposed, permuted)
   EPI_PATCH = 5,       // residual row of patch token: acc + bias[n] + pos[1 + i][n]
+  EPI_RESIDUAL_LN = 6, // EPI_RESIDUAL, then h = LayerNorm(out row) in bf16 (N = 384 only)
 };
 
 struct EpiParams {
@@ -34,7 +35,15 @@ struct EpiParams {
   const float* pos = nullptr;
   int patches = 0;
   int regs = 0;
+  // EPI_RESIDUAL_LN
+  const float* ln_g = nullptr;
+  const float* ln_b = nullptr;
+  float eps = 0.f;
+  uint16_t* h = nullptr;
 };
+
+// Widths for which launch_gemm fuses the LayerNorm after a residual update.
+constexpr bool residual_ln_fusable(int n) { return n == 384; }
 
 // One-time per-device set-up of the GEMM epilogues (the GELU Phi table; a
 // synchronous copy).  launch_gemm does it on first use; encoders call it at

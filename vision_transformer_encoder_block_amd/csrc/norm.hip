@@ -13,44 +13,23 @@ namespace {
 
 constexpr int MAXV = 64;  // columns per lane: dim <= 4096
 
-// Sum over the LPR lanes of a lane group (LPR a power of two <= 64).
-template <int LPR>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // LayerNorm of one row held by a group of LPR lanes as V4 float4 groups each
 // (lane sl of the group holds columns 4 (sl + LPR i) .. + 3).  Every lane of
-// the wave must call it (the group sums shuffle); all LayerNorms of the
-// library go through it, so they agree bit for bit on the same row.
+// the wave must call it (the group sums shuffle).  All LayerNorms of the
+// library, including the one fused into the residual GEMM epilogue, go
+// through ln_group_normalize, so they agree bit for bit on the same row.
 template <int V4, int LPR>
 __device__ __forceinline__ void ln_vec(const float* __restrict__ xrow, const float* __restrict__ g,
                                        const float* __restrict__ b, float eps, int dim, int sl, float4 (&v)[V4]) {
   const float4* xr = reinterpret_cast<const float4*>(xrow);
-  float s = 0.f;
+  float4 gg[V4], bb[V4];
 #pragma unroll
   for (int i = 0; i < V4; ++i) {
     v[i] = xr[sl + LPR * i];
-    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    gg[i] = reinterpret_cast<const float4*>(g)[sl + LPR * i];
+    bb[i] = reinterpret_cast<const float4*>(b)[sl + LPR * i];
   }
-  const float mean = group_sum<LPR>(s) / (float)dim;
-  float q = 0.f;
-#pragma unroll
-  for (int i = 0; i < V4; ++i) {
-    v[i].x -= mean, v[i].y -= mean, v[i].z -= mean, v[i].w -= mean;
-    q += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
-  }
-  const float rstd = rsqrtf(group_sum<LPR>(q) / (float)dim + eps);
-#pragma unroll
-  for (int i = 0; i < V4; ++i) {
-    const int c4 = sl + LPR * i;
-    const float4 gg = reinterpret_cast<const float4*>(g)[c4];
-    const float4 bb = reinterpret_cast<const float4*>(b)[c4];
-    v[i] = make_float4(v[i].x * rstd * gg.x + bb.x, v[i].y * rstd * gg.y + bb.y, v[i].z * rstd * gg.z + bb.z,
-                       v[i].w * rstd * gg.w + bb.w);
-  }
+  ln_group_normalize<V4, LPR>(v, gg, bb, eps, dim);
 }
 
 // Lane group shape for dim = 64 V: the widest group that divides the row into float4s.

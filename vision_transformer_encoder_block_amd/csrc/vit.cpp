@@ -304,9 +304,13 @@ int run_encoder(vit_model* m, const Geom& g, const float* images, int batch, flo
   VIT_HIP(vit::launch_gemm(m->cols, m->patch_w, batch * g.P, D, pl.kpad, pe, st), "patch embedding");
   VIT_HIP(vit::launch_assemble(m->x, batch, N, D, m->cls, g.pos, m->reg, pl.R, st), "token assembly");
   int tap_i = 0;
+  // For D = 384 the residual GEMMs also apply the LayerNorm that follows them
+  // (out projection -> LN2, fc2 -> LN1 of the next block), so h arrives ready.
+  const bool fuse_ln = vit::residual_ln_fusable(D);
   for (int l = 0; l < pl.L; ++l) {
     const BlockW& w = m->blocks[l];
-    VIT_HIP(vit::launch_layernorm(m->x, M, D, w.ln1_g, w.ln1_b, eps, m->h, false, st), "ln1");
+    if (!fuse_ln || l == 0)
+      VIT_HIP(vit::launch_layernorm(m->x, M, D, w.ln1_g, w.ln1_b, eps, m->h, false, st), "ln1");
     vit::EpiParams eq;
     eq.kind = vit::EPI_QKV;
     eq.bias = w.bqkv;
@@ -320,13 +324,17 @@ int run_encoder(vit_model* m, const Geom& g, const float* images, int batch, flo
     VIT_HIP(vit::launch_attention(m->q, m->k, m->vt, batch, N, pl.heads, g.nv, m->o, m->attn, pl.ws.attn_bytes, st),
             "attention");
     vit::EpiParams eo;
-    eo.kind = vit::EPI_RESIDUAL;
+    eo.kind = fuse_ln ? vit::EPI_RESIDUAL_LN : vit::EPI_RESIDUAL;
     eo.bias = w.bo;
     eo.ls = w.ls1;
     eo.out = m->x;
     eo.ldc = D;
+    eo.ln_g = w.ln2_g;
+    eo.ln_b = w.ln2_b;
+    eo.eps = eps;
+    eo.h = m->h;
     VIT_HIP(vit::launch_gemm(m->o, w.wo, M, D, D, eo, st), "out projection");
-    VIT_HIP(vit::launch_layernorm(m->x, M, D, w.ln2_g, w.ln2_b, eps, m->h, false, st), "ln2");
+    if (!fuse_ln) VIT_HIP(vit::launch_layernorm(m->x, M, D, w.ln2_g, w.ln2_b, eps, m->h, false, st), "ln2");
     vit::EpiParams e1;
     e1.kind = vit::EPI_GELU_BF16;
     e1.bias = w.b1;
@@ -334,11 +342,18 @@ int run_encoder(vit_model* m, const Geom& g, const float* images, int batch, flo
     e1.ldc = Hm;
     VIT_HIP(vit::launch_gemm(m->h, w.w1, M, Hm, D, e1, st), "fc1");
     vit::EpiParams e2;
-    e2.kind = vit::EPI_RESIDUAL;
+    const bool fuse_next = fuse_ln && l + 1 < pl.L;
+    e2.kind = fuse_next ? vit::EPI_RESIDUAL_LN : vit::EPI_RESIDUAL;
     e2.bias = w.b2;
     e2.ls = w.ls2;
     e2.out = m->x;
     e2.ldc = D;
+    if (fuse_next) {
+      e2.ln_g = m->blocks[l + 1].ln1_g;
+      e2.ln_b = m->blocks[l + 1].ln1_b;
+      e2.eps = eps;
+      e2.h = m->h;
+    }
     VIT_HIP(vit::launch_gemm(m->f, w.w2, M, D, Hm, e2, st), "fc2");
     if (taps && l < 32 && ((pl.cfg.tap_mask >> l) & 1u)) {
       const size_t per_img = (size_t)pl.ntaps * D * g.P;
@@ -600,6 +615,29 @@ int vit_destroy(vit_model* m) {
 }
 
 // ------------------------------------------------------------------ per-op entry points
+
+int vit_op_linear_residual_ln(const void* a, const void* w, const float* bias, const float* ls, int M, int N, int K,
+                              float* x, const float* g, const float* b, float eps, void* h, void* stream) {
+  if (!a || !w || !bias || !ls || !x || !g || !b || !h) return fail(VIT_ERR_ARG, "NULL pointer");
+  if (M < 1 || K < 64 || K % 64) return fail(VIT_ERR_SHAPE, "M >= 1 and K a positive multiple of 64");
+  if (!vit::residual_ln_fusable(N)) return fail(VIT_ERR_UNSUPPORTED, "the fused residual + LayerNorm needs N = 384");
+  if (!(eps > 0.f)) return fail(VIT_ERR_ARG, "eps must be positive");
+  if (((uintptr_t)bias | (uintptr_t)ls | (uintptr_t)x | (uintptr_t)g | (uintptr_t)b) % 16 || (uintptr_t)h % 8)
+    return fail(VIT_ERR_ARG, "vectors and x must be 16-byte aligned, h 8-byte aligned");
+  vit::EpiParams ep;
+  ep.kind = vit::EPI_RESIDUAL_LN;
+  ep.bias = bias;
+  ep.ls = ls;
+  ep.out = x;
+  ep.ldc = N;
+  ep.ln_g = g;
+  ep.ln_b = b;
+  ep.eps = eps;
+  ep.h = (uint16_t*)h;
+  VIT_HIP(vit::launch_gemm((const uint16_t*)a, (const uint16_t*)w, M, N, K, ep, (hipStream_t)stream),
+          "linear + residual + layernorm");
+  return VIT_OK;
+}
 
 int vit_op_preprocess(const void* frames, int batch, int src_h, int src_w, int bgr, float* images, int dst_h,
                       int dst_w, void* stream) {
