@@ -255,6 +255,8 @@ PMC_OPS = {
     "fc1": ("EpiGeluBf16", None),
     "attention": ("attention_kernel", None),
     "layernorm": ("layernorm_kernel", None),
+    "qkv": ("EpiQKV", None),
+    "residual_ln": ("EpiResidualLN", None),
 }
 
 
