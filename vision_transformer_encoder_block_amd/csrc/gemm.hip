@@ -104,9 +104,13 @@ __device__ __forceinline__ void store4_f32(float* p, const float (&v)[4], int nv
 // interpolation error is at most h^2/8 * max|Phi''| = 7.4e-6 (h = 1/64,
 // max|Phi''| = phi(1)), and outside [-6, 6] Phi is 0 or 1 to within 1e-9.
 // Entry i holds (Phi(x_i), Phi(x_{i+1}) - Phi(x_i)); the table is built on
-// the host from erfc in double precision and copied once per device.
+// the host from erfc in double precision and copied once per device.  It is
+// stored padded with zero entries to whole 1 KB blocks, the unit in which the
+// GEMM copies it into LDS.
 constexpr int kPhiPoints = 769;
-__device__ float2 g_phi_table[kPhiPoints];
+constexpr int kPhiBlocks = (kPhiPoints * 8 + 1023) / 1024;  // 7
+constexpr int kPhiPadded = kPhiBlocks * 128;                 // 896 entries
+__device__ float2 g_phi_table[kPhiPadded];
 
 __device__ __forceinline__ float gelu_table(float x, const float2* tab) {
   // t in [0, 768]; NaN converts to index 0 and propagates through f
@@ -153,13 +157,19 @@ struct EpiGeluBf16 {
   using Col = float4;
   using Row = NoRow;
   __device__ static float2* lds_phi() {
-    __shared__ float2 t[kPhiPoints];
+    __shared__ float2 t[kPhiPadded];
     return t;
   }
-  // copies the table to LDS at kernel start (published by the main loop's barriers)
-  __device__ void prologue(int tid, int nthreads) const {
-    float2* t = lds_phi();
-    for (int i = tid; i < kPhiPoints; i += nthreads) t[i] = phi[i];
+  // Starts the copy of the table into LDS at kernel start with direct-to-LDS
+  // loads (one 1 KB block per wave instruction).  Called before the operand
+  // loads of the first stages: loads complete in issue order, so the wait for
+  // stage 0 covers the table too and the barrier that publishes stage 0
+  // publishes it, with no load latency of its own before the pipeline starts.
+  __device__ void prologue(int wave, int lane, int nwaves) const {
+    const int32x4 r = make_rsrc_words(phi, (uint32_t)(kPhiPadded * 8));
+    const uint32_t base = lds_addr(lds_phi());
+    for (int j = wave; j < kPhiBlocks; j += nwaves)
+      dma16(r, (uint32_t)(j * 1024 + lane * 16), base + (uint32_t)(j * 1024));
   }
   __device__ Col col4(int n, int nvalid) const { return load4(bias + n, nvalid, vec); }
   __device__ Row pre(int, int, int) const { return {}; }
@@ -397,11 +407,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  if constexpr (HasPrologue<Epi>::value) epi.prologue(tid, 64 * NW);
-
   const int32x4 ra_src = make_rsrc_words(A, (uint32_t)((size_t)M * K * 2));
   const int32x4 rb_src = make_rsrc_words(W, (uint32_t)((size_t)N * K * 2));
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  if constexpr (HasPrologue<Epi>::value) epi.prologue(wave_u, lane, NW);
   // byte offset (at k = 0) of the chunk this lane fetches in each DMA instruction
   uint32_t a_off[A_IT], b_off[B_IT];
   {
@@ -703,7 +712,7 @@ const float2* phi_table_device() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
   std::lock_guard<std::mutex> lock(mu);
   if (!addr[dev]) {
-    float2 host[kPhiPoints];
+    float2 host[kPhiPadded] = {};
     double prev = 0.5 * std::erfc(6.0 / std::sqrt(2.0));  // Phi(-6)
     for (int i = 0; i < kPhiPoints; ++i) {
       const double x1 = -6.0 + (i + 1) / 64.0;
