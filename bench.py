@@ -198,6 +198,8 @@ def _source_digest():
     for fn in sorted(os.listdir(csrc)):
         if fn.endswith((".hip", ".h")):
             h.update(open(os.path.join(csrc, fn), "rb").read())
+    # compile flags change the kernels too
+    h.update(open(os.path.join(ROOT, "vision_transformer_encoder_block_amd", "build.py"), "rb").read())
     return h.hexdigest()[:16]
 
 

@@ -35,6 +35,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source flags.  The attention kernel runs with the IEEE mode bit off:
+# its row maxima come straight from MFMA accumulators, and in IEEE mode every
+# fmax input is first quieted (one extra instruction per logit).  Clang allows
+# that mode only with relaxed NaN handling for the file; a NaN logit still
+# reaches the output through exp2 and the products.
+EXTRA_FLAGS = {"attention.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -45,7 +53,7 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc(), *lang, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *lang, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -239,12 +239,16 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
           if (key >= N) s[kb][e] = -INFINITY;
         }
     }
-    // tile max of this lane's 32 logits as a tree (short dependency chain)
-    float mx[8];
+    // tile max of this lane's 32 logits: maxima of groups of three
+    // (v_max3_f32), then of the group maxima (17 instructions, depth 4)
+    auto sv = [&](int f) { return s[f >> 4][f & 15]; };
+    float g3[11];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mx[i] = fmaxf(fmaxf(s[i >> 2][(i & 3) * 4], s[i >> 2][(i & 3) * 4 + 1]),
-                                          fmaxf(s[i >> 2][(i & 3) * 4 + 2], s[i >> 2][(i & 3) * 4 + 3]));
-    float mt = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])), fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
+    for (int i = 0; i < 10; ++i) g3[i] = fmaxf(fmaxf(sv(3 * i), sv(3 * i + 1)), sv(3 * i + 2));
+    g3[10] = fmaxf(sv(30), sv(31));
+    const float u0 = fmaxf(fmaxf(g3[0], g3[1]), g3[2]), u1 = fmaxf(fmaxf(g3[3], g3[4]), g3[5]);
+    const float u2 = fmaxf(fmaxf(g3[6], g3[7]), g3[8]), u3 = fmaxf(g3[9], g3[10]);
+    float mt = fmaxf(fmaxf(fmaxf(u0, u1), u2), u3);
     mt = half_swap_max(mt);
     // Lazy rescaling: the reference max m_run only moves (and O, l are only
     // rescaled) when some query's tile max exceeds it by more than 8, so

@@ -63,12 +63,14 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 // gfx9 data format word); loads at offsets >= `bytes` return zeros.
 typedef int int32x4 __attribute__((ext_vector_type(4)));
 
+// The words must be wave-uniform (the descriptor is an SGPR operand of the
+// inline assembly below); readfirstlane states that to the compiler.
 __device__ __forceinline__ int32x4 make_rsrc_words(const void* p, uint32_t bytes) {
   const uint64_t a = (uint64_t)(uintptr_t)p;
   int32x4 r;
-  r[0] = (int)(uint32_t)a;
-  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
-  r[2] = (int)bytes;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
   r[3] = 0x00020000;
   return r;
 }
