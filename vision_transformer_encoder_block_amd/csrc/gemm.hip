@@ -390,15 +390,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   constexpr int WTM = BM / WGM, WTN = BN / WGN;     // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;       // 32x32 blocks per wave
   constexpr int CPR = BKT / 8;                      // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;                     // rows per DMA instruction
-  constexpr int A_IT = BM / (RPI * NW), B_IT = BN / (RPI * NW);  // DMA instructions per wave per stage
-  constexpr int L = A_IT + B_IT;
+  constexpr int RPI = 64 / CPR;                     // rows per DMA instruction (1 KB)
+  // The DMA instructions of one stage (A rows, then W rows, RPI rows each)
+  // go round-robin to the waves: instruction k is wave k % NW's (k / NW)-th.
+  constexpr int A_INS = BM / RPI, TOT = (BM + BN) / RPI;
+  constexpr int LHI = (TOT + NW - 1) / NW;          // per wave and stage, at most
+  constexpr int L = TOT / NW;                       // ... at least (the waits count these)
+  constexpr bool A_SPLIT = A_INS % NW == 0;         // instruction i of every wave reads the same operand
   constexpr int KS = BKT / 16;                      // MFMA k-steps per stage
   constexpr int STAGE_BYTES = (BM + BN) * BKT * 2;
   static_assert(BKT == 32 || BKT == 64 || BKT == 128, "BK");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-  static_assert(A_IT * RPI * NW == BM && B_IT * RPI * NW == BN, "DMA split");
-  static_assert(S >= 2 && S * L < 64, "pipeline depth");
+  static_assert(A_INS * RPI == BM && TOT * RPI == BM + BN && L >= 1, "DMA split");
+  static_assert(S >= 2 && S * LHI < 64, "pipeline depth");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -411,29 +415,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   const int32x4 rb_src = make_rsrc_words(W, (uint32_t)((size_t)N * K * 2));
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   if constexpr (HasPrologue<Epi>::value) epi.prologue(wave_u, lane, NW);
-  // byte offset (at k = 0) of the chunk this lane fetches in each DMA instruction
-  uint32_t a_off[A_IT], b_off[B_IT];
+  // byte offset (at k = 0) of the chunk this lane fetches in each of its DMA
+  // instructions; instruction k fills LDS bytes [1024 k, 1024 (k + 1)) of the
+  // stage (A's BM rows first, so W's rows start at BM * BKT * 2 = 1024 A_INS)
+  uint32_t g_off[LHI];
   {
     const int sub = lane / CPR, pc = lane % CPR;
 #pragma unroll
-    for (int j = 0; j < A_IT; ++j) {
-      const int row = (j * NW + wave) * RPI + sub;
-      a_off[j] = (uint32_t)(m0 + row) * (uint32_t)K * 2u + (uint32_t)swz_k<BKT>(row, pc) * 16u;
-    }
-#pragma unroll
-    for (int j = 0; j < B_IT; ++j) {
-      const int row = (j * NW + wave) * RPI + sub;
-      b_off[j] = (uint32_t)(n0 + row) * (uint32_t)K * 2u + (uint32_t)swz_k<BKT>(row, pc) * 16u;
+    for (int i = 0; i < LHI; ++i) {
+      const int k = min(i * NW + wave, TOT - 1);
+      const bool is_a = A_SPLIT ? i < A_INS / NW : k < A_INS;
+      const int row = (is_a ? k : k - A_INS) * RPI + sub;
+      g_off[i] = (uint32_t)((is_a ? m0 : n0) + row) * (uint32_t)K * 2u + (uint32_t)swz_k<BKT>(row, pc) * 16u;
     }
   }
   auto issue = [&](auto stage, int kt) {
     const uint32_t blk = lds_addr(stage_lds<STAGE_BYTES, decltype(stage)::value>());
     const uint32_t koff = (uint32_t)kt * (BKT * 2);
 #pragma unroll
-    for (int j = 0; j < A_IT; ++j) dma16(ra_src, a_off[j] + koff, blk + (uint32_t)(j * NW + wave_u) * 1024u);
-#pragma unroll
-    for (int j = 0; j < B_IT; ++j)
-      dma16(rb_src, b_off[j] + koff, blk + (uint32_t)(BM * BKT * 2 + (j * NW + wave_u) * 1024));
+    for (int i = 0; i < LHI; ++i) {
+      const int k = i * NW + wave_u;
+      if (LHI == L || k < TOT) {  // wave-uniform
+        const bool is_a = A_SPLIT ? i < A_INS / NW : k < A_INS;
+        dma16(is_a ? ra_src : rb_src, g_off[i] + koff, blk + (uint32_t)k * 1024u);
+      }
+    }
   };
 
   f32x16 acc[TM][TN];
@@ -469,7 +475,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(af[buf][i], bw[buf][j], acc[i][j]);
   };
   // wait until at most `later` stages of this wave's loads are in flight
-  // (the ones issued after the stage being waited for)
+  // (the ones issued after the stage being waited for); with L the smaller
+  // per-wave count this is exact or stricter than needed
   auto wait_stages = [&](int later) {
     static_for<0, S>([&](auto c) {
       if (later == decltype(c)::value) wait_vm<decltype(c)::value * L>();
@@ -509,19 +516,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
 
   // accumulator element e of block (i, j): row 8*(e/4) + 4*lhalf + e%4, column lrow
   if constexpr (HasRowLN<Epi>::value) {
-    // Whole rows: stage acc + bias of the 64 x kD tile (rows 0..31 in stage 0,
-    // 32..63 in stage 1; row stride kD + 4 floats), then every wave finishes 8
-    // rows, two at a time (32 lanes x 3 float4 per row, the lane groups of the
-    // standalone LayerNorm).  All reads come before the first store.
+    // Whole rows: stage acc + bias of the BM x kD tile (row stride kD + 4
+    // floats; RPS consecutive rows per pipeline stage buffer), then the waves
+    // finish the rows two at a time (32 lanes x 3 float4 per row, the lane
+    // groups of the standalone LayerNorm).  All reads come before the first store.
     constexpr int D = Epi::kD;
-    static_assert(BN == D && BM == 64 && WGM == 2 && TM == 1 && NW == 8, "row tile shape");
+    static_assert(BN == D && BM == 32 * WGM && TM == 1, "row tile shape");
     constexpr int LDR = D + 4;
-    static_assert(32 * LDR * 4 <= STAGE_BYTES, "half a tile per stage");
-    constexpr int LPR = 32, V4 = D / (4 * LPR), PASSES = BM / (NW * 2);
-    float* half0 = reinterpret_cast<float*>(stage_lds<STAGE_BYTES, 0>());
-    float* half1 = reinterpret_cast<float*>(stage_lds<STAGE_BYTES, 1>());
+    constexpr int RPS = 32 * LDR * 4 <= STAGE_BYTES ? 32 : 16;  // staged rows per stage buffer
+    static_assert(RPS * LDR * 4 <= STAGE_BYTES && BM <= RPS * S, "staging must fit in the stage LDS");
+    // row pair p = pass * NW + wave (rows 2p, 2p + 1, one per lane half)
+    constexpr int LPR = 32, V4 = D / (4 * LPR), PAIRS = BM / 2, PASSES = (PAIRS + NW - 1) / NW;
+    float* rows_lds[S];
+    static_for<0, S>([&](auto c) { rows_lds[decltype(c)::value] = reinterpret_cast<float*>(stage_lds<STAGE_BYTES, decltype(c)::value>()); });
+    auto row_ptr = [&](int r) { return rows_lds[r / RPS] + (r % RPS) * LDR; };
     {
-      float* mine = wm == 0 ? half0 : half1;
       float bcol[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) bcol[j] = epi.bias[wn * WTN + j * 32 + lrow];
@@ -529,7 +538,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          mine[((e >> 2) * 8 + lhalf * 4 + (e & 3)) * LDR + wn * WTN + j * 32 + lrow] = acc[0][j][e] + bcol[j];
+          row_ptr(wm * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3))[wn * WTN + j * 32 + lrow] = acc[0][j][e] + bcol[j];
     }
     __syncthreads();
     const int sl = lane & 31;
@@ -543,9 +552,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
     float4 v[PASSES][V4], xo[PASSES][V4];
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
-      const int r = wave * (2 * PASSES) + pass * 2 + (lane >> 5);
+      const int r = min(pass * NW + wave, PAIRS - 1) * 2 + (lane >> 5);
       const int mc = min(m0 + r, M - 1);
-      const float* src = (r < 32 ? half0 : half1) + (r & 31) * LDR;
+      const float* src = row_ptr(r);
 #pragma unroll
       for (int i = 0; i < V4; ++i) {
         v[pass][i] = *reinterpret_cast<const float4*>(src + 4 * (sl + LPR * i));
@@ -555,7 +564,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
-      const int m = m0 + wave * (2 * PASSES) + pass * 2 + (lane >> 5);
+      if (PAIRS % NW != 0 && pass * NW + wave >= PAIRS) break;  // wave-uniform
+      const int m = m0 + (pass * NW + wave) * 2 + (lane >> 5);
 #pragma unroll
       for (int i = 0; i < V4; ++i) {
         float4& t = v[pass][i];
