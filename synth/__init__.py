@@ -43,6 +43,8 @@ __all__ = [
     "make_params",
     "make_images",
     "make_class_embeddings",
+    "make_head_params",
+    "make_taps",
     "round_bf16",
 ]
 
@@ -78,6 +80,11 @@ PRESETS = {
 IMAGE_SEED_BASE = 2000
 CLASS_SEED = 3000
 SINK_SEED = 4000
+HEAD_SEED = 5000
+TAPS_SEED = 6000
+
+# LibreYOLO DINOv2 semantic head (the diagram's "Projector P4" and "Task head")
+HEAD = dict(width=256, half=128, bottlenecks=3, classes=19, taps=4)
 
 
 def preset(name: str, **overrides) -> dict:
@@ -258,3 +265,56 @@ def make_class_embeddings(cfg: dict, classes: int | None = None, seed: int = CLA
     g /= np.sqrt((g * g).sum(axis=1, keepdims=True))
     g = g.astype(np.float32)
     return round_bf16(g) if cfg.get("bf16_params") else g
+
+
+def make_head_params(cfg: dict, seed: int = HEAD_SEED, classes: int | None = None) -> dict:
+    """Random parameters of the semantic head on the taps of ``cfg`` (conv weights in
+    the [out, in, kh, kw] layout of torch.nn.Conv2d).
+
+    Draw order (one PCG64 stream): proj_w [256, 4D, 1, 1], proj_ln_g, proj_ln_b; for
+    Bottleneck i = 1..3: bn{i}_w1 [128, 128, 3, 3], bn{i}_ln1_g, bn{i}_ln1_b,
+    bn{i}_w2, bn{i}_ln2_g, bn{i}_ln2_b; out_w [256, 640, 1, 1], out_ln_g, out_ln_b,
+    final_ln_g, final_ln_b; lat_w [256, 256, 1, 1], lat_b; smooth_w [256, 256, 3, 3],
+    smooth_b; gn_g, gn_b; pred_w [C, 256, 1, 1], pred_b.  Weights and biases are
+    N(0, 0.02), norm scales 1 + N(0, 0.02), norm shifts N(0, 0.02); rounded to bf16
+    when the encoder's parameters are.
+    """
+    D = cfg["dim"]
+    W, Hf, C = HEAD["width"], HEAD["half"], HEAD["classes"] if classes is None else classes
+    rng = np.random.default_rng(seed)
+    sd = np.float32(0.02)
+
+    def normal(*shape):
+        return rng.standard_normal(shape, dtype=np.float32) * sd
+
+    def gamma(n):
+        return np.float32(1.0) + normal(n)
+
+    P = {}
+    P["proj_w"] = normal(W, HEAD["taps"] * D, 1, 1)
+    P["proj_ln_g"], P["proj_ln_b"] = gamma(W), normal(W)
+    for i in range(1, HEAD["bottlenecks"] + 1):
+        P[f"bn{i}_w1"] = normal(Hf, Hf, 3, 3)
+        P[f"bn{i}_ln1_g"], P[f"bn{i}_ln1_b"] = gamma(Hf), normal(Hf)
+        P[f"bn{i}_w2"] = normal(Hf, Hf, 3, 3)
+        P[f"bn{i}_ln2_g"], P[f"bn{i}_ln2_b"] = gamma(Hf), normal(Hf)
+    P["out_w"] = normal(W, (2 + HEAD["bottlenecks"]) * Hf, 1, 1)
+    P["out_ln_g"], P["out_ln_b"] = gamma(W), normal(W)
+    P["final_ln_g"], P["final_ln_b"] = gamma(W), normal(W)
+    P["lat_w"], P["lat_b"] = normal(W, W, 1, 1), normal(W)
+    P["smooth_w"], P["smooth_b"] = normal(W, W, 3, 3), normal(W)
+    P["gn_g"], P["gn_b"] = gamma(W), normal(W)
+    P["pred_w"], P["pred_b"] = normal(C, W, 1, 1), normal(C)
+    if cfg.get("bf16_params"):
+        P = {k: round_bf16(v) for k, v in P.items()}
+    return P
+
+
+def make_taps(cfg: dict, batch: int, seed: int = TAPS_SEED, gh: int | None = None, gw: int | None = None) -> np.ndarray:
+    """Stand-in taps [batch, 4, D, gh, gw] float32 ~ N(0, 1) (LayerNormed features are
+    of unit scale), for testing the head apart from the encoder."""
+    g = grid(cfg)
+    gh = g[0] if gh is None else gh
+    gw = g[1] if gw is None else gw
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((batch, HEAD["taps"], cfg["dim"], gh, gw), dtype=np.float32)
