@@ -1,0 +1,104 @@
+/*
+ * vit_head.h - C ABI of the semantic head on the encoder's taps (MI355X, gfx950).
+ *
+ * The operation (LibreYOLO DINOv2 "n semantic" diagram, libreyolo.com):
+ *   "Projector P4": the taps (LayerNormed patch features after blocks 3, 6,
+ *   9, 12; vit_forward's d_taps) concatenated along channels; Conv2d 1x1
+ *   taps*D -> width without bias, channel LayerNorm, SiLU; split into halves
+ *   a, b; three Bottlenecks without shortcut, the first on b and each next one
+ *   on the previous output ("Projector Bottleneck": Conv2d 3x3/1 pad 1 without
+ *   bias, channel LayerNorm, SiLU, twice); concat a, b and the three outputs
+ *   (5 * width / 2 channels); "Projector output ConvX" (Conv2d 1x1 -> width
+ *   without bias, channel LayerNorm, SiLU); a final channel LayerNorm.
+ *   "Task head": lateral Conv2d 1x1 width -> width with bias; smoothing
+ *   Conv2d 3x3 pad 1 with bias; GroupNorm (groups); GELU (exact erf form);
+ *   Dropout2d (identity in evaluation); predict Conv2d 1x1 width -> classes
+ *   with bias; bilinear resize to out_h x out_w (align_corners=False).
+ *   "Size equivalence": width 256 and taps 3/6/9/12 at every size.
+ *
+ * Readings where the diagram is silent: a channel LayerNorm normalises the
+ * channels of each pixel (biased variance, eps inside the square root, here
+ * ln_eps = 1e-6 like the encoder's) with a per-channel affine; GroupNorm uses
+ * gn_eps = 1e-5 and a per-channel affine; the predict conv has a bias.
+ *
+ * Ownership, streams and errors follow vit.h: the caller allocates all device
+ * memory; every call enqueues on `stream` and returns without synchronising
+ * (except vit_head_create, which synchronises once after the upload); return
+ * values are 0 or a negative vit_status, with vit_last_error() describing the
+ * calling thread's last failure.  Calls on one vit_head must not overlap.
+ *
+ * Numerics: conv operands bf16 (nearest even) with fp32 accumulation; the
+ * normalisation statistics, the logits and the resize are fp32; activations
+ * between layers are stored as bf16.
+ */
+#ifndef VIT_HEAD_H
+#define VIT_HEAD_H
+
+#include <stddef.h>
+
+#include "vit.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct vit_head vit_head;
+
+typedef struct vit_head_config {
+  int grid_h, grid_w;   /* patch grid of the taps (37 x 37 for DINOv2-S/14 @518) */
+  int dim;              /* channels of one tap (encoder width D); multiple of 64 */
+  int taps;             /* number of taps concatenated (4) */
+  int width;            /* projector width (256); multiple of 128 */
+  int groups;           /* GroupNorm groups (32); width must equal 8 * groups */
+  int classes;          /* predicted classes (19); 1..1024 */
+  int out_h, out_w;     /* size of the resized logits (the image: 518 x 518) */
+  int max_batch;        /* largest batch passed to vit_head_forward */
+  float ln_eps;         /* channel LayerNorm epsilon (1e-6) */
+  float gn_eps;         /* GroupNorm epsilon (1e-5) */
+} vit_head_config;
+
+typedef struct vit_head_sizes {
+  size_t weight_bytes;     /* device bytes for the packed weights */
+  size_t workspace_bytes;  /* device bytes for activations */
+  size_t host_floats;      /* length of the fp32 parameter blob vit_head_create reads */
+} vit_head_sizes;
+
+/* The diagram's head for DINOv2-S/14 at 518 x 518 (grid 37 x 37, D 384, 4 taps,
+ * width 256, 32 groups, 19 classes, logits 518 x 518), max_batch 8.  Pure host. */
+int vit_head_config_preset(vit_head_config* out);
+
+/* Validate `cfg` and report the buffer sizes it needs.  Pure host function. */
+int vit_head_plan(const vit_head_config* cfg, vit_head_sizes* out);
+
+/* Build a head from the fp32 blob `host_params` (host memory, `host_floats`
+ * values), packing it into `d_weights` and binding `d_workspace` (device,
+ * 256-byte aligned, at least vit_head_plan's sizes).  Conv weights are
+ * rounded to bf16 (nearest even).  Synchronises `stream` before returning.
+ *
+ * Blob layout (fp32, concatenated in this order; conv weights [out, in, kh, kw]
+ * as in torch.nn.Conv2d; W = width, H2 = width / 2, T = taps * dim):
+ *   proj_w [W, T, 1, 1], proj_ln_g [W], proj_ln_b [W],
+ *   for i = 1, 2, 3: bn{i}_w1 [H2, H2, 3, 3], bn{i}_ln1_g [H2], bn{i}_ln1_b [H2],
+ *                    bn{i}_w2 [H2, H2, 3, 3], bn{i}_ln2_g [H2], bn{i}_ln2_b [H2],
+ *   out_w [W, 5 * H2, 1, 1], out_ln_g [W], out_ln_b [W], final_ln_g [W], final_ln_b [W],
+ *   lat_w [W, W, 1, 1], lat_b [W], smooth_w [W, W, 3, 3], smooth_b [W],
+ *   gn_g [W], gn_b [W], pred_w [classes, W, 1, 1], pred_b [classes]. */
+int vit_head_create(const vit_head_config* cfg, const float* host_params, size_t host_floats, void* d_weights,
+                    size_t weight_bytes, void* d_workspace, size_t workspace_bytes, void* stream, vit_head** out);
+
+/* Head forward for `batch` (1..max_batch) images.
+ *   d_taps    device fp32 [batch, taps, dim, grid_h, grid_w] (vit_forward's d_taps), 16-byte aligned
+ *   d_logits  device fp32 [batch, classes, out_h, out_w]: resized class logits
+ *   d_grid    NULL, or device fp32 [batch, classes, grid_h, grid_w]: the logits
+ *             before the resize
+ * Enqueue only. */
+int vit_head_forward(vit_head* h, const float* d_taps, int batch, float* d_logits, float* d_grid, void* stream);
+
+/* Release the host-side handle (device buffers belong to the caller). */
+int vit_head_destroy(vit_head* h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VIT_HEAD_H */

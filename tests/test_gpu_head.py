@@ -1,0 +1,135 @@
+"""GPU parity of the semantic head on the taps (LibreYOLO DINOv2 diagram,
+"Projector P4" and "Task head") against the float64 oracle.
+
+The head runs every conv on bf16 operands with fp32 accumulation and stores
+the activations between layers as bf16; each of its ten stored activations
+(taps, stem, six Bottleneck convs, projector output, lateral, GroupNorm output)
+carries a relative rounding of at most 2^-9, and every one is followed by a
+normalisation or a conv that keeps the activation scale near 1.  Summed over
+the ten, that is 10 * 2^-9 = 1.95e-2 of the logit scale in the worst case; the
+fp32 GEMM sums add far less (K <= 2304 terms at 2^-24).  The bound is 2e-2 of
+the largest |logit|.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import vision_transformer_encoder_block_amd as vit
+from gpu_util import f32_dev, host, require_gpu, say
+from oracle import head_oracle as H
+from oracle import vit_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 2e-2
+
+
+def run_head(hcfg, Ph, taps):
+    head = vit.SemanticHead(hcfg, Ph)
+    logits, grid = head.forward(f32_dev(taps), want_grid=True)
+    out = host(logits), host(grid)
+    head.close()
+    return out
+
+
+def oracle_head(taps, Ph, out_h, out_w):
+    refs = [H.semantic_head(taps[b], Ph, out_h, out_w) for b in range(taps.shape[0])]
+    return np.stack([r["logits"] for r in refs]), np.stack([r["grid"] for r in refs])
+
+
+def check(name, got, ref):
+    assert got.shape == ref.shape
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    scale = np.abs(ref).max()
+    say(f"{name}: max |gpu - oracle| = {err:.3e}, max |logit| = {scale:.3e}, ratio {err / scale:.3e}")
+    assert err <= REL_TOL * scale
+
+
+def check_labels(got, ref):
+    """Argmax over classes agrees wherever the oracle's top-two margin exceeds twice the bound."""
+    tol = REL_TOL * np.abs(ref).max()
+    srt = np.sort(ref, axis=1)
+    clear = (srt[:, -1] - srt[:, -2]) > 2 * tol
+    agree = np.argmax(got, axis=1) == np.argmax(ref, axis=1)
+    say(f"labels: {clear.mean():.3f} of pixels clear of ties, all of them agree: {agree[clear].all()}")
+    assert agree[clear].all()
+
+
+@pytest.mark.parametrize("batch,gh,gw,out", [(2, 6, 5, (84, 70)), (3, 13, 11, (100, 90)), (1, 1, 1, (7, 5))])
+def test_head_matches_oracle_small_grids(batch, gh, gw, out):
+    require_gpu()
+    cfg = synth.preset("vits14_518")
+    say(f"semantic head, batch {batch}, grid {gh}x{gw} -> {out}")
+    Ph = synth.make_head_params(cfg)
+    taps = synth.make_taps(cfg, batch, gh=gh, gw=gw)
+    got, got_grid = run_head(vit.head_config(gh, gw, out[0], out[1], batch), Ph, taps)
+    ref, ref_grid = oracle_head(taps, Ph, *out)
+    check("grid logits", got_grid, ref_grid)
+    check("resized logits", got, ref)
+
+
+def test_head_full_geometry_b8():
+    require_gpu()
+    cfg = synth.preset("vits14_518")
+    say("semantic head, batch 8, grid 37x37 -> 518x518")
+    Ph = synth.make_head_params(cfg)
+    taps = synth.make_taps(cfg, 8)
+    hcfg = vit.head_config_preset()
+    got, got_grid = run_head(hcfg, Ph, taps)
+    ref, ref_grid = oracle_head(taps, Ph, 518, 518)
+    check("grid logits", got_grid, ref_grid)
+    check("resized logits", got, ref)
+    check_labels(got, ref)
+
+
+def test_head_on_encoder_taps():
+    """The encoder's own taps (DINOv2-S/14 @518, batch 2) through the head."""
+    require_gpu()
+    cfg = synth.preset("vits14_518")
+    say("DINOv2-S/14 @518 b2 encoder taps -> semantic head")
+    P = synth.make_params(cfg)
+    Ph = synth.make_head_params(cfg)
+    x = synth.make_images(cfg, 2)
+    enc = vit.Encoder(cfg, P, max_batch=2)
+    _, taps = enc.forward(f32_dev(x), with_taps=True)
+    head = vit.SemanticHead(vit.head_config(37, 37, 518, 518, 2), Ph)
+    logits, grid = head.forward(taps, want_grid=True)
+    got, got_grid, taps_h = host(logits), host(grid), host(taps)
+    head.close()
+    enc.close()
+    ref, ref_grid = oracle_head(taps_h, Ph, 518, 518)
+    check("grid logits", got_grid, ref_grid)
+    check("resized logits", got, ref)
+
+
+def test_head_batch_invariance():
+    """Each image's logits do not depend on the rest of the batch (bit for bit)."""
+    require_gpu()
+    cfg = synth.preset("vits14_518")
+    Ph = synth.make_head_params(cfg)
+    taps = synth.make_taps(cfg, 3, gh=9, gw=10)
+    head = vit.SemanticHead(vit.head_config(9, 10, 40, 44, 3), Ph)
+    all3 = host(head.forward(f32_dev(taps)))
+    for b in range(3):
+        one = host(head.forward(f32_dev(taps[b:b + 1])))
+        np.testing.assert_array_equal(all3[b:b + 1], one)
+    head.close()
+
+
+def test_head_rejects_bad_calls():
+    require_gpu()
+    cfg = synth.preset("vits14_518")
+    Ph = synth.make_head_params(cfg)
+    head = vit.SemanticHead(vit.head_config(4, 4, 8, 8, 2), Ph)
+    taps = f32_dev(synth.make_taps(cfg, 3, gh=4, gw=4))
+    out = torch.empty((3, 19, 8, 8), device="cuda")
+    with pytest.raises(vit.VitError):
+        head.forward(taps, logits_out=out)      # batch 3 > max_batch 2
+    r = vit.lib().vit_head_forward(head.handle, vit._ptr(taps), 0, vit._ptr(out), None, None)
+    assert r == -3
+    head.close()
+    with pytest.raises(vit.VitError):
+        vit.SemanticHead(vit.head_config(4, 4, 8, 8, 2), np.zeros(10, np.float32))

@@ -137,3 +137,55 @@ def test_create_and_calls_validate_before_touching_the_device(L):
     assert lib.vit_op_preprocess(fake, 1, 8, 0, 0, fake, 4, 4, None) == -2
     assert lib.vit_op_preprocess(fake, 1, 8, 8, 0, fake, 70000, 4, None) == -2
     assert lib.vit_destroy(None) == 0
+
+
+# ------------------------------------------------------------------ semantic head (host side)
+
+def test_head_preset_matches_the_diagram(L):
+    c = vit.head_config_preset()
+    # LibreYOLO DINOv2 diagram: 4 taps of 384 x 37 x 37, projector width 256,
+    # GroupNorm 32 groups, 19 classes resized to 518 x 518
+    assert (c.grid_h, c.grid_w, c.dim, c.taps, c.width, c.groups, c.classes, c.out_h, c.out_w) == \
+        (37, 37, 384, 4, 256, 32, 19, 518, 518)
+    assert c.ln_eps == pytest.approx(1e-6) and c.gn_eps == pytest.approx(1e-5)
+    s = vit.head_plan(c)
+    Ph = synth.make_head_params(synth.preset("vits14_518"))
+    assert s.host_floats == vit.pack_head_params(Ph).size
+    assert s.weight_bytes > 2 * s.host_floats // 2 and s.workspace_bytes > 0
+
+
+def test_head_plan_rejects_bad_configs(L):
+    lib = ctypes.CDLL(vit.LIB_PATH)
+
+    def plan(**kw):
+        c = vit.head_config_preset()
+        for k, v in kw.items():
+            setattr(c, k, v)
+        out = vit.HeadSizes()
+        return lib.vit_head_plan(ctypes.byref(c), ctypes.byref(out))
+
+    assert plan() == 0
+    assert plan(width=128, groups=16) == 0
+    assert plan(width=192, groups=24) == -5      # width 128 or 256 only
+    assert plan(groups=16) == -5                 # width must be 8 * groups
+    assert plan(dim=100) == -5
+    assert plan(classes=0) == -1
+    assert plan(max_batch=0) == -1
+    assert plan(grid_h=0) == -2
+    assert plan(ln_eps=0.0) == -1
+    assert lib.vit_head_plan(None, ctypes.byref(vit.HeadSizes())) == -1
+
+
+def test_head_create_validates_before_touching_the_device(L):
+    lib = ctypes.CDLL(vit.LIB_PATH)
+    c = vit.head_config_preset()
+    s = vit.head_plan(c)
+    blob = np.zeros(s.host_floats - 1, np.float32)
+    h = ctypes.c_void_p()
+    fake = ctypes.c_void_p(256)
+    r = lib.vit_head_create(ctypes.byref(c), blob.ctypes.data_as(ctypes.c_void_p), ctypes.c_size_t(blob.size), fake,
+                            ctypes.c_size_t(s.weight_bytes), fake, ctypes.c_size_t(s.workspace_bytes), None,
+                            ctypes.byref(h))
+    assert r == -3 and not h.value
+    assert b"floats" in vit.lib().vit_last_error()
+    assert lib.vit_head_forward(None, None, 1, None, None, None) == -1

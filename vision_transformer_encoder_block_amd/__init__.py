@@ -24,6 +24,7 @@ __all__ = [
     "vit_destroy", "vit_last_error", "vit_op_layernorm", "vit_op_linear", "vit_op_qkv", "vit_op_attention",
     "vit_op_attention_workspace", "vit_op_preprocess", "vit_op_linear_residual_ln",
     "Encoder", "EncoderGraph", "EPI_BIAS_BF16", "EPI_GELU_BF16", "EPI_RESIDUAL", "EPI_BIAS_F32",
+    "HeadConfig", "HeadSizes", "head_config_preset", "head_config", "head_plan", "pack_head_params", "SemanticHead",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvit.so")
@@ -85,6 +86,12 @@ _SIGNATURES = {
     "vit_op_attention_workspace": (ctypes.c_size_t, [_I, _I, _I]),
     "vit_op_preprocess": (_I, [_P, _I, _I, _I, _I, _P, _I, _I, _P]),
     "vit_op_linear_residual_ln": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P, _P, ctypes.c_float, _P, _P]),
+    "vit_head_config_preset": (_I, [_P]),
+    "vit_head_plan": (_I, [_P, _P]),
+    "vit_head_create": (_I, [_P, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P,
+                             ctypes.POINTER(_P)]),
+    "vit_head_forward": (_I, [_P, _P, _I, _P, _P, _P]),
+    "vit_head_destroy": (_I, [_P]),
 }
 
 
@@ -332,3 +339,91 @@ class EncoderGraph:
     def replay(self):
         self.graph.replay()
 
+
+
+# ---------------------------------------------------------------------------- semantic head
+
+class HeadConfig(ctypes.Structure):
+    """Mirror of vit_head_config (include/vit_head.h)."""
+    _fields_ = [("grid_h", _I), ("grid_w", _I), ("dim", _I), ("taps", _I), ("width", _I), ("groups", _I),
+                ("classes", _I), ("out_h", _I), ("out_w", _I), ("max_batch", _I), ("ln_eps", ctypes.c_float),
+                ("gn_eps", ctypes.c_float)]
+
+
+class HeadSizes(ctypes.Structure):
+    """Mirror of vit_head_sizes."""
+    _fields_ = [("weight_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t),
+                ("host_floats", ctypes.c_size_t)]
+
+
+def head_config_preset() -> HeadConfig:
+    c = HeadConfig()
+    _check("vit_head_config_preset", lib().vit_head_config_preset(ctypes.byref(c)))
+    return c
+
+
+def head_config(grid_h: int, grid_w: int, out_h: int, out_w: int, max_batch: int, dim: int = 384, taps: int = 4,
+                width: int = 256, classes: int = 19) -> HeadConfig:
+    """A HeadConfig for the given geometry (the diagram's widths and epsilons otherwise)."""
+    return HeadConfig(grid_h, grid_w, dim, taps, width, width // 8, classes, out_h, out_w, max_batch, 1e-6, 1e-5)
+
+
+def head_plan(cfg: HeadConfig) -> HeadSizes:
+    s = HeadSizes()
+    _check("vit_head_plan", lib().vit_head_plan(ctypes.byref(cfg), ctypes.byref(s)))
+    return s
+
+
+_HEAD_ORDER = (["proj_w", "proj_ln_g", "proj_ln_b"]
+               + [f"bn{i}_{k}" for i in (1, 2, 3) for k in ("w1", "ln1_g", "ln1_b", "w2", "ln2_g", "ln2_b")]
+               + ["out_w", "out_ln_g", "out_ln_b", "final_ln_g", "final_ln_b", "lat_w", "lat_b", "smooth_w",
+                  "smooth_b", "gn_g", "gn_b", "pred_w", "pred_b"])
+
+
+def pack_head_params(P: dict) -> np.ndarray:
+    """Concatenate a head parameter dictionary into the fp32 blob order of vit_head_create."""
+    return np.concatenate([np.ascontiguousarray(P[k], dtype=np.float32).ravel() for k in _HEAD_ORDER])
+
+
+class SemanticHead:
+    """A created semantic head with torch-owned weight and workspace buffers."""
+
+    def __init__(self, cfg: HeadConfig, params: dict | np.ndarray, device: str = "cuda", stream=None):
+        import torch
+        self.cfg = cfg
+        self.sizes = head_plan(cfg)
+        blob = params if isinstance(params, np.ndarray) else pack_head_params(params)
+        self.device = torch.device(device)
+        self.weights = torch.empty(self.sizes.weight_bytes, dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(self.sizes.workspace_bytes, dtype=torch.uint8, device=self.device)
+        blob = np.ascontiguousarray(blob, dtype=np.float32)
+        h = _P()
+        _check("vit_head_create", lib().vit_head_create(ctypes.byref(cfg), blob.ctypes.data, blob.size,
+                                                        _ptr(self.weights), self.sizes.weight_bytes,
+                                                        _ptr(self.workspace), self.sizes.workspace_bytes,
+                                                        _stream(stream), ctypes.byref(h)))
+        self.handle = h
+
+    def forward(self, taps, logits_out=None, want_grid: bool = False, stream=None):
+        import torch
+        c = self.cfg
+        B = taps.shape[0]
+        if logits_out is None:
+            logits_out = torch.empty((B, c.classes, c.out_h, c.out_w), dtype=torch.float32, device=self.device)
+        grid = None
+        if want_grid:
+            grid = torch.empty((B, c.classes, c.grid_h, c.grid_w), dtype=torch.float32, device=self.device)
+        _check("vit_head_forward", lib().vit_head_forward(self.handle, _ptr(taps), B, _ptr(logits_out), _ptr(grid),
+                                                          _stream(stream)))
+        return (logits_out, grid) if want_grid else logits_out
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            lib().vit_head_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

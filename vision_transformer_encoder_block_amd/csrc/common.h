@@ -144,4 +144,25 @@ __device__ __forceinline__ void ln_group_normalize(float4 (&v)[V4], const float4
                        v[i].z * rstd * gg[i].z + bb[i].z, v[i].w * rstd * gg[i].w + bb[i].w);
 }
 
+// Source index and weight of output position i along an axis (n_in -> n_out):
+// the centre (i + 1/2) n_in / n_out - 1/2 is the exact rational
+// ((2i + 1) n_in - n_out) / (2 n_out), split into its integer part and an
+// exactly computed remainder, so the weight carries only the rounding of one
+// division (a float coordinate near 700 would carry an ulp of 6e-5).
+// Negative centres clamp to 0; indices past the edge clamp to n_in - 1.
+__device__ __forceinline__ void bilinear_tap(int i, int n_in, int n_out, int& i0, int& i1, float& w) {
+  const long long num = (long long)(2 * i + 1) * n_in - n_out;
+  const long long den = 2LL * n_out;
+  if (num <= 0) {
+    i0 = 0;
+    w = 0.f;
+  } else {
+    const long long q = num / den;
+    i0 = (int)q;
+    w = (float)(num - q * den) / (float)den;
+  }
+  i0 = min(i0, n_in - 1);
+  i1 = min(i0 + 1, n_in - 1);
+}
+
 }  // namespace vit

@@ -123,27 +123,6 @@ __global__ __launch_bounds__(256) void crops_kernel(const float* __restrict__ im
   }
 }
 
-// Source index and weight of output position i along an axis (n_in -> n_out):
-// the centre (i + 1/2) n_in / n_out - 1/2 is the exact rational
-// ((2i + 1) n_in - n_out) / (2 n_out), split into its integer part and an
-// exactly computed remainder, so the weight carries only the rounding of one
-// division (a float coordinate near 700 would carry an ulp of 6e-5).
-// Negative centres clamp to 0; indices past the edge clamp to n_in - 1.
-__device__ __forceinline__ void bilinear_tap(int i, int n_in, int n_out, int& i0, int& i1, float& w) {
-  const long long num = (long long)(2 * i + 1) * n_in - n_out;
-  const long long den = 2LL * n_out;
-  if (num <= 0) {
-    i0 = 0;
-    w = 0.f;
-  } else {
-    const long long q = num / den;
-    i0 = (int)q;
-    w = (float)(num - q * den) / (float)den;
-  }
-  i0 = min(i0, n_in - 1);
-  i1 = min(i0 + 1, n_in - 1);
-}
-
 // Frame preprocessing: one thread per output pixel of one row.  Bilinear
 // sample (half-pixel centres, coordinates clamped at the edges) of the three
 // 8-bit channels, scaled by 1/255 and normalised with the ImageNet mean/std

@@ -1,0 +1,312 @@
+// Host runtime and C ABI of the semantic head on the encoder's taps: config
+// validation, buffer planning, weight packing (fp32 blob -> bf16 GEMM
+// operands with 3x3 kernels reordered to (ky, kx, c) columns, fp32 vectors)
+// and the launch sequence on the caller's stream.  Like the encoder, the head
+// never allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "host_error.h"
+#include "kernels.h"
+#include "vit_head.h"
+
+namespace {
+
+using vit::report_error;
+
+int hip_fail(hipError_t e, const char* what) {
+  return report_error(VIT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define HEAD_HIP(call, what)                          \
+  do {                                                \
+    hipError_t e_ = (call);                           \
+    if (e_ != hipSuccess) return hip_fail(e_, what);  \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+constexpr int kBottlenecks = 3;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+uint16_t host_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+struct HeadPlan {
+  vit_head_config cfg;
+  int P = 0, T = 0, W = 0, H2 = 0, C = 0;   // pixels per image, concat width, width, half, classes
+  size_t host_floats = 0;
+  // weights (byte offsets)
+  size_t proj_w, proj_g, proj_b, out_w, out_g, out_b, fin_g, fin_b, lat_w, lat_b, sm_w, sm_b, gn_g, gn_b, pred_w,
+      pred_b, wtotal;
+  size_t bn_w[kBottlenecks][2], bn_g[kBottlenecks][2], bn_b[kBottlenecks][2];
+  // workspace (byte offsets)
+  size_t x0, f, y, t, col, p4, lat, g, grid, stotal;
+};
+
+int validate(const vit_head_config* c) {
+  if (!c) return report_error(VIT_ERR_ARG, "vit_head_config is NULL");
+  if (c->grid_h < 1 || c->grid_w < 1 || (long)c->grid_h * c->grid_w > (1L << 20))
+    return report_error(VIT_ERR_SHAPE, "grid must be at least 1 x 1 and at most 2^20 pixels");
+  if (c->dim < 64 || c->dim % 64) return report_error(VIT_ERR_UNSUPPORTED, "dim must be a positive multiple of 64");
+  if (c->taps < 1 || c->taps > 16) return report_error(VIT_ERR_ARG, "taps must be in [1, 16]");
+  if (c->width != 128 && c->width != 256)
+    return report_error(VIT_ERR_UNSUPPORTED, "width must be 128 or 256 (channel LayerNorm rows of 64 or 128 lanes)");
+  if (c->groups < 1 || c->width != 8 * c->groups) return report_error(VIT_ERR_UNSUPPORTED, "width must equal 8 * groups");
+  if (c->classes < 1 || c->classes > 1024) return report_error(VIT_ERR_ARG, "classes must be in [1, 1024]");
+  if (c->out_h < 1 || c->out_w < 1 || c->out_h > 65535 || c->out_w > 65535)
+    return report_error(VIT_ERR_ARG, "out_h and out_w must be in [1, 65535]");
+  if (c->max_batch < 1 || c->max_batch > 4096) return report_error(VIT_ERR_ARG, "max_batch must be in [1, 4096]");
+  if ((long)c->max_batch * c->grid_h * c->grid_w * 9 * c->width > (1L << 31))
+    return report_error(VIT_ERR_SIZE, "batch x grid too large");
+  if (!(c->ln_eps > 0.f) || !std::isfinite(c->ln_eps) || !(c->gn_eps > 0.f) || !std::isfinite(c->gn_eps))
+    return report_error(VIT_ERR_ARG, "epsilons must be positive");
+  return VIT_OK;
+}
+
+int build_plan(const vit_head_config* c, HeadPlan& pl) {
+  int r = validate(c);
+  if (r) return r;
+  pl.cfg = *c;
+  pl.P = c->grid_h * c->grid_w;
+  pl.T = c->taps * c->dim;
+  pl.W = c->width;
+  pl.H2 = c->width / 2;
+  pl.C = c->classes;
+  const size_t W = pl.W, H2 = pl.H2, T = pl.T, C = pl.C;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  pl.proj_w = take(W * T * 2);
+  pl.proj_g = take(W * 4);
+  pl.proj_b = take(W * 4);
+  for (int i = 0; i < kBottlenecks; ++i)
+    for (int j = 0; j < 2; ++j) {
+      pl.bn_w[i][j] = take(H2 * 9 * H2 * 2);
+      pl.bn_g[i][j] = take(H2 * 4);
+      pl.bn_b[i][j] = take(H2 * 4);
+    }
+  pl.out_w = take(W * 5 * H2 * 2);
+  pl.out_g = take(W * 4);
+  pl.out_b = take(W * 4);
+  pl.fin_g = take(W * 4);
+  pl.fin_b = take(W * 4);
+  pl.lat_w = take(W * W * 2);
+  pl.lat_b = take(W * 4);
+  pl.sm_w = take(W * 9 * W * 2);
+  pl.sm_b = take(W * 4);
+  pl.gn_g = take(W * 4);
+  pl.gn_b = take(W * 4);
+  pl.pred_w = take(C * W * 2);
+  pl.pred_b = take(C * 4);
+  pl.wtotal = off;
+  pl.host_floats = W * T + 2 * W + kBottlenecks * 2 * (H2 * H2 * 9 + 2 * H2) + W * 5 * H2 + 4 * W + W * W + W +
+                   W * W * 9 + W + 2 * W + C * W + C;
+
+  const size_t M = (size_t)c->max_batch * pl.P;
+  off = 0;
+  pl.x0 = take(M * T * 2);
+  pl.f = take(M * W * 4);
+  pl.y = take(M * 5 * H2 * 2);
+  pl.t = take(M * H2 * 2);
+  pl.col = take(M * 9 * W * 2);
+  pl.p4 = take(M * W * 2);
+  pl.lat = take(M * W * 2);
+  pl.g = take(M * W * 2);
+  pl.grid = take(M * C * 4);
+  pl.stotal = off;
+  return VIT_OK;
+}
+
+}  // namespace
+
+struct vit_head {
+  HeadPlan pl;
+  char* w = nullptr;   // weights
+  char* s = nullptr;   // workspace
+};
+
+extern "C" {
+
+int vit_head_config_preset(vit_head_config* out) {
+  if (!out) return report_error(VIT_ERR_ARG, "out is NULL");
+  *out = vit_head_config{37, 37, 384, 4, 256, 32, 19, 518, 518, 8, 1e-6f, 1e-5f};
+  return VIT_OK;
+}
+
+int vit_head_plan(const vit_head_config* cfg, vit_head_sizes* out) {
+  if (!out) return report_error(VIT_ERR_ARG, "out is NULL");
+  HeadPlan pl;
+  int r = build_plan(cfg, pl);
+  if (r) return r;
+  out->weight_bytes = pl.wtotal;
+  out->workspace_bytes = pl.stotal;
+  out->host_floats = pl.host_floats;
+  return VIT_OK;
+}
+
+int vit_head_create(const vit_head_config* cfg, const float* host_params, size_t host_floats, void* d_weights,
+                    size_t weight_bytes, void* d_workspace, size_t workspace_bytes, void* stream, vit_head** out) {
+  if (!out) return report_error(VIT_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  HeadPlan pl;
+  int r = build_plan(cfg, pl);
+  if (r) return r;
+  if (!host_params || !d_weights || !d_workspace) return report_error(VIT_ERR_ARG, "NULL parameter or buffer pointer");
+  if (host_floats != pl.host_floats)
+    return report_error(VIT_ERR_SIZE, "parameter blob has " + std::to_string(host_floats) + " floats, expected " +
+                                          std::to_string(pl.host_floats));
+  if (weight_bytes < pl.wtotal) return report_error(VIT_ERR_SIZE, "weight buffer smaller than vit_head_plan's weight_bytes");
+  if (workspace_bytes < pl.stotal)
+    return report_error(VIT_ERR_SIZE, "workspace smaller than vit_head_plan's workspace_bytes");
+  if (((uintptr_t)d_weights | (uintptr_t)d_workspace) % kAlign)
+    return report_error(VIT_ERR_ARG, "device buffers must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (vit::prepare_gemm() != hipSuccess) return report_error(VIT_ERR_HIP, "GEMM tables could not be set up");
+
+  std::vector<unsigned char> stage(pl.wtotal, 0);
+  const float* src = host_params;
+  auto put_f32 = [&](size_t at, size_t n) {
+    std::memcpy(stage.data() + at, src, n * 4);
+    src += n;
+  };
+  auto put_bf16 = [&](size_t at, size_t n) {  // [out, in, 1, 1] = GEMM [N, K]
+    uint16_t* d = reinterpret_cast<uint16_t*>(stage.data() + at);
+    for (size_t i = 0; i < n; ++i) d[i] = host_bf16(src[i]);
+    src += n;
+  };
+  auto put_conv3 = [&](size_t at, size_t co, size_t ci) {  // [co, ci, 3, 3] -> [co, (ky, kx, ci)]
+    uint16_t* d = reinterpret_cast<uint16_t*>(stage.data() + at);
+    for (size_t o = 0; o < co; ++o)
+      for (size_t c = 0; c < ci; ++c)
+        for (size_t k = 0; k < 9; ++k) d[o * 9 * ci + k * ci + c] = host_bf16(src[(o * ci + c) * 9 + k]);
+    src += co * ci * 9;
+  };
+  const size_t W = pl.W, H2 = pl.H2, T = pl.T, C = pl.C;
+  put_bf16(pl.proj_w, W * T);
+  put_f32(pl.proj_g, W);
+  put_f32(pl.proj_b, W);
+  for (int i = 0; i < kBottlenecks; ++i)
+    for (int j = 0; j < 2; ++j) {
+      put_conv3(pl.bn_w[i][j], H2, H2);
+      put_f32(pl.bn_g[i][j], H2);
+      put_f32(pl.bn_b[i][j], H2);
+    }
+  put_bf16(pl.out_w, W * 5 * H2);
+  put_f32(pl.out_g, W);
+  put_f32(pl.out_b, W);
+  put_f32(pl.fin_g, W);
+  put_f32(pl.fin_b, W);
+  put_bf16(pl.lat_w, W * W);
+  put_f32(pl.lat_b, W);
+  put_conv3(pl.sm_w, W, W);
+  put_f32(pl.sm_b, W);
+  put_f32(pl.gn_g, W);
+  put_f32(pl.gn_b, W);
+  put_bf16(pl.pred_w, C * W);
+  put_f32(pl.pred_b, C);
+  if ((size_t)(src - host_params) != pl.host_floats) return report_error(VIT_ERR_ARG, "internal: blob walk mismatch");
+
+  auto* h = new (std::nothrow) vit_head();
+  if (!h) return report_error(VIT_ERR_ARG, "out of host memory");
+  h->pl = pl;
+  h->w = (char*)d_weights;
+  h->s = (char*)d_workspace;
+  hipError_t e = hipMemcpyAsync(d_weights, stage.data(), pl.wtotal, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "head weight upload");
+  }
+  *out = h;
+  return VIT_OK;
+}
+
+int vit_head_forward(vit_head* h, const float* d_taps, int batch, float* d_logits, float* d_grid, void* stream) {
+  if (!h || !d_taps || !d_logits) return report_error(VIT_ERR_ARG, "NULL head, taps or logits pointer");
+  const HeadPlan& pl = h->pl;
+  const vit_head_config& c = pl.cfg;
+  if (batch < 1 || batch > c.max_batch) return report_error(VIT_ERR_SIZE, "batch must be in [1, max_batch]");
+  if ((uintptr_t)d_taps % 16) return report_error(VIT_ERR_ARG, "taps must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const int M = batch * pl.P, W = pl.W, H2 = pl.H2, T = pl.T, C = pl.C, ldy = 5 * H2;
+  char* w = h->w;
+  char* s = h->s;
+  auto bf = [](char* p, size_t at) { return reinterpret_cast<uint16_t*>(p + at); };
+  auto f32 = [](char* p, size_t at) { return reinterpret_cast<float*>(p + at); };
+  uint16_t *x0 = bf(s, pl.x0), *y = bf(s, pl.y), *t = bf(s, pl.t), *col = bf(s, pl.col), *p4 = bf(s, pl.p4),
+           *lat = bf(s, pl.lat), *g = bf(s, pl.g);
+  float *f = f32(s, pl.f), *grid = f32(s, pl.grid);
+  auto gemm_f32 = [&](const uint16_t* a, size_t wo, int N, int K, const float* bias, float* outp) {
+    vit::EpiParams ep;
+    ep.kind = vit::EPI_BIAS_F32;
+    ep.bias = bias;
+    ep.out = outp;
+    ep.ldc = N;
+    return vit::launch_gemm(a, bf(w, wo), M, N, K, ep, st);
+  };
+
+  // Projector P4
+  HEAD_HIP(vit::launch_taps_cl(d_taps, batch, c.taps, c.dim, pl.P, x0, st), "taps to channels-last");
+  HEAD_HIP(gemm_f32(x0, pl.proj_w, W, T, nullptr, f), "projector conv");
+  HEAD_HIP(vit::launch_chan_ln(f, M, W, f32(w, pl.proj_g), f32(w, pl.proj_b), c.ln_eps, true, nullptr, nullptr, y,
+                               ldy, 0, st),
+           "projector LayerNorm");
+  for (int i = 0; i < kBottlenecks; ++i) {
+    // input: b (channels H2 .. 2 H2) for the first, then the previous output
+    HEAD_HIP(vit::launch_im2col3(y, ldy, H2 * (i + 1), H2, batch, c.grid_h, c.grid_w, col, st), "bottleneck im2col");
+    HEAD_HIP(gemm_f32(col, pl.bn_w[i][0], H2, 9 * H2, nullptr, f), "bottleneck conv 1");
+    HEAD_HIP(vit::launch_chan_ln(f, M, H2, f32(w, pl.bn_g[i][0]), f32(w, pl.bn_b[i][0]), c.ln_eps, true, nullptr,
+                                 nullptr, t, H2, 0, st),
+             "bottleneck LayerNorm 1");
+    HEAD_HIP(vit::launch_im2col3(t, H2, 0, H2, batch, c.grid_h, c.grid_w, col, st), "bottleneck im2col");
+    HEAD_HIP(gemm_f32(col, pl.bn_w[i][1], H2, 9 * H2, nullptr, f), "bottleneck conv 2");
+    HEAD_HIP(vit::launch_chan_ln(f, M, H2, f32(w, pl.bn_g[i][1]), f32(w, pl.bn_b[i][1]), c.ln_eps, true, nullptr,
+                                 nullptr, y, ldy, H2 * (i + 2), st),
+             "bottleneck LayerNorm 2");
+  }
+  HEAD_HIP(gemm_f32(y, pl.out_w, W, ldy, nullptr, f), "projector output conv");
+  HEAD_HIP(vit::launch_chan_ln(f, M, W, f32(w, pl.out_g), f32(w, pl.out_b), c.ln_eps, true, f32(w, pl.fin_g),
+                               f32(w, pl.fin_b), p4, W, 0, st),
+           "projector output LayerNorms");
+  // Task head
+  {
+    vit::EpiParams ep;
+    ep.kind = vit::EPI_BIAS_BF16;
+    ep.bias = f32(w, pl.lat_b);
+    ep.out = lat;
+    ep.ldc = W;
+    HEAD_HIP(vit::launch_gemm(p4, bf(w, pl.lat_w), M, W, W, ep, st), "lateral conv");
+  }
+  HEAD_HIP(vit::launch_im2col3(lat, W, 0, W, batch, c.grid_h, c.grid_w, col, st), "smoothing im2col");
+  HEAD_HIP(gemm_f32(col, pl.sm_w, W, 9 * W, f32(w, pl.sm_b), f), "smoothing conv");
+  HEAD_HIP(vit::launch_groupnorm_gelu(f, batch, pl.P, W, c.groups, f32(w, pl.gn_g), f32(w, pl.gn_b), c.gn_eps, g, st),
+           "GroupNorm + GELU");
+  HEAD_HIP(gemm_f32(g, pl.pred_w, C, W, f32(w, pl.pred_b), grid), "predict conv");
+  HEAD_HIP(vit::launch_resize_nchw(grid, C, C, batch, c.grid_h, c.grid_w, d_logits, c.out_h, c.out_w, st),
+           "logit resize");
+  if (d_grid)
+    HEAD_HIP(vit::launch_resize_nchw(grid, C, C, batch, c.grid_h, c.grid_w, d_grid, c.grid_h, c.grid_w, st),
+             "grid logits");
+  return VIT_OK;
+}
+
+int vit_head_destroy(vit_head* h) {
+  delete h;
+  return VIT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,238 @@
+// Kernels of the semantic head on the encoder's taps (LibreYOLO DINOv2
+// diagram, "Projector P4", "Projector Bottleneck", "Projector output ConvX",
+// "Task head").  Activations live channels-last, one row per pixel
+// ([batch * gh * gw, C]), so 1x1 convs are plain GEMMs on the MFMA kernel and
+// 3x3 convs are an im2col here followed by the same GEMM.  What remains here
+// is the data movement and the per-pixel / per-group normalisations:
+//   taps_cl_kernel        channel-first fp32 taps -> channels-last bf16 concat
+//   im2col3_kernel        3x3 / pad 1 patches of a channels-last slice
+//   chan_ln_kernel        channel LayerNorm (+ SiLU) (+ a second LayerNorm)
+//   groupnorm_gelu_kernel GroupNorm over (channels of a group x pixels) + GELU
+//   resize_nchw_kernel    bilinear resize of class-minor logits to [B, C, H, W]
+#include "common.h"
+#include "kernels.h"
+
+namespace vit {
+namespace {
+
+// One 64-channel x 64-pixel tile of one (image, tap) through LDS: reads are
+// contiguous along pixels (the taps are channel-first), writes are 16 bytes
+// (8 channels) per lane along the concatenated channels of a pixel row.
+__global__ __launch_bounds__(256) void taps_cl_kernel(const float* __restrict__ taps, int ntaps, int D, int P,
+                                                      uint16_t* __restrict__ out) {
+  __shared__ float tile[64][65];
+  const int p0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int bt = blockIdx.z;              // b * ntaps + t
+  const int b = bt / ntaps, t = bt - b * ntaps;
+  const float* src = taps + ((size_t)bt * D + c0) * P;
+  const int tid = threadIdx.x;
+  const int col = tid & 63;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = (tid >> 6) + 4 * k;   // channel within the tile
+    tile[r][col] = (p0 + col < P) ? src[(size_t)r * P + p0 + col] : 0.f;
+  }
+  __syncthreads();
+  const int ldo = ntaps * D;
+  const int chunk = tid & 7;            // 8 channels
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int pl = (tid >> 3) + 32 * pass;
+    if (p0 + pl < P) {
+      const int c = chunk * 8;
+      uint4 u = make_uint4(pack_bf16x2(tile[c][pl], tile[c + 1][pl]), pack_bf16x2(tile[c + 2][pl], tile[c + 3][pl]),
+                           pack_bf16x2(tile[c + 4][pl], tile[c + 5][pl]), pack_bf16x2(tile[c + 6][pl], tile[c + 7][pl]));
+      *reinterpret_cast<uint4*>(out + ((size_t)b * P + p0 + pl) * ldo + t * D + c0 + c) = u;
+    }
+  }
+}
+
+// out[m, (ky * 3 + kx) * C + c] = in[pixel (y + ky - 1, x + kx - 1) of image b, c0 + c],
+// zero outside the grid.  One thread per 8 channels of one (pixel, tap).
+__global__ __launch_bounds__(256) void im2col3_kernel(const uint16_t* __restrict__ in, int ld_in, int c0, int C,
+                                                      int batch, int gh, int gw, uint16_t* __restrict__ out) {
+  const int chunks = C / 8;
+  const size_t total = (size_t)batch * gh * gw * 9 * chunks;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int ch = (int)(idx % chunks);
+  const size_t mk = idx / chunks;
+  const int k = (int)(mk % 9);
+  const size_t m = mk / 9;
+  const int P = gh * gw;
+  const int b = (int)(m / P), pix = (int)(m - (size_t)b * P);
+  const int y = pix / gw + k / 3 - 1, x = pix % gw + k % 3 - 1;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (y >= 0 && y < gh && x >= 0 && x < gw)
+    v = *reinterpret_cast<const uint4*>(in + ((size_t)b * P + y * gw + x) * ld_in + c0 + ch * 8);
+  *reinterpret_cast<uint4*>(out + m * (size_t)(9 * C) + k * C + ch * 8) = v;
+}
+
+// Channel LayerNorm of rows of x [M, C] (C / 4 lanes per row, one float4
+// each), optionally SiLU and a second LayerNorm, written as bf16 to
+// out + m * ld_out + c0.  The statistics use the encoder's LayerNorm routine.
+template <int C>
+__global__ __launch_bounds__(256) void chan_ln_kernel(const float* __restrict__ x, int M, const float* __restrict__ g,
+                                                      const float* __restrict__ b, float eps, bool silu,
+                                                      const float* __restrict__ g2, const float* __restrict__ b2,
+                                                      uint16_t* __restrict__ out, int ld_out, int c0) {
+  constexpr int LPR = C / 4;
+  constexpr int RPW = 64 / LPR;          // rows per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sl = lane % LPR;
+  const int m = (blockIdx.x * 4 + wave) * RPW + lane / LPR;
+  const int mc = min(m, M - 1);          // every lane joins the group sums
+  float4 v[1] = {reinterpret_cast<const float4*>(x + (size_t)mc * C)[sl]};
+  const float4 gg[1] = {reinterpret_cast<const float4*>(g)[sl]};
+  const float4 bb[1] = {reinterpret_cast<const float4*>(b)[sl]};
+  ln_group_normalize<1, LPR>(v, gg, bb, eps, C);
+  if (silu) {
+    v[0].x = v[0].x / (1.f + expf(-v[0].x));
+    v[0].y = v[0].y / (1.f + expf(-v[0].y));
+    v[0].z = v[0].z / (1.f + expf(-v[0].z));
+    v[0].w = v[0].w / (1.f + expf(-v[0].w));
+  }
+  if (g2) {
+    const float4 g2v[1] = {reinterpret_cast<const float4*>(g2)[sl]};
+    const float4 b2v[1] = {reinterpret_cast<const float4*>(b2)[sl]};
+    ln_group_normalize<1, LPR>(v, g2v, b2v, eps, C);
+  }
+  if (m < M)
+    *reinterpret_cast<uint2*>(out + (size_t)m * ld_out + c0 + sl * 4) =
+        make_uint2(pack_bf16x2(v[0].x, v[0].y), pack_bf16x2(v[0].z, v[0].w));
+}
+
+// GroupNorm (8 channels per group) over the P pixels of one image, then the
+// per-channel affine and the exact GELU; one workgroup per (group, image),
+// two passes for the mean and the biased variance as in the definition.
+__global__ __launch_bounds__(256) void groupnorm_gelu_kernel(const float* __restrict__ x, int P, int C,
+                                                             const float* __restrict__ g, const float* __restrict__ bta,
+                                                             float eps, uint16_t* __restrict__ out) {
+  __shared__ float red[4];
+  const int grp = blockIdx.x, b = blockIdx.y;
+  const int c0 = grp * 8;
+  const float* base = x + (size_t)b * P * C + c0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto block_sum = [&](float s) {
+    s = wave_sum(s);
+    if (lane == 0) red[wave] = s;
+    __syncthreads();
+    const float t = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return t;
+  };
+  float s = 0.f;
+  for (int p = tid; p < P; p += 256) {
+    const float4 u = reinterpret_cast<const float4*>(base + (size_t)p * C)[0];
+    const float4 w = reinterpret_cast<const float4*>(base + (size_t)p * C)[1];
+    s += ((u.x + u.y) + (u.z + u.w)) + ((w.x + w.y) + (w.z + w.w));
+  }
+  const float n = 8.f * (float)P;
+  const float mean = block_sum(s) / n;
+  float q = 0.f;
+  for (int p = tid; p < P; p += 256) {
+    const float4 u = reinterpret_cast<const float4*>(base + (size_t)p * C)[0];
+    const float4 w = reinterpret_cast<const float4*>(base + (size_t)p * C)[1];
+    const float d[8] = {u.x - mean, u.y - mean, u.z - mean, u.w - mean, w.x - mean, w.y - mean, w.z - mean, w.w - mean};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q += d[i] * d[i];
+  }
+  const float rstd = rsqrtf(block_sum(q) / n + eps);
+  float gs[8], bs[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) gs[i] = g[c0 + i] * rstd, bs[i] = bta[c0 + i];
+  for (int p = tid; p < P; p += 256) {
+    const float4 u = reinterpret_cast<const float4*>(base + (size_t)p * C)[0];
+    const float4 w = reinterpret_cast<const float4*>(base + (size_t)p * C)[1];
+    const float v[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float z = (v[i] - mean) * gs[i] + bs[i];
+      y[i] = 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
+    }
+    *reinterpret_cast<uint4*>(out + ((size_t)b * P + p) * C + c0) =
+        make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+  }
+}
+
+// Bilinear resize (half-pixel centres, exact rational taps, clamped) of
+// class-minor logits in [batch * gh * gw, ldi] to out [batch, classes, H, W];
+// one thread per output pixel, looping over the classes.
+__global__ __launch_bounds__(256) void resize_nchw_kernel(const float* __restrict__ in, int ldi, int classes, int gh,
+                                                          int gw, float* __restrict__ out, int H, int W) {
+  const int x = blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= W) return;
+  const int y = blockIdx.y, b = blockIdx.z;
+  int y0, y1, x0, x1;
+  float ly, lx;
+  bilinear_tap(y, gh, H, y0, y1, ly);
+  bilinear_tap(x, gw, W, x0, x1, lx);
+  const float* base = in + (size_t)b * gh * gw * ldi;
+  const float* r00 = base + (size_t)(y0 * gw + x0) * ldi;
+  const float* r01 = base + (size_t)(y0 * gw + x1) * ldi;
+  const float* r10 = base + (size_t)(y1 * gw + x0) * ldi;
+  const float* r11 = base + (size_t)(y1 * gw + x1) * ldi;
+  float* o = out + (size_t)b * classes * H * W + (size_t)y * W + x;
+  for (int c = 0; c < classes; ++c) {
+    const float top = (1.f - lx) * r00[c] + lx * r01[c];
+    const float bot = (1.f - lx) * r10[c] + lx * r11[c];
+    o[(size_t)c * H * W] = (1.f - ly) * top + ly * bot;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_taps_cl(const float* taps, int batch, int ntaps, int D, int P, uint16_t* out, hipStream_t s) {
+  if (batch < 1 || ntaps < 1 || D % 64 || P < 1 || (long)batch * ntaps > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(taps_cl_kernel, dim3((P + 63) / 64, D / 64, batch * ntaps), dim3(256), 0, s, taps, ntaps, D, P,
+                     out);
+  return hipGetLastError();
+}
+
+hipError_t launch_im2col3(const uint16_t* in, int ld_in, int c0, int C, int batch, int gh, int gw, uint16_t* out,
+                          hipStream_t s) {
+  if (C % 8 || ld_in % 8 || c0 % 8 || c0 + C > ld_in || batch < 1 || gh < 1 || gw < 1) return hipErrorInvalidValue;
+  const size_t total = (size_t)batch * gh * gw * 9 * (C / 8);
+  hipLaunchKernelGGL(im2col3_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, in, ld_in, c0, C, batch,
+                     gh, gw, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_chan_ln(const float* x, int M, int C, const float* g, const float* b, float eps, bool silu,
+                          const float* g2, const float* b2, uint16_t* out, int ld_out, int c0, hipStream_t s) {
+  if (M < 1 || ld_out % 4 || c0 % 4 || c0 + C > ld_out) return hipErrorInvalidValue;
+  if (C == 256) {
+    const int rows_per_block = 4 * (64 / 64);
+    hipLaunchKernelGGL(chan_ln_kernel<256>, dim3((M + rows_per_block - 1) / rows_per_block), dim3(256), 0, s, x, M,
+                       g, b, eps, silu, g2, b2, out, ld_out, c0);
+  } else if (C == 128) {
+    const int rows_per_block = 4 * (64 / 32);
+    hipLaunchKernelGGL(chan_ln_kernel<128>, dim3((M + rows_per_block - 1) / rows_per_block), dim3(256), 0, s, x, M,
+                       g, b, eps, silu, g2, b2, out, ld_out, c0);
+  } else if (C == 64) {
+    const int rows_per_block = 4 * (64 / 16);
+    hipLaunchKernelGGL(chan_ln_kernel<64>, dim3((M + rows_per_block - 1) / rows_per_block), dim3(256), 0, s, x, M,
+                       g, b, eps, silu, g2, b2, out, ld_out, c0);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_groupnorm_gelu(const float* x, int batch, int P, int C, int groups, const float* g, const float* b,
+                                 float eps, uint16_t* out, hipStream_t s) {
+  if (groups < 1 || C != 8 * groups || batch < 1 || batch > 65535 || P < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(groupnorm_gelu_kernel, dim3(groups, batch), dim3(256), 0, s, x, P, C, g, b, eps, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_resize_nchw(const float* in, int ldi, int classes, int batch, int gh, int gw, float* out, int H,
+                              int W, hipStream_t s) {
+  if (classes < 1 || ldi < classes || batch < 1 || batch > 65535 || H < 1 || H > 65535 || W < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(resize_nchw_kernel, dim3((W + 255) / 256, H, batch), dim3(256), 0, s, in, ldi, classes, gh, gw,
+                     out, H, W);
+  return hipGetLastError();
+}
+
+}  // namespace vit

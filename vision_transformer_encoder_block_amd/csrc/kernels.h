@@ -97,6 +97,25 @@ size_t attention_workspace_bytes(int batch, int tokens, int heads);
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
                             int heads, int nv, uint16_t* o, float* work, size_t work_bytes, hipStream_t s);
 
+// ---- semantic head (channels-last activations, one row per pixel)
+// Taps [batch, ntaps, D, P] fp32 (channel-first) -> out bf16 [batch * P, ntaps * D].
+hipError_t launch_taps_cl(const float* taps, int batch, int ntaps, int D, int P, uint16_t* out, hipStream_t s);
+// 3x3 / pad-1 patches of channels c0 .. c0 + C of in [batch * gh * gw, ld_in] bf16
+// into out [batch * gh * gw, 9 * C] bf16, columns in (ky, kx, c) order.
+hipError_t launch_im2col3(const uint16_t* in, int ld_in, int c0, int C, int batch, int gh, int gw, uint16_t* out,
+                          hipStream_t s);
+// Channel LayerNorm of rows of x [M, C] fp32 (C = 64, 128 or 256), then SiLU if
+// `silu`, then a second LayerNorm if g2 != null; bf16 into out + m * ld_out + c0.
+hipError_t launch_chan_ln(const float* x, int M, int C, const float* g, const float* b, float eps, bool silu,
+                          const float* g2, const float* b2, uint16_t* out, int ld_out, int c0, hipStream_t s);
+// GroupNorm (C = 8 * groups) of x [batch * P, C] fp32 per image, affine, exact GELU -> bf16 [batch * P, C].
+hipError_t launch_groupnorm_gelu(const float* x, int batch, int P, int C, int groups, const float* g, const float* b,
+                                 float eps, uint16_t* out, hipStream_t s);
+// Bilinear resize (half-pixel centres) of class-minor in [batch * gh * gw, ldi]
+// to out [batch, classes, H, W] fp32.
+hipError_t launch_resize_nchw(const float* in, int ldi, int classes, int batch, int gh, int gw, float* out, int H,
+                              int W, hipStream_t s);
+
 // fp32 -> bf16 (nearest even) of n values.
 hipError_t launch_to_bf16(const float* x, size_t n, uint16_t* y, hipStream_t s);
 

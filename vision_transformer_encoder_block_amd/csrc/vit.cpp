@@ -11,6 +11,7 @@
 #include <string>
 #include <vector>
 
+#include "host_error.h"
 #include "kernels.h"
 #include "vit.h"
 #include "vit_ops.h"
@@ -714,3 +715,7 @@ int vit_op_attention(const void* q, const void* k, const void* vt, int batch, in
 }
 
 }  // extern "C"
+
+namespace vit {
+int report_error(int code, const std::string& msg) { return fail(code, msg); }
+}  // namespace vit
