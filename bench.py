@@ -314,6 +314,47 @@ KERNEL_NAMES = {
 }
 
 
+def head_flops(hcfg, batch: int) -> float:
+    """Algorithmic FLOP of the semantic head (2 per multiply-add over its convs)."""
+    M = batch * hcfg.grid_h * hcfg.grid_w
+    W, H2, T, C = hcfg.width, hcfg.width // 2, hcfg.taps * hcfg.dim, hcfg.classes
+    macs = T * W + 6 * 9 * H2 * H2 + 5 * H2 * W + W * W + 9 * W * W + W * C
+    return 2.0 * M * macs
+
+
+def bench_head(steps=30, warmup=5):
+    """DINOv2-S/14 @518 batch 8: the encoder with its four taps, then the LibreYOLO
+    DINOv2 semantic head (projector P4 + task head, logits resized to 518 x 518)."""
+    import torch
+    import synth
+    import vision_transformer_encoder_block_amd as vit
+    cfg = synth.preset("vits14_518")
+    B = 8
+    enc = vit.Encoder(cfg, synth.make_params(cfg), max_batch=B)
+    hcfg = vit.head_config_preset()
+    head = vit.SemanticHead(hcfg, synth.make_head_params(cfg))
+    x = torch.from_numpy(synth.make_images(cfg, B)).cuda()
+    tok = torch.empty((B, enc.tokens, cfg["dim"]), dtype=torch.float32, device="cuda")
+    taps = torch.empty((B, 4, cfg["dim"], 37, 37), dtype=torch.float32, device="cuda")
+    logits = torch.empty((B, hcfg.classes, hcfg.out_h, hcfg.out_w), dtype=torch.float32, device="cuda")
+
+    def both():
+        enc.forward(x, with_taps=True, tokens_out=tok, taps_out=taps)
+        head.forward(taps, logits_out=logits)
+
+    ms_all, _ = time_gpu(both, steps, warmup)
+    ms_head, _ = time_gpu(lambda: head.forward(taps, logits_out=logits), steps, warmup)
+    torch.cuda.synchronize()
+    assert torch.isfinite(logits).all().item(), "non-finite logits"
+    fl = head_flops(hcfg, B)
+    tf = fl / (ms_head * 1e-3) / 1e12
+    head.close()
+    enc.close()
+    return {"workload": "DINOv2-S/14 @518 b8, taps 3/6/9/12 -> semantic head -> 19 x 518 x 518 logits",
+            "images_per_s": B / (ms_all * 1e-3), "ms_per_step": ms_all, "head_ms": ms_head,
+            "head_gflop": fl / 1e9, "head_tflops": tf, "head_pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,6 +364,8 @@ def main():
     ap.add_argument("--no-large", action="store_true", help="skip the ViT-L/16 @1024 b1 line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (for scaling HBM counters)")
+    ap.add_argument("--head-only", action="store_true",
+                    help="run only the semantic-head leg (DINOv2-S/14 @518 b8 + head) and print its JSON")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: turn two rocprofv3 --pmc CSVs into profiles/hbm_traffic.json")
     args = ap.parse_args()
@@ -336,6 +379,9 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
 
+    if args.head_only:
+        print(json.dumps(bench_head(args.steps, args.warmup)), flush=True)
+        return
     if args.copy_calibration:
         copy_calibration()
     log("ViT-S/16 @336 b32 ...")
@@ -351,6 +397,9 @@ def main():
     log("frame preprocessing ...")
     pre = bench_preprocess()
     log(json.dumps(pre))
+    log("semantic head ...")
+    hd = bench_head()
+    log(json.dumps(hd))
     log("kernel breakdown ...")
     bd = kernel_breakdown(cfg, 32)
     for n, b in bd.items():
@@ -383,6 +432,7 @@ def main():
                                  "eager_images_per_s": large["eager_images_per_s"],
                                  "tflops": large["tflops"], "pct_bf16_peak": 100 * large["frac_bf16_peak"]}
     out["preprocess"] = pre
+    out["semantic_head"] = hd
     if not args.no_cpu:
         log("CPU oracle baseline ...")
         out["cpu_baseline"] = cpu_baseline()

@@ -19,7 +19,6 @@ import synth
 import vision_transformer_encoder_block_amd as vit
 from gpu_util import f32_dev, host, require_gpu, say
 from oracle import head_oracle as H
-from oracle import vit_oracle as O
 
 pytestmark = pytest.mark.gpu
 

@@ -382,10 +382,28 @@ __device__ __forceinline__ int swz_k(int r, int c) {
   else return c ^ (r & 15);
 }
 
-template <int BM, int BN, int BKT, int WGM, int WGN, int S, class Epi>
+// Addressing of the A operand.  Linear: row m of A holds its K values
+// contiguously (A is [M, K]).
+struct AMapLinear {
+  static constexpr bool kConv = false;
+};
+// 3x3 / stride 1 / zero padding 1 convolution read in place (implicit GEMM):
+// column k = (ky * 3 + kx) * C + c of row m, the pixel (y, x) of image b on a
+// gh x gw grid, is in[(b * gh * gw + (y + ky - 1) * gw + x + kx - 1) * ld + c0 + c],
+// and zero where that pixel lies outside the grid.  C is a multiple of the K
+// step, so every step reads one tap; outside pixels get an offset past the
+// end of the buffer, which the range check of the direct-to-LDS load turns
+// into zeros.
+struct AMapConv3 {
+  static constexpr bool kConv = true;
+  int gh, gw, ld, c0, C;
+  uint32_t bytes;  // size of `in` in bytes
+};
+
+template <int BM, int BN, int BKT, int WGM, int WGN, int S, class Epi, class AM = AMapLinear>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t* __restrict__ A,
                                                                   const bf16_t* __restrict__ W, int M, int N, int K,
-                                                                  int tiles_m, int tiles_n, Epi epi) {
+                                                                  int tiles_m, int tiles_n, Epi epi, AM am = {}) {
   constexpr int NW = WGM * WGN;                     // waves per workgroup
   constexpr int WTM = BM / WGM, WTN = BN / WGN;     // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;       // 32x32 blocks per wave
@@ -411,7 +429,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const int32x4 ra_src = make_rsrc_words(A, (uint32_t)((size_t)M * K * 2));
+  static_assert(!AM::kConv || A_SPLIT, "implicit convolution needs whole A instructions per wave");
+  uint32_t a_bytes = (uint32_t)((size_t)M * K * 2);
+  if constexpr (AM::kConv) a_bytes = am.bytes;
+  const int32x4 ra_src = make_rsrc_words(A, a_bytes);
   const int32x4 rb_src = make_rsrc_words(W, (uint32_t)((size_t)N * K * 2));
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   if constexpr (HasPrologue<Epi>::value) epi.prologue(wave_u, lane, NW);
@@ -419,6 +440,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   // instructions; instruction k fills LDS bytes [1024 k, 1024 (k + 1)) of the
   // stage (A's BM rows first, so W's rows start at BM * BKT * 2 = 1024 A_INS)
   uint32_t g_off[LHI];
+  // implicit convolution: the A row's image offset (b * gh * gw) and pixel
+  // (y, x); rows past M get a y that no tap brings inside the grid
+  constexpr int A_PER_WAVE = AM::kConv ? A_INS / NW : 0;
+  int cpb[A_PER_WAVE > 0 ? A_PER_WAVE : 1], cy[A_PER_WAVE > 0 ? A_PER_WAVE : 1], cx[A_PER_WAVE > 0 ? A_PER_WAVE : 1];
   {
     const int sub = lane / CPR, pc = lane % CPR;
 #pragma unroll
@@ -427,16 +452,45 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
       const bool is_a = A_SPLIT ? i < A_INS / NW : k < A_INS;
       const int row = (is_a ? k : k - A_INS) * RPI + sub;
       g_off[i] = (uint32_t)((is_a ? m0 : n0) + row) * (uint32_t)K * 2u + (uint32_t)swz_k<BKT>(row, pc) * 16u;
+      if constexpr (AM::kConv) {
+        if (i < A_PER_WAVE) {
+          const int m = m0 + row;
+          const int P = am.gh * am.gw;
+          const int b = m / P, pix = m - b * P;
+          cpb[i] = b * P;
+          cy[i] = m < M ? pix / am.gw : -4;
+          cx[i] = pix - (pix / am.gw) * am.gw;
+          g_off[i] = (uint32_t)swz_k<BKT>(row, pc) * 16u;  // chunk within the step
+        }
+      }
     }
   }
   auto issue = [&](auto stage, int kt) {
     const uint32_t blk = lds_addr(stage_lds<STAGE_BYTES, decltype(stage)::value>());
     const uint32_t koff = (uint32_t)kt * (BKT * 2);
+    int ky = 0, kx = 0, cbase = 0;
+    if constexpr (AM::kConv) {
+      const int kel = kt * BKT;
+      const int tap = kel / am.C;
+      ky = tap / 3 - 1;
+      kx = tap - 3 * (tap / 3) - 1;
+      cbase = am.c0 + kel - tap * am.C;
+    }
 #pragma unroll
     for (int i = 0; i < LHI; ++i) {
       const int k = i * NW + wave_u;
       if (LHI == L || k < TOT) {  // wave-uniform
         const bool is_a = A_SPLIT ? i < A_INS / NW : k < A_INS;
+        if constexpr (AM::kConv) {
+          if (i < A_PER_WAVE) {
+            const int y = cy[i] + ky, x = cx[i] + kx;
+            const bool in = (unsigned)y < (unsigned)am.gh && (unsigned)x < (unsigned)am.gw;
+            const uint32_t off =
+                in ? (uint32_t)((cpb[i] + y * am.gw + x) * am.ld + cbase) * 2u + g_off[i] : 0x80000000u;
+            dma16(ra_src, off, blk + (uint32_t)k * 1024u);
+            continue;
+          }
+        }
         dma16(is_a ? ra_src : rb_src, g_off[i] + koff, blk + (uint32_t)k * 1024u);
       }
     }
@@ -687,12 +741,12 @@ struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, S = S_;
 };
 
-template <class C, class Epi>
-hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
+template <class C, class Epi, class AM = AMapLinear>
+hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s, AM am = {}) {
   const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
   if (K % C::BK != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<C::BM, C::BN, C::BK, C::WGM, C::WGN, C::S, Epi>), dim3(tiles_m * tiles_n),
-                     dim3(64 * C::WGM * C::WGN), 0, s, A, W, M, N, K, tiles_m, tiles_n, epi);
+  hipLaunchKernelGGL((gemm_bf16_kernel<C::BM, C::BN, C::BK, C::WGM, C::WGN, C::S, Epi, AM>), dim3(tiles_m * tiles_n),
+                     dim3(64 * C::WGM * C::WGN), 0, s, A, W, M, N, K, tiles_m, tiles_n, epi, am);
   return hipGetLastError();
 }
 
@@ -703,13 +757,23 @@ hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi&
 using CfgMid = Cfg<128, 128, 64, 2, 2, 2>;
 using CfgSmall = Cfg<64, 128, 64, 2, 2, 2>;
 using CfgBig = Cfg<256, 256, 64, 2, 4, 2>;
+using CfgTiny = Cfg<64, 64, 64, 2, 2, 2>;
 
-template <class Epi>
-hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
+template <class Epi, class AM = AMapLinear>
+hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s,
+                    AM am = {}) {
   const long mid_tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if ((long)M * N >= 32L * 1024 * 1024) return run<CfgBig>(A, W, M, N, K, epi, s);
-  if (K <= 512 && mid_tiles < 512) return run<CfgSmall>(A, W, M, N, K, epi, s);
-  return run<CfgMid>(A, W, M, N, K, epi, s);
+  if ((long)M * N >= 32L * 1024 * 1024) return run<CfgBig>(A, W, M, N, K, epi, s, am);
+#ifndef SKINNY_RULE
+#define SKINNY_RULE 2
+#endif
+  if (SKINNY_RULE > 0 && mid_tiles < 256) {  // fewer 128 x 128 tiles than compute units
+    const long small_tiles = (long)((M + 63) / 64) * ((N + 127) / 128);
+    if (SKINNY_RULE == 1 || small_tiles >= 256) return run<CfgSmall>(A, W, M, N, K, epi, s, am);
+    return run<CfgTiny>(A, W, M, N, K, epi, s, am);
+  }
+  if (K <= 512 && mid_tiles < 512) return run<CfgSmall>(A, W, M, N, K, epi, s, am);
+  return run<CfgMid>(A, W, M, N, K, epi, s, am);
 }
 
 // Phi table of the GELU epilogue: built once per device (synchronous copy to
@@ -805,6 +869,31 @@ hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, int M, int N, int K
     }
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_conv3(const uint16_t* in, int ld_in, int c0, int C, int batch, int gh, int gw,
+                             const uint16_t* W, int N, const EpiParams& ep, hipStream_t s) {
+  if (C <= 0 || C % BK || c0 < 0 || c0 % 8 || ld_in % 8 || c0 + C > ld_in || batch < 1 || gh < 1 || gw < 1 || N <= 0)
+    return hipErrorInvalidValue;
+  const size_t M = (size_t)batch * gh * gw, K = (size_t)9 * C;
+  const size_t bytes = M * ld_in * 2;
+  if (bytes >= (1ull << 31) || (M + 128) * K * 2 >= (1ull << 32) || (size_t)(N + 128) * K * 2 >= (1ull << 32))
+    return hipErrorInvalidValue;  // 32-bit buffer offsets; 0x80000000 marks the zero padding
+  auto al = [](const void* p, size_t n) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % n == 0; };
+  const bool par16 = N % 4 == 0 && al(ep.bias, 16);
+  const AMapConv3 am{gh, gw, ld_in, c0, C, (uint32_t)bytes};
+  switch (ep.kind) {
+    case EPI_BIAS_BF16: {
+      const bool vec = ep.ldc % 4 == 0 && par16 && al(ep.out, 8);
+      return dispatch(in, W, (int)M, N, (int)K, EpiBiasBf16{ep.bias, (bf16_t*)ep.out, ep.ldc, vec}, s, am);
+    }
+    case EPI_BIAS_F32: {
+      const bool vec = ep.ldc % 4 == 0 && par16 && al(ep.out, 16);
+      return dispatch(in, W, (int)M, N, (int)K, EpiBiasF32{ep.bias, (float*)ep.out, ep.ldc, vec}, s, am);
+    }
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace vit

@@ -1,7 +1,8 @@
 // Host runtime and C ABI of the semantic head on the encoder's taps: config
 // validation, buffer planning, weight packing (fp32 blob -> bf16 GEMM
-// operands with 3x3 kernels reordered to (ky, kx, c) columns, fp32 vectors)
-// and the launch sequence on the caller's stream.  Like the encoder, the head
+// operands with 3x3 kernels reordered to (ky, kx, c) columns, the column
+// order of the implicit-GEMM convolution; fp32 vectors) and the launch
+// sequence on the caller's stream.  Like the encoder, the head
 // never allocates device memory.
 #include <hip/hip_runtime.h>
 
@@ -51,7 +52,7 @@ struct HeadPlan {
       pred_b, wtotal;
   size_t bn_w[kBottlenecks][2], bn_g[kBottlenecks][2], bn_b[kBottlenecks][2];
   // workspace (byte offsets)
-  size_t x0, f, y, t, col, p4, lat, g, grid, stotal;
+  size_t x0, f, y, t, p4, lat, g, grid, stotal;
 };
 
 int validate(const vit_head_config* c) {
@@ -122,7 +123,6 @@ int build_plan(const vit_head_config* c, HeadPlan& pl) {
   pl.f = take(M * W * 4);
   pl.y = take(M * 5 * H2 * 2);
   pl.t = take(M * H2 * 2);
-  pl.col = take(M * 9 * W * 2);
   pl.p4 = take(M * W * 2);
   pl.lat = take(M * W * 2);
   pl.g = take(M * W * 2);
@@ -247,16 +247,23 @@ int vit_head_forward(vit_head* h, const float* d_taps, int batch, float* d_logit
   char* s = h->s;
   auto bf = [](char* p, size_t at) { return reinterpret_cast<uint16_t*>(p + at); };
   auto f32 = [](char* p, size_t at) { return reinterpret_cast<float*>(p + at); };
-  uint16_t *x0 = bf(s, pl.x0), *y = bf(s, pl.y), *t = bf(s, pl.t), *col = bf(s, pl.col), *p4 = bf(s, pl.p4),
-           *lat = bf(s, pl.lat), *g = bf(s, pl.g);
+  uint16_t *x0 = bf(s, pl.x0), *y = bf(s, pl.y), *t = bf(s, pl.t), *p4 = bf(s, pl.p4), *lat = bf(s, pl.lat),
+           *g = bf(s, pl.g);
   float *f = f32(s, pl.f), *grid = f32(s, pl.grid);
-  auto gemm_f32 = [&](const uint16_t* a, size_t wo, int N, int K, const float* bias, float* outp) {
+  auto f32_out = [&](const float* bias, float* outp, int N) {
     vit::EpiParams ep;
     ep.kind = vit::EPI_BIAS_F32;
     ep.bias = bias;
     ep.out = outp;
     ep.ldc = N;
-    return vit::launch_gemm(a, bf(w, wo), M, N, K, ep, st);
+    return ep;
+  };
+  auto gemm_f32 = [&](const uint16_t* a, size_t wo, int N, int K, const float* bias, float* outp) {
+    return vit::launch_gemm(a, bf(w, wo), M, N, K, f32_out(bias, outp, N), st);
+  };
+  // 3x3 / pad 1 conv of channels c0 .. c0 + Cin of a channels-last buffer (implicit GEMM)
+  auto conv3_f32 = [&](const uint16_t* in, int ld, int c0, int Cin, size_t wo, int N, const float* bias, float* outp) {
+    return vit::launch_gemm_conv3(in, ld, c0, Cin, batch, c.grid_h, c.grid_w, bf(w, wo), N, f32_out(bias, outp, N), st);
   };
 
   // Projector P4
@@ -267,13 +274,11 @@ int vit_head_forward(vit_head* h, const float* d_taps, int batch, float* d_logit
            "projector LayerNorm");
   for (int i = 0; i < kBottlenecks; ++i) {
     // input: b (channels H2 .. 2 H2) for the first, then the previous output
-    HEAD_HIP(vit::launch_im2col3(y, ldy, H2 * (i + 1), H2, batch, c.grid_h, c.grid_w, col, st), "bottleneck im2col");
-    HEAD_HIP(gemm_f32(col, pl.bn_w[i][0], H2, 9 * H2, nullptr, f), "bottleneck conv 1");
+    HEAD_HIP(conv3_f32(y, ldy, H2 * (i + 1), H2, pl.bn_w[i][0], H2, nullptr, f), "bottleneck conv 1");
     HEAD_HIP(vit::launch_chan_ln(f, M, H2, f32(w, pl.bn_g[i][0]), f32(w, pl.bn_b[i][0]), c.ln_eps, true, nullptr,
                                  nullptr, t, H2, 0, st),
              "bottleneck LayerNorm 1");
-    HEAD_HIP(vit::launch_im2col3(t, H2, 0, H2, batch, c.grid_h, c.grid_w, col, st), "bottleneck im2col");
-    HEAD_HIP(gemm_f32(col, pl.bn_w[i][1], H2, 9 * H2, nullptr, f), "bottleneck conv 2");
+    HEAD_HIP(conv3_f32(t, H2, 0, H2, pl.bn_w[i][1], H2, nullptr, f), "bottleneck conv 2");
     HEAD_HIP(vit::launch_chan_ln(f, M, H2, f32(w, pl.bn_g[i][1]), f32(w, pl.bn_b[i][1]), c.ln_eps, true, nullptr,
                                  nullptr, y, ldy, H2 * (i + 2), st),
              "bottleneck LayerNorm 2");
@@ -291,8 +296,7 @@ int vit_head_forward(vit_head* h, const float* d_taps, int batch, float* d_logit
     ep.ldc = W;
     HEAD_HIP(vit::launch_gemm(p4, bf(w, pl.lat_w), M, W, W, ep, st), "lateral conv");
   }
-  HEAD_HIP(vit::launch_im2col3(lat, W, 0, W, batch, c.grid_h, c.grid_w, col, st), "smoothing im2col");
-  HEAD_HIP(gemm_f32(col, pl.sm_w, W, 9 * W, f32(w, pl.sm_b), f), "smoothing conv");
+  HEAD_HIP(conv3_f32(lat, W, 0, W, pl.sm_w, W, f32(w, pl.sm_b), f), "smoothing conv");
   HEAD_HIP(vit::launch_groupnorm_gelu(f, batch, pl.P, W, c.groups, f32(w, pl.gn_g), f32(w, pl.gn_b), c.gn_eps, g, st),
            "GroupNorm + GELU");
   HEAD_HIP(gemm_f32(g, pl.pred_w, C, W, f32(w, pl.pred_b), grid), "predict conv");

@@ -2,10 +2,10 @@
 // diagram, "Projector P4", "Projector Bottleneck", "Projector output ConvX",
 // "Task head").  Activations live channels-last, one row per pixel
 // ([batch * gh * gw, C]), so 1x1 convs are plain GEMMs on the MFMA kernel and
-// 3x3 convs are an im2col here followed by the same GEMM.  What remains here
-// is the data movement and the per-pixel / per-group normalisations:
+// 3x3 convs are implicit GEMMs on it (the A loads gather the 3x3
+// neighbourhood in place).  What remains here is the data movement and the
+// per-pixel / per-group normalisations:
 //   taps_cl_kernel        channel-first fp32 taps -> channels-last bf16 concat
-//   im2col3_kernel        3x3 / pad 1 patches of a channels-last slice
 //   chan_ln_kernel        channel LayerNorm (+ SiLU) (+ a second LayerNorm)
 //   groupnorm_gelu_kernel GroupNorm over (channels of a group x pixels) + GELU
 //   resize_nchw_kernel    bilinear resize of class-minor logits to [B, C, H, W]
@@ -45,27 +45,6 @@ __global__ __launch_bounds__(256) void taps_cl_kernel(const float* __restrict__ 
       *reinterpret_cast<uint4*>(out + ((size_t)b * P + p0 + pl) * ldo + t * D + c0 + c) = u;
     }
   }
-}
-
-// out[m, (ky * 3 + kx) * C + c] = in[pixel (y + ky - 1, x + kx - 1) of image b, c0 + c],
-// zero outside the grid.  One thread per 8 channels of one (pixel, tap).
-__global__ __launch_bounds__(256) void im2col3_kernel(const uint16_t* __restrict__ in, int ld_in, int c0, int C,
-                                                      int batch, int gh, int gw, uint16_t* __restrict__ out) {
-  const int chunks = C / 8;
-  const size_t total = (size_t)batch * gh * gw * 9 * chunks;
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int ch = (int)(idx % chunks);
-  const size_t mk = idx / chunks;
-  const int k = (int)(mk % 9);
-  const size_t m = mk / 9;
-  const int P = gh * gw;
-  const int b = (int)(m / P), pix = (int)(m - (size_t)b * P);
-  const int y = pix / gw + k / 3 - 1, x = pix % gw + k % 3 - 1;
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (y >= 0 && y < gh && x >= 0 && x < gw)
-    v = *reinterpret_cast<const uint4*>(in + ((size_t)b * P + y * gw + x) * ld_in + c0 + ch * 8);
-  *reinterpret_cast<uint4*>(out + m * (size_t)(9 * C) + k * C + ch * 8) = v;
 }
 
 // Channel LayerNorm of rows of x [M, C] (C / 4 lanes per row, one float4
@@ -158,12 +137,13 @@ __global__ __launch_bounds__(256) void groupnorm_gelu_kernel(const float* __rest
 
 // Bilinear resize (half-pixel centres, exact rational taps, clamped) of
 // class-minor logits in [batch * gh * gw, ldi] to out [batch, classes, H, W];
-// one thread per output pixel, looping over the classes.
+// one thread per output pixel (flat index over H * W), looping over the
+// classes; consecutive threads write consecutive pixels of each class plane.
 __global__ __launch_bounds__(256) void resize_nchw_kernel(const float* __restrict__ in, int ldi, int classes, int gh,
                                                           int gw, float* __restrict__ out, int H, int W) {
-  const int x = blockIdx.x * blockDim.x + threadIdx.x;
-  if (x >= W) return;
-  const int y = blockIdx.y, b = blockIdx.z;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= H * W) return;
+  const int y = i / W, x = i - y * W, b = blockIdx.y;
   int y0, y1, x0, x1;
   float ly, lx;
   bilinear_tap(y, gh, H, y0, y1, ly);
@@ -173,11 +153,24 @@ __global__ __launch_bounds__(256) void resize_nchw_kernel(const float* __restric
   const float* r01 = base + (size_t)(y0 * gw + x1) * ldi;
   const float* r10 = base + (size_t)(y1 * gw + x0) * ldi;
   const float* r11 = base + (size_t)(y1 * gw + x1) * ldi;
-  float* o = out + (size_t)b * classes * H * W + (size_t)y * W + x;
-  for (int c = 0; c < classes; ++c) {
+  float* o = out + (size_t)b * classes * H * W + i;
+  const size_t plane = (size_t)H * W;
+  int c = 0;
+  for (; c + 4 <= classes; c += 4) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float top = (1.f - lx) * r00[c + j] + lx * r01[c + j];
+      const float bot = (1.f - lx) * r10[c + j] + lx * r11[c + j];
+      v[j] = (1.f - ly) * top + ly * bot;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[(c + j) * plane] = v[j];
+  }
+  for (; c < classes; ++c) {
     const float top = (1.f - lx) * r00[c] + lx * r01[c];
     const float bot = (1.f - lx) * r10[c] + lx * r11[c];
-    o[(size_t)c * H * W] = (1.f - ly) * top + ly * bot;
+    o[c * plane] = (1.f - ly) * top + ly * bot;
   }
 }
 
@@ -187,15 +180,6 @@ hipError_t launch_taps_cl(const float* taps, int batch, int ntaps, int D, int P,
   if (batch < 1 || ntaps < 1 || D % 64 || P < 1 || (long)batch * ntaps > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(taps_cl_kernel, dim3((P + 63) / 64, D / 64, batch * ntaps), dim3(256), 0, s, taps, ntaps, D, P,
                      out);
-  return hipGetLastError();
-}
-
-hipError_t launch_im2col3(const uint16_t* in, int ld_in, int c0, int C, int batch, int gh, int gw, uint16_t* out,
-                          hipStream_t s) {
-  if (C % 8 || ld_in % 8 || c0 % 8 || c0 + C > ld_in || batch < 1 || gh < 1 || gw < 1) return hipErrorInvalidValue;
-  const size_t total = (size_t)batch * gh * gw * 9 * (C / 8);
-  hipLaunchKernelGGL(im2col3_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, in, ld_in, c0, C, batch,
-                     gh, gw, out);
   return hipGetLastError();
 }
 
@@ -229,9 +213,10 @@ hipError_t launch_groupnorm_gelu(const float* x, int batch, int P, int C, int gr
 
 hipError_t launch_resize_nchw(const float* in, int ldi, int classes, int batch, int gh, int gw, float* out, int H,
                               int W, hipStream_t s) {
-  if (classes < 1 || ldi < classes || batch < 1 || batch > 65535 || H < 1 || H > 65535 || W < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(resize_nchw_kernel, dim3((W + 255) / 256, H, batch), dim3(256), 0, s, in, ldi, classes, gh, gw,
-                     out, H, W);
+  if (classes < 1 || ldi < classes || batch < 1 || batch > 65535 || H < 1 || W < 1 || (long)H * W > (1L << 30))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(resize_nchw_kernel, dim3((unsigned)(((long)H * W + 255) / 256), batch), dim3(256), 0, s, in, ldi,
+                     classes, gh, gw, out, H, W);
   return hipGetLastError();
 }
 

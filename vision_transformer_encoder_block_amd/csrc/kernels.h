@@ -45,6 +45,13 @@ struct EpiParams {
 // Widths for which launch_gemm fuses the LayerNorm after a residual update.
 constexpr bool residual_ln_fusable(int n) { return n == 384; }
 
+// 3x3 / stride 1 / pad 1 convolution as an implicit GEMM: A rows are the
+// pixels of in [batch * gh * gw, ld_in] (channels c0 .. c0 + C, C a multiple
+// of 64), columns in (ky, kx, c) order, read in place with zeros outside the
+// grid; W [N, 9 C].  Epilogues EPI_BIAS_BF16 and EPI_BIAS_F32.
+hipError_t launch_gemm_conv3(const uint16_t* in, int ld_in, int c0, int C, int batch, int gh, int gw,
+                             const uint16_t* W, int N, const EpiParams& ep, hipStream_t s);
+
 // One-time per-device set-up of the GEMM epilogues (the GELU Phi table; a
 // synchronous copy).  launch_gemm does it on first use; encoders call it at
 // creation so that no later launch copies.
@@ -100,10 +107,6 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
 // ---- semantic head (channels-last activations, one row per pixel)
 // Taps [batch, ntaps, D, P] fp32 (channel-first) -> out bf16 [batch * P, ntaps * D].
 hipError_t launch_taps_cl(const float* taps, int batch, int ntaps, int D, int P, uint16_t* out, hipStream_t s);
-// 3x3 / pad-1 patches of channels c0 .. c0 + C of in [batch * gh * gw, ld_in] bf16
-// into out [batch * gh * gw, 9 * C] bf16, columns in (ky, kx, c) order.
-hipError_t launch_im2col3(const uint16_t* in, int ld_in, int c0, int C, int batch, int gh, int gw, uint16_t* out,
-                          hipStream_t s);
 // Channel LayerNorm of rows of x [M, C] fp32 (C = 64, 128 or 256), then SiLU if
 // `silu`, then a second LayerNorm if g2 != null; bf16 into out + m * ld_out + c0.
 hipError_t launch_chan_ln(const float* x, int M, int C, const float* g, const float* b, float eps, bool silu,
