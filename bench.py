@@ -219,15 +219,20 @@ def traffic_for(op):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
+def _cpu_threads():
+    """Threads NumPy's BLAS actually uses (the oracle's matrix products)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(budget_s=15.0, max_images=128):
     """The oracle (float64 NumPy), untuned, on ViT-S/16 @336 images until the budget is spent."""
     import synth
     from oracle import vit_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    cores = _cpu_threads()
     cfg = synth.preset("vits16_336")
     P = synth.make_params(cfg)
     x = synth.make_images(cfg, max_images)
@@ -350,9 +355,35 @@ def bench_head(steps=30, warmup=5):
     tf = fl / (ms_head * 1e-3) / 1e12
     head.close()
     enc.close()
+    # the head's dominant kernel: a Bottleneck 3x3 conv (implicit GEMM), timed alone
+    M, H2 = B * 37 * 37, hcfg.width // 2
+    xin = torch.randn(M, 5 * H2, device="cuda").to(torch.bfloat16)
+    wk = (torch.randn(H2, 9 * H2, device="cuda") * 0.05).to(torch.bfloat16)
+    cout = torch.empty(M, H2, device="cuda")
+    ms_conv, _ = time_gpu(lambda: vit.vit_op_conv3x3(xin, 5 * H2, H2, H2, B, 37, 37, wk, None, H2, cout), steps, warmup)
+    conv_tf = 2.0 * M * H2 * 9 * H2 / (ms_conv * 1e-3) / 1e12
     return {"workload": "DINOv2-S/14 @518 b8, taps 3/6/9/12 -> semantic head -> 19 x 518 x 518 logits",
             "images_per_s": B / (ms_all * 1e-3), "ms_per_step": ms_all, "head_ms": ms_head,
-            "head_gflop": fl / 1e9, "head_tflops": tf, "head_pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS}
+            "head_gflop": fl / 1e9, "head_tflops": tf, "head_pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS,
+            "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel<64, 64, ..., EpiBiasF32, AMapConv3> "
+                         "(Bottleneck 3x3 conv, M = 10952, N = 128, K = 1152)", "achieved": conv_tf,
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": conv_tf / PEAK_BF16_TFLOPS,
+                         "avg_launch_us": ms_conv * 1e3, "traffic": None}}
+
+
+def head_cpu_baseline(images=8):
+    """The head's oracle (float64 NumPy), untuned, on DINOv2-S/14 @518 stand-in taps."""
+    import synth
+    from oracle import head_oracle as H
+    cfg = synth.preset("vits14_518")
+    Ph = synth.make_head_params(cfg)
+    taps = synth.make_taps(cfg, images)
+    t0 = time.perf_counter()
+    for b in range(images):
+        H.semantic_head(taps[b], Ph, 518, 518)
+    dt = time.perf_counter() - t0
+    return {"value": images / dt, "unit": "images/s", "cores": _cpu_threads(), "kind": "oracle",
+            "sample": f"{images} images of 4 x 384 x 37 x 37 taps through the float64 head oracle, {dt:.1f} s"}
 
 
 def main():
@@ -432,6 +463,8 @@ def main():
                                  "eager_images_per_s": large["eager_images_per_s"],
                                  "tflops": large["tflops"], "pct_bf16_peak": 100 * large["frac_bf16_peak"]}
     out["preprocess"] = pre
+    if not args.no_cpu:
+        hd["cpu_baseline"] = head_cpu_baseline()
     out["semantic_head"] = hd
     if not args.no_cpu:
         log("CPU oracle baseline ...")

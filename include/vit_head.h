@@ -97,6 +97,22 @@ int vit_head_forward(vit_head* h, const float* d_taps, int batch, float* d_logit
 /* Release the host-side handle (device buffers belong to the caller). */
 int vit_head_destroy(vit_head* h);
 
+/* One 3x3 / stride 1 / zero-padding 1 convolution of the head (diagram,
+ * "Projector Bottleneck" and the task head's smoothing conv) as an implicit
+ * GEMM on channels-last bf16 activations:
+ *   out[m, n] = bias[n] + sum_{ky, kx, c} w[n, (ky * 3 + kx) * cin + c] *
+ *               in[pixel (y + ky - 1, x + kx - 1) of image b, c0 + c]
+ * for row m = pixel (y, x) of image b on a gh x gw grid; terms whose pixel
+ * lies outside the grid are zero.
+ *   in   device bf16 [batch * gh * gw, ld_in], 16-byte aligned; channels c0 .. c0 + cin
+ *        (cin a positive multiple of 64, c0 and ld_in multiples of 8)
+ *   w    device bf16 [n_out, 9 * cin] (torch's [n_out, cin, 3, 3] with columns in (ky, kx, c) order)
+ *   bias device fp32 [n_out] or NULL (zero)
+ *   out  device fp32 [batch * gh * gw, n_out]
+ * Enqueue only. */
+int vit_op_conv3x3(const void* in, int ld_in, int c0, int cin, int batch, int gh, int gw, const void* w,
+                   const float* bias, int n_out, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

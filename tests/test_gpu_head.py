@@ -132,3 +132,39 @@ def test_head_rejects_bad_calls():
     head.close()
     with pytest.raises(vit.VitError):
         vit.SemanticHead(vit.head_config(4, 4, 8, 8, 2), np.zeros(10, np.float32))
+
+
+def _round_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("batch,gh,gw,ld,c0,cin,n_out,bias", [
+    (2, 5, 7, 640, 128, 128, 128, False),    # a Bottleneck input slice of the C2f concat
+    (1, 37, 37, 256, 0, 256, 256, True),     # the smoothing conv at the full grid
+    (3, 1, 1, 128, 0, 128, 64, True),        # every neighbour is padding
+    (2, 9, 4, 192, 64, 64, 19, False),       # ragged N
+])
+def test_conv3x3_matches_oracle(batch, gh, gw, ld, c0, cin, n_out, bias):
+    """vit_op_conv3x3 (implicit GEMM) against the oracle's convolution.  Inputs and
+    weights are bf16 values, so every product is exact in fp32 and the only error
+    is the fp32 sum of 9 cin terms: |err| <= 9 cin 2^-24 sum |w x| (+ the bias add)."""
+    require_gpu()
+    say(f"conv3x3 batch {batch} grid {gh}x{gw} ld {ld} c0 {c0} cin {cin} -> {n_out}")
+    rng = np.random.default_rng(gh * 100 + cin)
+    x = _round_bf16(rng.standard_normal((batch * gh * gw, ld)))
+    w4 = _round_bf16(rng.standard_normal((n_out, cin, 3, 3)) * 0.05)
+    b = torch.from_numpy(rng.standard_normal(n_out).astype(np.float32)) if bias else None
+    wk = w4.permute(0, 2, 3, 1).reshape(n_out, 9 * cin).contiguous()      # (ky, kx, c) columns
+    out = torch.empty((batch * gh * gw, n_out), device="cuda")
+    vit.vit_op_conv3x3(x.cuda(), ld, c0, cin, batch, gh, gw, wk.cuda(), None if b is None else b.cuda(), n_out, out)
+    got = host(out)
+    xs = x.double().numpy()[:, c0:c0 + cin].reshape(batch, gh, gw, cin).transpose(0, 3, 1, 2)
+    w64 = w4.double().numpy()
+    ref = np.stack([H.conv2d(xs[i], w64, None if b is None else b.double().numpy(), 1) for i in range(batch)])
+    ref = ref.transpose(0, 2, 3, 1).reshape(batch * gh * gw, n_out)
+    absref = np.stack([H.conv2d(np.abs(xs[i]), np.abs(w64), None, 1) for i in range(batch)])
+    absref = absref.transpose(0, 2, 3, 1).reshape(batch * gh * gw, n_out)
+    bound = 9 * cin * 2.0 ** -24 * absref + 2.0 ** -24 * np.abs(ref) + 1e-30
+    err = np.abs(got - ref)
+    say(f"max err / bound = {(err / bound).max():.3f}")
+    assert (err <= bound).all()

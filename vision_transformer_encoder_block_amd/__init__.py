@@ -25,6 +25,7 @@ __all__ = [
     "vit_op_attention_workspace", "vit_op_preprocess", "vit_op_linear_residual_ln",
     "Encoder", "EncoderGraph", "EPI_BIAS_BF16", "EPI_GELU_BF16", "EPI_RESIDUAL", "EPI_BIAS_F32",
     "HeadConfig", "HeadSizes", "head_config_preset", "head_config", "head_plan", "pack_head_params", "SemanticHead",
+    "vit_op_conv3x3",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvit.so")
@@ -92,6 +93,7 @@ _SIGNATURES = {
                              ctypes.POINTER(_P)]),
     "vit_head_forward": (_I, [_P, _P, _I, _P, _P, _P]),
     "vit_head_destroy": (_I, [_P]),
+    "vit_op_conv3x3": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
 }
 
 
@@ -383,6 +385,11 @@ _HEAD_ORDER = (["proj_w", "proj_ln_g", "proj_ln_b"]
 def pack_head_params(P: dict) -> np.ndarray:
     """Concatenate a head parameter dictionary into the fp32 blob order of vit_head_create."""
     return np.concatenate([np.ascontiguousarray(P[k], dtype=np.float32).ravel() for k in _HEAD_ORDER])
+
+
+def vit_op_conv3x3(x, ld_in, c0, cin, batch, gh, gw, w, bias, n_out, out, stream=None):
+    return _check("vit_op_conv3x3", lib().vit_op_conv3x3(_ptr(x), ld_in, c0, cin, batch, gh, gw, _ptr(w), _ptr(bias),
+                                                         n_out, _ptr(out), _stream(stream)))
 
 
 class SemanticHead:

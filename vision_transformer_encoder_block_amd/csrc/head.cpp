@@ -313,4 +313,22 @@ int vit_head_destroy(vit_head* h) {
   return VIT_OK;
 }
 
+int vit_op_conv3x3(const void* in, int ld_in, int c0, int cin, int batch, int gh, int gw, const void* w,
+                   const float* bias, int n_out, float* out, void* stream) {
+  if (!in || !w || !out) return report_error(VIT_ERR_ARG, "NULL pointer");
+  if (cin < 64 || cin % 64 || c0 < 0 || c0 % 8 || ld_in % 8 || c0 + cin > ld_in)
+    return report_error(VIT_ERR_SHAPE, "cin a positive multiple of 64, c0 and ld_in multiples of 8, c0 + cin <= ld_in");
+  if (batch < 1 || gh < 1 || gw < 1 || n_out < 1) return report_error(VIT_ERR_SHAPE, "batch, grid and n_out must be >= 1");
+  if ((uintptr_t)in % 16) return report_error(VIT_ERR_ARG, "in must be 16-byte aligned");
+  vit::EpiParams ep;
+  ep.kind = vit::EPI_BIAS_F32;
+  ep.bias = bias;
+  ep.out = out;
+  ep.ldc = n_out;
+  HEAD_HIP(vit::launch_gemm_conv3((const uint16_t*)in, ld_in, c0, cin, batch, gh, gw, (const uint16_t*)w, n_out, ep,
+                                  (hipStream_t)stream),
+           "conv3x3");
+  return VIT_OK;
+}
+
 }  // extern "C"
