@@ -1,0 +1,77 @@
+"""Pins of the fp8 (OCP E4M3) oracle (CPU only): the format's closed-form values,
+torch's float8_e4m3fn cast, brute force, and the saturation reading."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quant_oracle as Q
+
+
+def test_table_closed_forms():
+    t = Q.E4M3_TABLE
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0          # largest finite: 1.75 * 2^8
+    assert t[0x08] == 2.0 ** -6                            # smallest normal
+    assert t[0x01] == 2.0 ** -9                            # smallest subnormal: 1/8 * 2^-6
+    assert t[0x38] == 1.0                                  # exponent 7 = bias
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])         # the only NaNs; no infinity
+    assert np.isfinite(t).sum() == 254
+    assert (np.diff(t[:0x7F]) > 0).all()                   # codes 0..0x7E increase
+    np.testing.assert_array_equal(t[0x80:0xFF], -t[:0x7F])
+
+
+def test_codes_match_torch_float8_e4m3fn():
+    rng = np.random.default_rng(3)
+    vals = Q.E4M3_TABLE[:0x7F]
+    mids = (vals[:-1] + vals[1:]) / 2                      # exact ties between neighbours
+    x = np.concatenate([rng.standard_normal(20000) * 30, rng.standard_normal(5000) * 1e-3, vals, mids, -vals, -mids,
+                        [464.0, -464.0]]).astype(np.float32)
+    x = x[np.abs(x.astype(np.float64)) <= 464.0]           # torch turns larger magnitudes into NaN
+    got = Q.quantize_e4m3(x, 1.0)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_brute_force_nearest_with_ties_to_even():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(300).astype(np.float32) * 20
+    got = Q.quantize_e4m3(x, 1.0)
+    for xi, ci in zip(x, got):
+        best = min(range(0x7F), key=lambda c: (abs(Q.E4M3_TABLE[c] - abs(float(xi))), c & 1))
+        assert ci == (best | (0x80 if xi < 0 else 0))
+
+
+def test_saturation_sign_and_nan():
+    q = Q.quantize_e4m3(np.array([500.0, -1000.0, 1e30, -1e30, 449.0], np.float32), 1.0)
+    np.testing.assert_array_equal(q, [0x7E, 0xFE, 0x7E, 0xFE, 0x7E])
+    q = Q.quantize_e4m3(np.array([-0.0, -1e-9, 0.0, 1e-9, np.nan], np.float32), 1.0)
+    np.testing.assert_array_equal(q, [0x80, 0x80, 0x00, 0x00, 0x7F])
+
+
+def test_scale_product_is_rounded_in_float32():
+    # x * s_inv is formed in float32 before the code is chosen: here the exact
+    # product 3.6250000812 lies above the 3.5 / 3.75 midpoint (code 71), but its
+    # float32 rounding is the midpoint itself, which goes to the even code 70
+    x, s_inv = np.float32(0.38119414), np.float32(9.50959)
+    assert float(x) * float(s_inv) > 3.625 and np.float32(x * s_inv) == np.float32(3.625)
+    assert Q.quantize_e4m3(np.array([x]), s_inv)[0] == 70
+
+
+def test_round_trip_error_bound():
+    # normal range: |x - dequant(quant(x))| <= 2^-4 |x| (half a unit in the last place)
+    rng = np.random.default_rng(9)
+    x = (rng.uniform(2.0 ** -6, 448.0, 5000) * rng.choice([-1, 1], 5000)).astype(np.float32)
+    d = Q.dequantize_e4m3(Q.quantize_e4m3(x, 1.0), 1.0)
+    assert (np.abs(d - x) <= 2.0 ** -4 * np.abs(x)).all()
+
+
+def test_linear_fp8_brute_force():
+    rng = np.random.default_rng(11)
+    qa = rng.integers(0, 0x7F, (3, 5)).astype(np.uint8) | (rng.integers(0, 2, (3, 5)) * 0x80).astype(np.uint8)
+    qw = rng.integers(0, 0x7F, (2, 5)).astype(np.uint8)
+    b = rng.standard_normal(2)
+    y = Q.linear_fp8(qa, 0.5, qw, 0.25, b)
+    for m in range(3):
+        for n in range(2):
+            s = sum(Q.e4m3_value(int(qa[m, k])) * 0.5 * Q.e4m3_value(int(qw[n, k])) * 0.25 for k in range(5))
+            assert y[m, n] == pytest.approx(s + b[n], rel=1e-13, abs=1e-13)
