@@ -99,6 +99,34 @@ size_t vit_op_attention_workspace(int batch, int tokens, int heads);
 int vit_op_attention(const void* q, const void* k, const void* vt, int batch, int tokens, int heads,
                      void* o, void* work, size_t work_bytes, void* stream);
 
+/* ---- low-precision (fp8) linear layer -------------------------------------
+ * The encoder's Linear layers (LibreYOLO DINOv2 diagram, "Encoder block") with
+ * both operands in 8-bit floating point, the OCP E4M3 format gfx950's matrix
+ * cores read: 1 sign, 4 exponent (bias 7) and 3 mantissa bits; largest finite
+ * magnitude 448; codes 0x7F / 0xFF are NaN; no infinity.  The DINOv2
+ * deployment article discusses reduced-precision (INT8) engines; E4M3 is the
+ * 8-bit format of these matrix cores.  Scales are per tensor. */
+
+/* amax[0] = max_i |x[i]| (NaN ignored) over n values of x, fp32 (x_bf16 = 0)
+ * or bf16 (x_bf16 = 1); amax is a device float, overwritten. */
+int vit_op_absmax(const void* x, int x_bf16, size_t n, float* amax, void* stream);
+
+/* E4M3 codes: out[i] = E4M3(x[i] * s_inv), the product rounded to fp32 first,
+ * then the nearest E4M3 value with ties to the even mantissa, magnitudes past
+ * 448 (and infinities) saturated to +-448, the sign kept (also when the value
+ * rounds to zero), NaN -> 0x7F.  x fp32 or bf16 [n]; out uint8 [n], 4-byte
+ * aligned.  A per-tensor scale s = amax / 448 maps the largest magnitude to
+ * the largest code (s_inv = 1 / s). */
+int vit_op_quantize_fp8(const void* x, int x_bf16, size_t n, float s_inv, void* out, void* stream);
+
+/* out[m, n] = scale * sum_k A[m, k] W[n, k] + bias[n] with A [M, K] and W
+ * [N, K] E4M3 codes (uint8, row-major, K contiguous), scale = s_a * s_w the
+ * product of the operands' scales, bias [N] fp32 or NULL, out [M, N] fp32
+ * (out_f32 = 1) or bf16.  K must be a multiple of 128.  Products of two E4M3
+ * values are exact in fp32; the sums are fp32. */
+int vit_op_linear_fp8(const void* a, const void* w, int M, int N, int K, float scale, const float* bias, void* out,
+                      int out_f32, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

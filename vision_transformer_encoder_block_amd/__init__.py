@@ -25,7 +25,7 @@ __all__ = [
     "vit_op_attention_workspace", "vit_op_preprocess", "vit_op_linear_residual_ln",
     "Encoder", "EncoderGraph", "EPI_BIAS_BF16", "EPI_GELU_BF16", "EPI_RESIDUAL", "EPI_BIAS_F32",
     "HeadConfig", "HeadSizes", "head_config_preset", "head_config", "head_plan", "pack_head_params", "SemanticHead",
-    "vit_op_conv3x3",
+    "vit_op_conv3x3", "vit_op_absmax", "vit_op_quantize_fp8", "vit_op_linear_fp8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvit.so")
@@ -94,6 +94,9 @@ _SIGNATURES = {
     "vit_head_forward": (_I, [_P, _P, _I, _P, _P, _P]),
     "vit_head_destroy": (_I, [_P]),
     "vit_op_conv3x3": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
+    "vit_op_absmax": (_I, [_P, _I, ctypes.c_size_t, _P, _P]),
+    "vit_op_quantize_fp8": (_I, [_P, _I, ctypes.c_size_t, ctypes.c_float, _P, _P]),
+    "vit_op_linear_fp8": (_I, [_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _I, _P]),
 }
 
 
@@ -390,6 +393,24 @@ def pack_head_params(P: dict) -> np.ndarray:
 def vit_op_conv3x3(x, ld_in, c0, cin, batch, gh, gw, w, bias, n_out, out, stream=None):
     return _check("vit_op_conv3x3", lib().vit_op_conv3x3(_ptr(x), ld_in, c0, cin, batch, gh, gw, _ptr(w), _ptr(bias),
                                                          n_out, _ptr(out), _stream(stream)))
+
+
+def vit_op_absmax(x, n, amax, stream=None):
+    import torch
+    return _check("vit_op_absmax", lib().vit_op_absmax(_ptr(x), int(x.dtype == torch.bfloat16), n, _ptr(amax),
+                                                       _stream(stream)))
+
+
+def vit_op_quantize_fp8(x, n, s_inv, out, stream=None):
+    import torch
+    return _check("vit_op_quantize_fp8", lib().vit_op_quantize_fp8(_ptr(x), int(x.dtype == torch.bfloat16), n, s_inv,
+                                                                   _ptr(out), _stream(stream)))
+
+
+def vit_op_linear_fp8(a, w, M, N, K, scale, bias, out, stream=None):
+    import torch
+    return _check("vit_op_linear_fp8", lib().vit_op_linear_fp8(_ptr(a), _ptr(w), M, N, K, scale, _ptr(bias), _ptr(out),
+                                                               int(out.dtype == torch.float32), _stream(stream)))
 
 
 class SemanticHead:

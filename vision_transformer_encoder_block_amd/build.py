@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvit.so")
 
-SOURCES = ["vit.cpp", "head.cpp", "gemm.hip", "attention.hip", "norm.hip", "embed.hip", "scores.hip", "head.hip"]
+SOURCES = ["vit.cpp", "head.cpp", "gemm.hip", "attention.hip", "norm.hip", "embed.hip", "scores.hip", "head.hip", "quant.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -223,6 +223,30 @@ struct EpiBiasF32 {
   }
 };
 
+// fp8 products: acc is the fp32 sum of products of E4M3 values; `scale`
+// (the product of the two operands' dequantisation scales) restores the units:
+// out = acc * scale + bias, in fp32 or bf16.
+template <bool F32>
+struct EpiScale {
+  float scale;
+  const float* bias;
+  void* out;
+  int ldc;
+  bool vec;
+  using Col = float4;
+  using Row = NoRow;
+  __device__ Col col4(int n, int nvalid) const { return bias ? load4(bias + n, nvalid, vec) : make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ Row pre(int, int, int) const { return {}; }
+  __device__ void finish4(float (&v)[4], const Col& b, const Row&) const {
+    v[0] = fmaf(v[0], scale, b.x), v[1] = fmaf(v[1], scale, b.y);
+    v[2] = fmaf(v[2], scale, b.z), v[3] = fmaf(v[3], scale, b.w);
+  }
+  __device__ void write4(int m, int n, const float (&v)[4], int nvalid) const {
+    if constexpr (F32) store4_f32((float*)out + (size_t)m * ldc + n, v, nvalid, vec);
+    else store4_bf16((bf16_t*)out + (size_t)m * ldc + n, v, nvalid, vec);
+  }
+};
+
 // Q and K columns (n < 2D) of the fused projection: head-major rows of 64.
 // D % 64 == 0, so the 4 columns of a lane never straddle a head.
 struct EpiQK {
@@ -373,14 +397,42 @@ __device__ __forceinline__ void static_for(F&& f) {
 // the last MFMAs of step kt issue, so the LDS latency of the next step hides
 // under them.
 
-// Chunk swizzle for rows of BK bf16 (BK / 8 chunks of 16 bytes): the 16 rows
-// read by 16 consecutive lanes of one ds_read_b128 hit distinct 4-bank groups.
-template <int BKT>
-__device__ __forceinline__ int swz_k(int r, int c) {
-  if constexpr (BKT == 32) return c ^ ((r >> 2) & 3);
-  else if constexpr (BKT == 64) return c ^ ((r >> 1) & 7);
+// Chunk swizzle for rows of CPR chunks of 16 bytes: the 16 rows read by 16
+// consecutive lanes of one ds_read_b128 hit distinct 4-bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz_c(int r, int c) {
+  if constexpr (CPR == 4) return c ^ ((r >> 2) & 3);
+  else if constexpr (CPR == 8) return c ^ ((r >> 1) & 7);
   else return c ^ (r & 15);
 }
+
+// Matrix-core operand formats.
+//   bf16: v_mfma_f32_32x32x16_bf16; a lane's fragment is one 16-byte chunk
+//         (8 values) of its row.
+//   fp8 (OCP E4M3): v_mfma_f32_32x32x64_f8f6f4 without block scales; a lane's
+//         fragment is two chunks (32 values).  Lanes l and l + 32 hold the two
+//         halves of the 64 k values of row l % 32, in the same arrangement for
+//         A and B, which is all the dot products need.
+typedef int int32x8 __attribute__((ext_vector_type(8)));
+struct MmaBf16 {
+  static constexpr int ES = 2, KPM = 16, CPF = 1;  // bytes per value, k per MFMA, chunks per fragment
+  using Frag = bf16x8;
+  __device__ static Frag frag(const uint4& c0, const uint4&) { return as_bf16x8(c0); }
+  __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) { return mfma32x32x16(a, b, c); }
+};
+struct MmaFp8 {
+  static constexpr int ES = 1, KPM = 64, CPF = 2;
+  using Frag = int32x8;
+  __device__ static Frag frag(const uint4& c0, const uint4& c1) {
+    Frag f;
+    f[0] = (int)c0.x, f[1] = (int)c0.y, f[2] = (int)c0.z, f[3] = (int)c0.w;
+    f[4] = (int)c1.x, f[5] = (int)c1.y, f[6] = (int)c1.z, f[7] = (int)c1.w;
+    return f;
+  }
+  __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
 
 // Addressing of the A operand.  Linear: row m of A holds its K values
 // contiguously (A is [M, K]).
@@ -400,14 +452,15 @@ struct AMapConv3 {
   uint32_t bytes;  // size of `in` in bytes
 };
 
-template <int BM, int BN, int BKT, int WGM, int WGN, int S, class Epi, class AM = AMapLinear>
+template <int BM, int BN, int BKT, int WGM, int WGN, int S, class Epi, class AM = AMapLinear, class MT = MmaBf16>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t* __restrict__ A,
                                                                   const bf16_t* __restrict__ W, int M, int N, int K,
                                                                   int tiles_m, int tiles_n, Epi epi, AM am = {}) {
   constexpr int NW = WGM * WGN;                     // waves per workgroup
   constexpr int WTM = BM / WGM, WTN = BN / WGN;     // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;       // 32x32 blocks per wave
-  constexpr int CPR = BKT / 8;                      // 16-byte chunks per row
+  constexpr int ES = MT::ES;                        // bytes per operand value
+  constexpr int CPR = BKT * ES / 16;                // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;                     // rows per DMA instruction (1 KB)
   // The DMA instructions of one stage (A rows, then W rows, RPI rows each)
   // go round-robin to the waves: instruction k is wave k % NW's (k / NW)-th.
@@ -415,9 +468,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   constexpr int LHI = (TOT + NW - 1) / NW;          // per wave and stage, at most
   constexpr int L = TOT / NW;                       // ... at least (the waits count these)
   constexpr bool A_SPLIT = A_INS % NW == 0;         // instruction i of every wave reads the same operand
-  constexpr int KS = BKT / 16;                      // MFMA k-steps per stage
-  constexpr int STAGE_BYTES = (BM + BN) * BKT * 2;
-  static_assert(BKT == 32 || BKT == 64 || BKT == 128, "BK");
+  constexpr int KS = BKT / MT::KPM;                 // MFMA k-steps per stage
+  constexpr int STAGE_BYTES = (BM + BN) * BKT * ES;
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "BK");
+  static_assert(!AM::kConv || ES == 2, "implicit convolution reads bf16 activations");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(A_INS * RPI == BM && TOT * RPI == BM + BN && L >= 1, "DMA split");
   static_assert(S >= 2 && S * LHI < 64, "pipeline depth");
@@ -430,15 +484,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   const int m0 = tm * BM, n0 = tn * BN;
 
   static_assert(!AM::kConv || A_SPLIT, "implicit convolution needs whole A instructions per wave");
-  uint32_t a_bytes = (uint32_t)((size_t)M * K * 2);
+  uint32_t a_bytes = (uint32_t)((size_t)M * K * ES);
   if constexpr (AM::kConv) a_bytes = am.bytes;
   const int32x4 ra_src = make_rsrc_words(A, a_bytes);
-  const int32x4 rb_src = make_rsrc_words(W, (uint32_t)((size_t)N * K * 2));
+  const int32x4 rb_src = make_rsrc_words(W, (uint32_t)((size_t)N * K * ES));
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   if constexpr (HasPrologue<Epi>::value) epi.prologue(wave_u, lane, NW);
   // byte offset (at k = 0) of the chunk this lane fetches in each of its DMA
   // instructions; instruction k fills LDS bytes [1024 k, 1024 (k + 1)) of the
-  // stage (A's BM rows first, so W's rows start at BM * BKT * 2 = 1024 A_INS)
+  // stage (A's BM rows first, so W's rows start at BM * BKT * ES = 1024 A_INS)
   uint32_t g_off[LHI];
   // implicit convolution: the A row's image offset (b * gh * gw) and pixel
   // (y, x); rows past M get a y that no tap brings inside the grid
@@ -451,7 +505,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
       const int k = min(i * NW + wave, TOT - 1);
       const bool is_a = A_SPLIT ? i < A_INS / NW : k < A_INS;
       const int row = (is_a ? k : k - A_INS) * RPI + sub;
-      g_off[i] = (uint32_t)((is_a ? m0 : n0) + row) * (uint32_t)K * 2u + (uint32_t)swz_k<BKT>(row, pc) * 16u;
+      g_off[i] = (uint32_t)((is_a ? m0 : n0) + row) * (uint32_t)K * (uint32_t)ES + (uint32_t)swz_c<CPR>(row, pc) * 16u;
       if constexpr (AM::kConv) {
         if (i < A_PER_WAVE) {
           const int m = m0 + row;
@@ -460,14 +514,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
           cpb[i] = b * P;
           cy[i] = m < M ? pix / am.gw : -4;
           cx[i] = pix - (pix / am.gw) * am.gw;
-          g_off[i] = (uint32_t)swz_k<BKT>(row, pc) * 16u;  // chunk within the step
+          g_off[i] = (uint32_t)swz_c<CPR>(row, pc) * 16u;  // chunk within the step
         }
       }
     }
   }
   auto issue = [&](auto stage, int kt) {
     const uint32_t blk = lds_addr(stage_lds<STAGE_BYTES, decltype(stage)::value>());
-    const uint32_t koff = (uint32_t)kt * (BKT * 2);
+    const uint32_t koff = (uint32_t)kt * (BKT * ES);
     int ky = 0, kx = 0, cbase = 0;
     if constexpr (AM::kConv) {
       const int kel = kt * BKT;
@@ -506,27 +560,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
 
   const int KT = K / BKT;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  bf16x8 af[2][TM], bw[2][TN];
+  typename MT::Frag af[2][TM], bw[2][TN];
   auto read = [&](auto stage, int buf, int ks) {
     const uint4* Ac = stage_lds<STAGE_BYTES, decltype(stage)::value>();
     const uint4* Bc = Ac + BM * CPR;
-    const int qd = ks * 2 + lhalf;
+    const int qd = (ks * 2 + lhalf) * MT::CPF;   // first chunk of this lane's fragment
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = wm * WTM + i * 32 + lrow;
-      af[buf][i] = as_bf16x8(Ac[r * CPR + swz_k<BKT>(r, qd)]);
+      af[buf][i] = MT::frag(Ac[r * CPR + swz_c<CPR>(r, qd)], Ac[r * CPR + swz_c<CPR>(r, qd + MT::CPF - 1)]);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int r = wn * WTN + j * 32 + lrow;
-      bw[buf][j] = as_bf16x8(Bc[r * CPR + swz_k<BKT>(r, qd)]);
+      bw[buf][j] = MT::frag(Bc[r * CPR + swz_c<CPR>(r, qd)], Bc[r * CPR + swz_c<CPR>(r, qd + MT::CPF - 1)]);
     }
   };
   auto mma = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(af[buf][i], bw[buf][j], acc[i][j]);
+      for (int j = 0; j < TN; ++j) acc[i][j] = MT::mma(af[buf][i], bw[buf][j], acc[i][j]);
   };
   // wait until at most `later` stages of this wave's loads are in flight
   // (the ones issued after the stage being waited for); with L the smaller
@@ -741,11 +795,11 @@ struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, S = S_;
 };
 
-template <class C, class Epi, class AM = AMapLinear>
+template <class C, class Epi, class AM = AMapLinear, class MT = MmaBf16>
 hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s, AM am = {}) {
   const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
   if (K % C::BK != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<C::BM, C::BN, C::BK, C::WGM, C::WGN, C::S, Epi, AM>), dim3(tiles_m * tiles_n),
+  hipLaunchKernelGGL((gemm_bf16_kernel<C::BM, C::BN, C::BK, C::WGM, C::WGN, C::S, Epi, AM, MT>), dim3(tiles_m * tiles_n),
                      dim3(64 * C::WGM * C::WGN), 0, s, A, W, M, N, K, tiles_m, tiles_n, epi, am);
   return hipGetLastError();
 }
@@ -758,6 +812,10 @@ using CfgMid = Cfg<128, 128, 64, 2, 2, 2>;
 using CfgSmall = Cfg<64, 128, 64, 2, 2, 2>;
 using CfgBig = Cfg<256, 256, 64, 2, 4, 2>;
 using CfgTiny = Cfg<64, 64, 64, 2, 2, 2>;
+// fp8 operands: a K step of 128 values is the same 128-byte row slice as 64 bf16 values
+using CfgMid8 = Cfg<128, 128, 128, 2, 2, 2>;
+using CfgSmall8 = Cfg<64, 128, 128, 2, 2, 2>;
+using CfgTiny8 = Cfg<64, 64, 128, 2, 2, 2>;
 
 template <class Epi, class AM = AMapLinear>
 hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s,
@@ -811,6 +869,22 @@ hipError_t dispatch_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, c
 }
 
 using CfgRowLN = Cfg<64, EpiResidualLN::kD, 64, 2, 4, 2>;
+
+// fp8 tiles, chosen by the same rules as the bf16 ones (no 256 x 256 tile:
+// its fp8 fragments would not fit the registers)
+template <class Epi>
+hipError_t dispatch_fp8(const uint8_t* A, const uint8_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
+  const auto a = reinterpret_cast<const bf16_t*>(A);
+  const auto w = reinterpret_cast<const bf16_t*>(W);
+  const long mid_tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
+  if (mid_tiles < 256) {
+    const long small_tiles = (long)((M + 63) / 64) * ((N + 127) / 128);
+    if (small_tiles >= 256) return run<CfgSmall8, Epi, AMapLinear, MmaFp8>(a, w, M, N, K, epi, s);
+    return run<CfgTiny8, Epi, AMapLinear, MmaFp8>(a, w, M, N, K, epi, s);
+  }
+  if (K <= 1024 && mid_tiles < 512) return run<CfgSmall8, Epi, AMapLinear, MmaFp8>(a, w, M, N, K, epi, s);
+  return run<CfgMid8, Epi, AMapLinear, MmaFp8>(a, w, M, N, K, epi, s);
+}
 
 }  // namespace
 
@@ -869,6 +943,16 @@ hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, int M, int N, int K
     }
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* W, int M, int N, int K, float scale, const float* bias,
+                           void* out, int ldc, bool out_f32, hipStream_t s) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || ldc < N || !out) return hipErrorInvalidValue;
+  if ((size_t)(M + 256) * K >= (1ull << 32) || (size_t)(N + 256) * K >= (1ull << 32)) return hipErrorInvalidValue;
+  auto al = [](const void* p, size_t n) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % n == 0; };
+  const bool vec = N % 4 == 0 && ldc % 4 == 0 && al(bias, 16) && al(out, out_f32 ? 16 : 8);
+  if (out_f32) return dispatch_fp8(A, W, M, N, K, EpiScale<true>{scale, bias, out, ldc, vec}, s);
+  return dispatch_fp8(A, W, M, N, K, EpiScale<false>{scale, bias, out, ldc, vec}, s);
 }
 
 hipError_t launch_gemm_conv3(const uint16_t* in, int ld_in, int c0, int C, int batch, int gh, int gw,

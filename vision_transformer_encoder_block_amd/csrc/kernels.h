@@ -52,6 +52,19 @@ constexpr bool residual_ln_fusable(int n) { return n == 384; }
 hipError_t launch_gemm_conv3(const uint16_t* in, int ld_in, int c0, int C, int batch, int gh, int gw,
                              const uint16_t* W, int N, const EpiParams& ep, hipStream_t s);
 
+// fp8 (OCP E4M3) GEMM: out[m, n] = scale * sum_k A[m, k] W[n, k] + bias[n]
+// (bias may be null) with A [M, K], W [N, K] as E4M3 codes, K a multiple of
+// 128; out fp32 or bf16 [M, ldc].
+hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* W, int M, int N, int K, float scale, const float* bias,
+                           void* out, int ldc, bool out_f32, hipStream_t s);
+
+// E4M3 codes of x[i] * s_inv (product in fp32; nearest value, ties to even,
+// saturated to +-448, sign kept, NaN -> 0x7F); x fp32 (x_bf16 == false) or bf16.
+hipError_t launch_quantize_fp8(const void* x, bool x_bf16, size_t n, float s_inv, uint8_t* out, hipStream_t s);
+
+// amax[0] = max |x[i]| over n fp32 (or bf16) values (NaN ignored); amax is written, not accumulated.
+hipError_t launch_absmax(const void* x, bool x_bf16, size_t n, float* amax, hipStream_t s);
+
 // One-time per-device set-up of the GEMM epilogues (the GELU Phi table; a
 // synchronous copy).  launch_gemm does it on first use; encoders call it at
 // creation so that no later launch copies.
