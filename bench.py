@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "images/s and % of bf16 MFMA peak, ViT-S/16@336 b32 and ViT-L/16@1024 b1"
 
@@ -371,6 +372,32 @@ def bench_head(steps=30, warmup=5):
                          "avg_launch_us": ms_conv * 1e3, "traffic": None}}
 
 
+def bench_fp8(steps=30, warmup=5):
+    """The fp8 (E4M3) linear layer against the bf16 one on the same shapes: the
+    encoder's fc1 / fc2 (ViT-S/16 @336 b32, ViT-L/16 @1024 b1) and a square
+    8192^3 product; TFLOP/s against the fp8 dense peak (5.0 PF)."""
+    import torch
+    import vision_transformer_encoder_block_amd as vit
+    g = torch.Generator(device="cuda").manual_seed(8)
+    res = {}
+    for name, M, N, K in [("vits_fc1", 14272, 1536, 384), ("vits_fc2", 14272, 384, 1536),
+                          ("vitl_fc1", 4101, 4096, 1024), ("square_8192", 8192, 8192, 8192)]:
+        qa = torch.randint(0, 0x7F, (M, K), dtype=torch.uint8, device="cuda", generator=g)
+        qw = torch.randint(0, 0x7F, (N, K), dtype=torch.uint8, device="cuda", generator=g)
+        bias = torch.zeros(N, device="cuda")
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ms8, _ = time_gpu(lambda: vit.vit_op_linear_fp8(qa, qw, M, N, K, 1.0, bias, out), steps, warmup)
+        a = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        w = torch.randn(N, K, device="cuda", generator=g).to(torch.bfloat16)
+        ms16, _ = time_gpu(lambda: vit.vit_op_linear(a, w, bias, M, N, K, vit.EPI_BIAS_BF16, None, out), steps, warmup)
+        fl = 2.0 * M * N * K
+        res[name] = {"shape": [M, N, K], "fp8_us": ms8 * 1e3, "fp8_tflops": fl / (ms8 * 1e-3) / 1e12,
+                     "fp8_frac_peak": fl / (ms8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                     "bf16_us": ms16 * 1e3, "bf16_tflops": fl / (ms16 * 1e-3) / 1e12, "speedup": ms16 / ms8}
+        del qa, qw, a, w, out
+    return res
+
+
 def head_cpu_baseline(images=8):
     """The head's oracle (float64 NumPy), untuned, on DINOv2-S/14 @518 stand-in taps."""
     import synth
@@ -397,6 +424,7 @@ def main():
                     help="also run a 256 MiB device copy (for scaling HBM counters)")
     ap.add_argument("--head-only", action="store_true",
                     help="run only the semantic-head leg (DINOv2-S/14 @518 b8 + head) and print its JSON")
+    ap.add_argument("--fp8-only", action="store_true", help="run only the fp8 linear leg and print its JSON")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: turn two rocprofv3 --pmc CSVs into profiles/hbm_traffic.json")
     args = ap.parse_args()
@@ -412,6 +440,9 @@ def main():
 
     if args.head_only:
         print(json.dumps(bench_head(args.steps, args.warmup)), flush=True)
+        return
+    if args.fp8_only:
+        print(json.dumps(bench_fp8(args.steps, args.warmup)), flush=True)
         return
     if args.copy_calibration:
         copy_calibration()
@@ -431,6 +462,9 @@ def main():
     log("semantic head ...")
     hd = bench_head()
     log(json.dumps(hd))
+    log("fp8 linear ...")
+    f8 = bench_fp8()
+    log(json.dumps(f8))
     log("kernel breakdown ...")
     bd = kernel_breakdown(cfg, 32)
     for n, b in bd.items():
@@ -466,6 +500,7 @@ def main():
     if not args.no_cpu:
         hd["cpu_baseline"] = head_cpu_baseline()
     out["semantic_head"] = hd
+    out["fp8_linear"] = f8
     if not args.no_cpu:
         log("CPU oracle baseline ...")
         out["cpu_baseline"] = cpu_baseline()
