@@ -48,7 +48,7 @@ typedef struct vit_head_config {
   int grid_h, grid_w;   /* patch grid of the taps (37 x 37 for DINOv2-S/14 @518) */
   int dim;              /* channels of one tap (encoder width D); multiple of 64 */
   int taps;             /* number of taps concatenated (4) */
-  int width;            /* projector width (256); multiple of 128 */
+  int width;            /* projector width: 256 (the diagram's, at every size) */
   int groups;           /* GroupNorm groups (32); width must equal 8 * groups */
   int classes;          /* predicted classes (19); 1..1024 */
   int out_h, out_w;     /* size of the resized logits (the image: 518 x 518) */

@@ -165,8 +165,8 @@ def test_head_plan_rejects_bad_configs(L):
         return lib.vit_head_plan(ctypes.byref(c), ctypes.byref(out))
 
     assert plan() == 0
-    assert plan(width=128, groups=16) == 0
-    assert plan(width=192, groups=24) == -5      # width 128 or 256 only
+    assert plan(width=128, groups=16) == -5     # the diagram's width 256 only
+    assert plan(width=192, groups=24) == -5
     assert plan(groups=16) == -5                 # width must be 8 * groups
     assert plan(dim=100) == -5
     assert plan(classes=0) == -1

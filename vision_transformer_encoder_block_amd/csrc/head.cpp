@@ -61,8 +61,8 @@ int validate(const vit_head_config* c) {
     return report_error(VIT_ERR_SHAPE, "grid must be at least 1 x 1 and at most 2^20 pixels");
   if (c->dim < 64 || c->dim % 64) return report_error(VIT_ERR_UNSUPPORTED, "dim must be a positive multiple of 64");
   if (c->taps < 1 || c->taps > 16) return report_error(VIT_ERR_ARG, "taps must be in [1, 16]");
-  if (c->width != 128 && c->width != 256)
-    return report_error(VIT_ERR_UNSUPPORTED, "width must be 128 or 256 (channel LayerNorm rows of 64 or 128 lanes)");
+  if (c->width != 256)
+    return report_error(VIT_ERR_UNSUPPORTED, "width must be 256 (the diagram's projector width at every size)");
   if (c->groups < 1 || c->width != 8 * c->groups) return report_error(VIT_ERR_UNSUPPORTED, "width must equal 8 * groups");
   if (c->classes < 1 || c->classes > 1024) return report_error(VIT_ERR_ARG, "classes must be in [1, 1024]");
   if (c->out_h < 1 || c->out_w < 1 || c->out_h > 65535 || c->out_w > 65535)
