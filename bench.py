@@ -305,6 +305,18 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib=256):
             continue
         out["ops"][op] = {"kernel_substring": sub, "fetch_kib": f, "write_kib": w,
                           "bytes_per_launch": (f * scale_f + w * scale_w) * 1024.0}
+    # out-proj and fc2 share the residual + LayerNorm kernel; they write the same
+    # bytes (x and the normalised rows) but fc2 reads a 4x longer A operand, so
+    # the dispatches split into two clusters by FETCH_SIZE
+    rl = [v for k, vs in fetch.items() if "EpiResidualLN" in k for v in vs]
+    w_rl = avg(write, "EpiResidualLN")
+    if rl and w_rl is not None and scale_f and scale_w:
+        mid = (min(rl) + max(rl)) / 2
+        for op, grp in (("out_proj", [v for v in rl if v < mid]), ("fc2", [v for v in rl if v >= mid])):
+            if grp:
+                f = sum(grp) / len(grp)
+                out["ops"][op] = {"kernel_substring": "EpiResidualLN (FETCH cluster)", "fetch_kib": f,
+                                  "write_kib": w_rl, "bytes_per_launch": (f * scale_f + w_rl * scale_w) * 1024.0}
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     json.dump(out, open(path, "w"), indent=1)
     print(json.dumps(out, indent=1))
