@@ -191,7 +191,11 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
 #pragma unroll
   for (int i = 0; i < S - 1; ++i)
     if (i < nt) issue(t_first + i, i);
-  wait_tiles(min(S - 2, nt - 1));  // tile t_first is in
+  // Every load so far is waited for here (tile t_first, which is needed, and
+  // the tiles issued with it): the explicit vmcnt(0) also tells the compiler
+  // that the Q fragments have landed, so it places no vmcnt waits for them in
+  // the loop, where they would also wait for the K / V^T tiles in flight.
+  wait_vm<0>();
   barrier_keep_loads();
   if ((t_first + 1) * KT > N) {
     fix_last(t_first, 0);
