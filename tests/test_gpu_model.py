@@ -83,6 +83,39 @@ def test_small_models(i, ls):
         gate(tok, desc, ref)
 
 
+def _random_configs(n=10, seed=4242):
+    """Seeded random small encoders: patch, grid, width, MLP width, registers,
+    depth, batch and (for some) a position table on another grid."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        patch = int(rng.choice([8, 14, 16]))
+        gh, gw = (int(v) for v in rng.integers(1, 10, 2))
+        dim = 64 * int(rng.choice([1, 2, 3, 4, 5, 6, 8]))
+        hidden = 64 * int(rng.integers(1, 4 * dim // 64 + 1))
+        pos = (gh, gw) if rng.random() < 0.6 else (int(rng.integers(2, 8)), int(rng.integers(2, 8)))
+        out.append(dict(img_h=gh * patch, img_w=gw * patch, patch=patch, dim=dim, heads=dim // 64, mlp_hidden=hidden,
+                        registers=int(rng.choice([0, 1, 2, 4])), depth=int(rng.integers(1, 3)), pos_grid=pos,
+                        seed=700 + i, batch=int(rng.integers(1, 4))))
+    return out
+
+
+RANDOM = _random_configs()
+
+
+@pytest.mark.parametrize("i", range(len(RANDOM)))
+def test_random_small_models(i):
+    over = dict(RANDOM[i])
+    batch = over.pop("batch")
+    cfg = synth.preset("vits16_224", bf16_params=True, **over)
+    say(f"random model {i}: {over} batch={batch} tokens={synth.tokens(cfg)}")
+    P = synth.make_params(cfg)
+    x = synth.make_images(cfg, batch, seed=950 + i)
+    grid = synth.grid(cfg)
+    pos = None if tuple(cfg["pos_grid"]) == grid else O.resample_pos(P["pos"], tuple(cfg["pos_grid"]), grid)
+    gate(*run_gpu(cfg, P, x)[:2], O.forward(x, P, cfg, pos=pos))
+
+
 def test_layerscale_zero_isolates_embedding_and_final_norm():
     # bf16-representable images: the patch embedding is then exact products summed in fp32
     cfg = synth.preset("vits16_224", layerscale=0.0, bf16_params=True, depth=2)
