@@ -49,7 +49,9 @@ def test_layernorm(rows, dim, out_fp32):
 # ------------------------------------------------------------------ GEMM epilogues
 
 SHAPES = [(1, 64, 64), (5, 150, 384), (130, 384, 384), (446, 1152, 384), (1000, 1536, 384), (257, 384, 1536),
-          (4101, 1024, 128), (300, 96, 768)]
+          (4101, 1024, 128), (300, 96, 768),
+          (3000, 3000, 640),   # 128 x 128 tiles, ragged in M and N
+          (4100, 8200, 192)]   # 256 x 256 tiles (M N >= 32M), ragged in M and N
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
