@@ -229,7 +229,9 @@ def test_attention_large_logits_stay_finite():
 
 @pytest.mark.parametrize("batch,src,dst,bgr", [(2, (720, 1280), (336, 336), True), (1, (37, 53), (45, 31), False),
                                                (3, (100, 150), (224, 224), False), (1, (518, 518), (518, 518), True),
-                                               (1, (1, 1), (3, 2), False)])
+                                               (1, (1, 1), (3, 2), False),
+                                               # rows of 5000 pixels: wider than the staged-row buffer
+                                               (1, (40, 5000), (30, 700), True)])
 def test_preprocess(batch, src, dst, bgr):
     say(f"preprocess batch={batch} {src} -> {dst} bgr={bgr}")
     frames = RNG.integers(0, 256, size=(batch,) + src + (3,), dtype=np.uint8)

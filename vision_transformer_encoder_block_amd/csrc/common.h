@@ -150,7 +150,7 @@ __device__ __forceinline__ void ln_group_normalize(float4 (&v)[V4], const float4
 // exactly computed remainder, so the weight carries only the rounding of one
 // division (a float coordinate near 700 would carry an ulp of 6e-5).
 // Negative centres clamp to 0; indices past the edge clamp to n_in - 1.
-__device__ __forceinline__ void bilinear_tap(int i, int n_in, int n_out, int& i0, int& i1, float& w) {
+__host__ __device__ __forceinline__ void bilinear_tap(int i, int n_in, int n_out, int& i0, int& i1, float& w) {
   const long long num = (long long)(2 * i + 1) * n_in - n_out;
   const long long den = 2LL * n_out;
   if (num <= 0) {
@@ -161,8 +161,8 @@ __device__ __forceinline__ void bilinear_tap(int i, int n_in, int n_out, int& i0
     i0 = (int)q;
     w = (float)(num - q * den) / (float)den;
   }
-  i0 = min(i0, n_in - 1);
-  i1 = min(i0 + 1, n_in - 1);
+  i0 = i0 < n_in - 1 ? i0 : n_in - 1;
+  i1 = i0 + 1 < n_in - 1 ? i0 + 1 : n_in - 1;
 }
 
 }  // namespace vit

@@ -123,10 +123,86 @@ __global__ __launch_bounds__(256) void crops_kernel(const float* __restrict__ im
   }
 }
 
-// Frame preprocessing: one thread per output pixel of one row.  Bilinear
-// sample (half-pixel centres, coordinates clamped at the edges) of the three
-// 8-bit channels, scaled by 1/255 and normalised with the ImageNet mean/std
-// (RGB order), written to three planes.  bgr: the frame stores B, G, R.
+// Frame preprocessing.  Bilinear sample (half-pixel centres, coordinates
+// clamped at the edges) of the three 8-bit channels, scaled by 1/255 and
+// normalised with the ImageNet mean/std (RGB order), written to three planes.
+// bgr: the frame stores B, G, R.
+constexpr float kMean[3] = {0.485f, 0.456f, 0.406f};
+constexpr float kInvStd[3] = {1.f / 0.229f, 1.f / 0.224f, 1.f / 0.225f};
+
+// Byte j of source row 0 is r0[o0 + j] (row 1: r1[o1 + j]); o0 and o1 may be
+// negative, but every byte read, o + 3 x + c, is an index into the rows' data.
+__device__ __forceinline__ void preprocess_pixel(const uint8_t* r0, int o0, const uint8_t* r1, int o1, int x0, int x1,
+                                                 float lx, float ly, bool bgr, float* o, size_t plane) {
+#pragma unroll
+  for (int oc = 0; oc < 3; ++oc) {
+    const int c = bgr ? 2 - oc : oc;
+    const float top = (1.f - lx) * (float)r0[o0 + x0 * 3 + c] + lx * (float)r0[o0 + x1 * 3 + c];
+    const float bot = (1.f - lx) * (float)r1[o1 + x0 * 3 + c] + lx * (float)r1[o1 + x1 * 3 + c];
+    const float v = (1.f - ly) * top + ly * bot;
+    o[oc * plane] = (v * (1.f / 255.f) - kMean[oc]) * kInvStd[oc];
+  }
+}
+
+// One workgroup per output row (y, image b).  The byte span of the two source
+// rows that the row's samples touch is copied to LDS with 16-byte loads (span
+// ends rounded out to 16 bytes, never used; a chunk that would reach past the
+// frames' last byte is read byte by byte), then every thread blends output
+// pixels x = tid, tid + 256, ...
+// from LDS: the frames are read once, in wide coalesced loads, instead of
+// twelve scattered byte loads per output pixel.
+constexpr int kPreSpanMax = 12288;  // LDS bytes per source row (4096 RGB pixels)
+
+__global__ __launch_bounds__(256) void preprocess_rows_kernel(const uint8_t* __restrict__ frames, uint32_t total_bytes,
+                                                              int sh, int sw, float* __restrict__ out, int dh, int dw,
+                                                              bool bgr) {
+  __shared__ uint4 rows[2][kPreSpanMax / 16 + 1];
+  const int y = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  int y0, y1, xa, xb, xc, xd;
+  float ly, lx;
+  bilinear_tap(y, sh, dh, y0, y1, ly);
+  bilinear_tap(0, sw, dw, xa, xb, lx);
+  bilinear_tap(dw - 1, sw, dw, xc, xd, lx);
+  const uint32_t frame = (uint32_t)b * (uint32_t)sh * (uint32_t)sw * 3u;
+  const uint32_t span_lo = (uint32_t)xa * 3u, span_hi = (uint32_t)(xd + 1) * 3u;  // bytes within a row
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(frames, total_bytes);
+  uint32_t base[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const uint32_t lo = frame + (uint32_t)(r ? y1 : y0) * (uint32_t)sw * 3u + span_lo;
+    base[r] = lo & ~15u;
+    const uint32_t n16 = (lo + (span_hi - span_lo) - base[r] + 15u) / 16u;
+    for (uint32_t i = tid; i < n16; i += 256) {
+      const uint32_t at = base[r] + 16u * i;
+      if (at + 16u <= total_bytes) {
+        rows[r][i] = buf_load16(rs, at);
+      } else {  // the chunk that reaches past the frames' last byte: byte loads
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (uint32_t j = 0; j < 16u && at + j < total_bytes; ++j) w[j >> 2] |= (uint32_t)frames[at + j] << (8 * (j & 3));
+        rows[r][i] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  }
+  __syncthreads();
+  // LDS row r holds global bytes from base[r] on; source byte j of row r is
+  // LDS byte j + (row start - base[r]), with row start - base[r] in
+  // [-span_lo, 15 - span_lo], so bytes j >= span_lo land at LDS bytes >= 0
+  const int o0 = (int)(frame + (uint32_t)y0 * (uint32_t)sw * 3u - base[0]);
+  const int o1 = (int)(frame + (uint32_t)y1 * (uint32_t)sw * 3u - base[1]);
+  const uint8_t* l0 = reinterpret_cast<const uint8_t*>(rows[0]);
+  const uint8_t* l1 = reinterpret_cast<const uint8_t*>(rows[1]);
+  const size_t plane = (size_t)dh * dw;
+  float* o = out + (size_t)b * 3 * plane + (size_t)y * dw;
+  for (int x = tid; x < dw; x += 256) {
+    int x0, x1;
+    bilinear_tap(x, sw, dw, x0, x1, lx);
+    preprocess_pixel(l0, o0, l1, o1, x0, x1, lx, ly, bgr, o + x, plane);
+  }
+}
+
+// Frames whose row span does not fit the LDS buffer (or whose batch needs
+// offsets of 32 bits or more): one thread per output pixel, reading the
+// frames directly.
 __global__ __launch_bounds__(256) void preprocess_kernel(const uint8_t* __restrict__ frames, int sh, int sw,
                                                          float* __restrict__ out, int dh, int dw, bool bgr) {
   const int x = blockIdx.x * blockDim.x + threadIdx.x;
@@ -137,18 +213,9 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint8_t* __restri
   bilinear_tap(y, sh, dh, y0, y1, ly);
   bilinear_tap(x, sw, dw, x0, x1, lx);
   const uint8_t* f = frames + (size_t)b * sh * sw * 3;
-  const uint8_t* r0 = f + (size_t)y0 * sw * 3;
-  const uint8_t* r1 = f + (size_t)y1 * sw * 3;
-  constexpr float kMean[3] = {0.485f, 0.456f, 0.406f};
-  constexpr float kInvStd[3] = {1.f / 0.229f, 1.f / 0.224f, 1.f / 0.225f};
-#pragma unroll
-  for (int oc = 0; oc < 3; ++oc) {
-    const int c = bgr ? 2 - oc : oc;
-    const float top = (1.f - lx) * (float)r0[x0 * 3 + c] + lx * (float)r0[x1 * 3 + c];
-    const float bot = (1.f - lx) * (float)r1[x0 * 3 + c] + lx * (float)r1[x1 * 3 + c];
-    const float v = (1.f - ly) * top + ly * bot;
-    out[(((size_t)b * 3 + oc) * dh + y) * dw + x] = (v * (1.f / 255.f) - kMean[oc]) * kInvStd[oc];
-  }
+  const size_t plane = (size_t)dh * dw;
+  preprocess_pixel(f + (size_t)y0 * sw * 3, 0, f + (size_t)y1 * sw * 3, 0, x0, x1, lx, ly, bgr,
+                   out + (size_t)b * 3 * plane + (size_t)y * dw + x, plane);
 }
 
 __global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ x, size_t n, bf16_t* __restrict__ y) {
@@ -192,8 +259,20 @@ hipError_t launch_preprocess(const uint8_t* frames, int batch, int sh, int sw, b
                              hipStream_t s) {
   if (batch < 1 || sh < 1 || sw < 1 || dh < 1 || dw < 1 || batch > 65535 || dh > 65535)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(preprocess_kernel, dim3((unsigned)((dw + 255) / 256), dh, batch), dim3(256), 0, s, frames, sh, sw,
-                     out, dh, dw, bgr);
+  // source byte span of one output row, rounded out to 16 bytes at both ends
+  int xa, xb, xc, xd;
+  float w;
+  bilinear_tap(0, sw, dw, xa, xb, w);
+  bilinear_tap(dw - 1, sw, dw, xc, xd, w);
+  const size_t span = (size_t)(xd + 1 - xa) * 3 + 30;
+  const size_t total = (size_t)batch * sh * sw * 3;
+  if (span <= (size_t)kPreSpanMax && total + 64 < (1ull << 32)) {
+    hipLaunchKernelGGL(preprocess_rows_kernel, dim3((unsigned)dh, (unsigned)batch), dim3(256), 0, s, frames,
+                       (uint32_t)total, sh, sw, out, dh, dw, bgr);
+  } else {
+    hipLaunchKernelGGL(preprocess_kernel, dim3((unsigned)((dw + 255) / 256), dh, batch), dim3(256), 0, s, frames, sh,
+                       sw, out, dh, dw, bgr);
+  }
   return hipGetLastError();
 }
 
