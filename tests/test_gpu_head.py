@@ -57,7 +57,9 @@ def check_labels(got, ref):
     assert agree[clear].all()
 
 
-@pytest.mark.parametrize("batch,gh,gw,out", [(2, 6, 5, (84, 70)), (3, 13, 11, (100, 90)), (1, 1, 1, (7, 5))])
+@pytest.mark.parametrize("batch,gh,gw,out", [(2, 6, 5, (84, 70)), (3, 13, 11, (100, 90)), (1, 1, 1, (7, 5)),
+                                             (1, 20, 17, (42, 30)),    # GroupNorm: 2 pixels per thread
+                                             (1, 50, 45, (33, 61))])   # GroupNorm: > 2048 pixels (loop)
 def test_head_matches_oracle_small_grids(batch, gh, gw, out):
     require_gpu()
     cfg = synth.preset("vits14_518")

@@ -84,6 +84,10 @@ __global__ __launch_bounds__(256) void chan_ln_kernel(const float* __restrict__ 
 // GroupNorm (8 channels per group) over the P pixels of one image, then the
 // per-channel affine and the exact GELU; one workgroup per (group, image),
 // two passes for the mean and the biased variance as in the definition.
+// PPT > 0: each thread holds its pixels tid + 256 i (i < PPT) in registers,
+// so the group is read from memory once; PPT = 0: three passes over memory
+// (any P).  Both sum in the same order, so they give the same bits.
+template <int PPT>
 __global__ __launch_bounds__(256) void groupnorm_gelu_kernel(const float* __restrict__ x, int P, int C,
                                                              const float* __restrict__ g, const float* __restrict__ bta,
                                                              float eps, uint16_t* __restrict__ out) {
@@ -100,30 +104,22 @@ __global__ __launch_bounds__(256) void groupnorm_gelu_kernel(const float* __rest
     __syncthreads();
     return t;
   };
-  float s = 0.f;
-  for (int p = tid; p < P; p += 256) {
+  auto load = [&](int p, float (&v)[8]) {
     const float4 u = reinterpret_cast<const float4*>(base + (size_t)p * C)[0];
     const float4 w = reinterpret_cast<const float4*>(base + (size_t)p * C)[1];
-    s += ((u.x + u.y) + (u.z + u.w)) + ((w.x + w.y) + (w.z + w.w));
-  }
+    v[0] = u.x, v[1] = u.y, v[2] = u.z, v[3] = u.w, v[4] = w.x, v[5] = w.y, v[6] = w.z, v[7] = w.w;
+  };
+  auto add_sum = [](float& s, const float (&v)[8]) { s += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7])); };
+  auto add_sq = [](float& q, const float (&v)[8], float mean) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float d = v[i] - mean;
+      q += d * d;
+    }
+  };
   const float n = 8.f * (float)P;
-  const float mean = block_sum(s) / n;
-  float q = 0.f;
-  for (int p = tid; p < P; p += 256) {
-    const float4 u = reinterpret_cast<const float4*>(base + (size_t)p * C)[0];
-    const float4 w = reinterpret_cast<const float4*>(base + (size_t)p * C)[1];
-    const float d[8] = {u.x - mean, u.y - mean, u.z - mean, u.w - mean, w.x - mean, w.y - mean, w.z - mean, w.w - mean};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q += d[i] * d[i];
-  }
-  const float rstd = rsqrtf(block_sum(q) / n + eps);
   float gs[8], bs[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) gs[i] = g[c0 + i] * rstd, bs[i] = bta[c0 + i];
-  for (int p = tid; p < P; p += 256) {
-    const float4 u = reinterpret_cast<const float4*>(base + (size_t)p * C)[0];
-    const float4 w = reinterpret_cast<const float4*>(base + (size_t)p * C)[1];
-    const float v[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+  auto store = [&](int p, const float (&v)[8], float mean) {
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -132,6 +128,47 @@ __global__ __launch_bounds__(256) void groupnorm_gelu_kernel(const float* __rest
     }
     *reinterpret_cast<uint4*>(out + ((size_t)b * P + p) * C + c0) =
         make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+  };
+  if constexpr (PPT > 0) {
+    float v[PPT][8];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+      if (tid + 256 * i < P) load(tid + 256 * i, v[i]);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+      if (tid + 256 * i < P) add_sum(s, v[i]);
+    const float mean = block_sum(s) / n;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+      if (tid + 256 * i < P) add_sq(q, v[i], mean);
+    const float rstd = rsqrtf(block_sum(q) / n + eps);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gs[i] = g[c0 + i] * rstd, bs[i] = bta[c0 + i];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+      if (tid + 256 * i < P) store(tid + 256 * i, v[i], mean);
+  } else {
+    float v[8];
+    float s = 0.f;
+    for (int p = tid; p < P; p += 256) {
+      load(p, v);
+      add_sum(s, v);
+    }
+    const float mean = block_sum(s) / n;
+    float q = 0.f;
+    for (int p = tid; p < P; p += 256) {
+      load(p, v);
+      add_sq(q, v, mean);
+    }
+    const float rstd = rsqrtf(block_sum(q) / n + eps);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gs[i] = g[c0 + i] * rstd, bs[i] = bta[c0 + i];
+    for (int p = tid; p < P; p += 256) {
+      load(p, v);
+      store(p, v, mean);
+    }
   }
 }
 
@@ -207,7 +244,18 @@ hipError_t launch_chan_ln(const float* x, int M, int C, const float* g, const fl
 hipError_t launch_groupnorm_gelu(const float* x, int batch, int P, int C, int groups, const float* g, const float* b,
                                  float eps, uint16_t* out, hipStream_t s) {
   if (groups < 1 || C != 8 * groups || batch < 1 || batch > 65535 || P < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(groupnorm_gelu_kernel, dim3(groups, batch), dim3(256), 0, s, x, P, C, g, b, eps, out);
+  const dim3 grid(groups, batch);
+  switch ((P + 255) / 256) {  // pixels per thread held in registers (up to 8)
+    case 1: hipLaunchKernelGGL(groupnorm_gelu_kernel<1>, grid, dim3(256), 0, s, x, P, C, g, b, eps, out); break;
+    case 2: hipLaunchKernelGGL(groupnorm_gelu_kernel<2>, grid, dim3(256), 0, s, x, P, C, g, b, eps, out); break;
+    case 3: hipLaunchKernelGGL(groupnorm_gelu_kernel<3>, grid, dim3(256), 0, s, x, P, C, g, b, eps, out); break;
+    case 4: hipLaunchKernelGGL(groupnorm_gelu_kernel<4>, grid, dim3(256), 0, s, x, P, C, g, b, eps, out); break;
+    case 5: hipLaunchKernelGGL(groupnorm_gelu_kernel<5>, grid, dim3(256), 0, s, x, P, C, g, b, eps, out); break;
+    case 6: hipLaunchKernelGGL(groupnorm_gelu_kernel<6>, grid, dim3(256), 0, s, x, P, C, g, b, eps, out); break;
+    case 7: hipLaunchKernelGGL(groupnorm_gelu_kernel<7>, grid, dim3(256), 0, s, x, P, C, g, b, eps, out); break;
+    case 8: hipLaunchKernelGGL(groupnorm_gelu_kernel<8>, grid, dim3(256), 0, s, x, P, C, g, b, eps, out); break;
+    default: hipLaunchKernelGGL(groupnorm_gelu_kernel<0>, grid, dim3(256), 0, s, x, P, C, g, b, eps, out);
+  }
   return hipGetLastError();
 }
 
