@@ -202,8 +202,16 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
     __syncthreads();
   }
 
+  // Issue priority falls as a wave gets through its key range (3 at the
+  // start, 2 past a quarter, 1 past half, 0 past three quarters).  The
+  // arbiter otherwise favours the oldest waves; their workgroup finishes
+  // first and leaves the CU with fewer waves to hide latency for the rest.
+  __builtin_amdgcn_s_setprio(3);
   for (int i = 0; i < nt; ++i) {
     const int t = t_first + i;
+    if (4 * i >= nt && 4 * (i - 1) < nt) __builtin_amdgcn_s_setprio(2);
+    if (2 * i >= nt && 2 * (i - 1) < nt) __builtin_amdgcn_s_setprio(1);
+    if (4 * i >= 3 * nt && 4 * (i - 1) < 3 * nt) __builtin_amdgcn_s_setprio(0);
     const int stage = i % S;
     const uint4* Ks = KV[stage][0];
     const uint4* Vs = KV[stage][1];
