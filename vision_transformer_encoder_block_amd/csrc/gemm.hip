@@ -822,12 +822,9 @@ hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const
                     AM am = {}) {
   const long mid_tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
   if ((long)M * N >= 32L * 1024 * 1024) return run<CfgBig>(A, W, M, N, K, epi, s, am);
-#ifndef SKINNY_RULE
-#define SKINNY_RULE 2
-#endif
-  if (SKINNY_RULE > 0 && mid_tiles < 256) {  // fewer 128 x 128 tiles than compute units
+  if (mid_tiles < 256) {  // fewer 128 x 128 tiles than compute units: 64 x 128, or 64 x 64 if that too is short
     const long small_tiles = (long)((M + 63) / 64) * ((N + 127) / 128);
-    if (SKINNY_RULE == 1 || small_tiles >= 256) return run<CfgSmall>(A, W, M, N, K, epi, s, am);
+    if (small_tiles >= 256) return run<CfgSmall>(A, W, M, N, K, epi, s, am);
     return run<CfgTiny>(A, W, M, N, K, epi, s, am);
   }
   if (K <= 512 && mid_tiles < 512) return run<CfgSmall>(A, W, M, N, K, epi, s, am);
