@@ -189,6 +189,22 @@ def test_vits14_518_b8_taps():
     np.testing.assert_array_equal(taps[:, 3], tok[:, 1:].reshape(8, 37, 37, 384).transpose(0, 3, 1, 2))
 
 
+@pytest.mark.parametrize("name", ["vits16_224", "vits16_336"])
+def test_layerscale_one_sensitivity(name):
+    """The full ViT-S workloads with LayerScale 1.0 (every block's bf16 rounding
+    reaches the output): errors are reported, and only finiteness is required;
+    the workloads' gates apply to LayerScale 1e-5."""
+    cfg = synth.preset(name, layerscale=1.0)
+    P = synth.make_params(cfg)
+    x = synth.make_images(cfg, 1)
+    ref = O.forward(x, P, cfg)
+    tok, desc, _ = run_gpu(cfg, P, x)
+    assert np.isfinite(tok).all() and np.isfinite(desc).all()
+    err = np.abs(tok - ref["tokens"]).max()
+    rms = np.sqrt(np.mean((tok - ref["tokens"]) ** 2))
+    say(f"  {name} LS=1: max|tokens err| = {err:.3e}, rms {rms:.3e}, desc cos = {cosine(desc[0], ref['desc'][0]):.6f}")
+
+
 @pytest.fixture(scope="module")
 def vitl():
     cfg = synth.preset("vitl16_1024")
