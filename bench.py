@@ -322,6 +322,47 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib=256):
     print(json.dumps(out, indent=1))
 
 
+def summarize_mfma(csv_path, simds=1024, clock_ghz=2.4):
+    """Matrix-core utilisation of the ViT-S/16@336 b32 block kernels from one
+    rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16,
+    SQ_INSTS_MFMA, SQ_INSTS_VALU_TRANS_F32) of this script's per-op loops.  The
+    loops also hold other workloads' dispatches of the same kernels, so each op
+    takes the dispatch cluster whose hardware FLOP count (MOPS x 512) is nearest
+    its algorithmic FLOPs at this workload.  A busy cycle is one SIMD's full-rate
+    MFMA cycle (1024 bf16 FLOPs), so utilisation = busy SIMD-cycles / (SIMDs x
+    dispatch duration x clock), the duration taken from the dispatch's own
+    timestamps and the clock the one the dense peak is quoted at.  Prints a
+    markdown table."""
+    import csv
+    import math
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        c = per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {})
+        c["dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    B, N, D, Hm = 32, 446, 384, 1536
+    M = B * N
+    ops = [("qkv", "EpiQKV", 2.0 * M * D * 3 * D), ("attention", "attention_kernel<4, false>", 4.0 * B * N * N * D),
+           ("out_proj", "EpiResidualLN", 2.0 * M * D * D), ("fc1", "EpiGeluBf16", 2.0 * M * D * Hm),
+           ("fc2", "EpiResidualLN", 2.0 * M * Hm * D)]
+    print("| Op | dispatches | dispatch us | hardware GFLOP (MOPS x 512) | algorithmic GFLOP | MFMA instr. | "
+          "MFMA busy % | transcendental instr. |")
+    print("|---|---|---|---|---|---|---|---|")
+    for op, sub, fl in ops:
+        groups = {}
+        for (name, _), c in per.items():
+            if sub in name and "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+                groups.setdefault(round(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]), []).append(c)
+        if not groups:
+            continue
+        mops = min(groups, key=lambda m: abs(math.log(max(m, 1) * 512.0 / fl)))
+        sel = groups[mops]
+        av = {k: sum(c.get(k, 0.0) for c in sel) / len(sel) for k in sel[0]}
+        util = av["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * av["dur_us"] * clock_ghz * 1e3)
+        print(f"| {op} | {len(sel)} | {av['dur_us']:.1f} | {mops * 512 / 1e9:.2f} | {fl / 1e9:.2f} | "
+              f"{av.get('SQ_INSTS_MFMA', 0):.0f} | {100 * util:.1f} | {av.get('SQ_INSTS_VALU_TRANS_F32', 0):.0f} |")
+
+
 KERNEL_NAMES = {
     "qkv": "gemm_bf16_kernel<EpiQKV>",
     "attention": "attention_kernel",
@@ -439,9 +480,14 @@ def main():
     ap.add_argument("--fp8-only", action="store_true", help="run only the fp8 linear leg and print its JSON")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: turn two rocprofv3 --pmc CSVs into profiles/hbm_traffic.json")
+    ap.add_argument("--summarize-mfma", metavar="CSV",
+                    help="host only: matrix-core utilisation table from a rocprofv3 --pmc CSV")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the encoder path is single-GPU (images are independent, "
