@@ -116,6 +116,17 @@ def test_random_small_models(i):
     gate(*run_gpu(cfg, P, x)[:2], O.forward(x, P, cfg, pos=pos))
 
 
+def test_vitg_width_model():
+    """The widest common ViT width, 1536 (24 heads of 64, as in ViT-g/14), on a
+    small image: 2 blocks, 4 registers, batch 2."""
+    cfg = synth.preset("vits16_224", img_h=56, img_w=42, patch=14, dim=1536, heads=24, mlp_hidden=4096, registers=4,
+                       depth=2, bf16_params=True, seed=880, pos_grid=(4, 3))
+    say(f"ViT-g width: tokens={synth.tokens(cfg)}")
+    P = synth.make_params(cfg)
+    x = synth.make_images(cfg, 2, seed=881)
+    gate(*run_gpu(cfg, P, x)[:2], O.forward(x, P, cfg))
+
+
 def test_layerscale_zero_isolates_embedding_and_final_norm():
     # bf16-representable images: the patch embedding is then exact products summed in fp32
     cfg = synth.preset("vits16_224", layerscale=0.0, bf16_params=True, depth=2)

@@ -46,6 +46,25 @@ def test_layernorm(rows, dim, out_fp32):
     assert np.all(np.abs(got - ref) <= tol), np.abs(got - ref).max()
 
 
+WIDTHS = [64 * v for v in list(range(1, 17)) + [20, 24, 32, 48, 64]]
+
+
+@pytest.mark.parametrize("dim", WIDTHS)
+def test_layernorm_every_supported_width(dim):
+    """Each supported width has its own lane layout (float4s per lane, lanes per
+    row): 37 rows (two rows per wave for narrow widths, a ragged last pair) at
+    every one, bf16 output."""
+    say(f"layernorm width {dim}")
+    rows = 37
+    x = RNG.standard_normal((rows, dim)).astype(np.float32) * 1.5 - 0.2
+    g = (1 + 0.02 * RNG.standard_normal(dim)).astype(np.float32)
+    b = (0.02 * RNG.standard_normal(dim)).astype(np.float32)
+    y = torch.empty((rows, dim), dtype=torch.bfloat16, device="cuda")
+    vit.vit_op_layernorm(f32_dev(x), rows, dim, f32_dev(g), f32_dev(b), 1e-6, y, 0)
+    ref = O.layer_norm(x.astype(np.float64), g, b, 1e-6)
+    assert np.all(np.abs(host(y) - ref) <= 2.0 ** -8 * np.abs(ref) + 2e-5 * (1 + np.abs(ref)))
+
+
 # ------------------------------------------------------------------ GEMM epilogues
 
 SHAPES = [(1, 64, 64), (5, 150, 384), (130, 384, 384), (446, 1152, 384), (1000, 1536, 384), (257, 384, 1536),
