@@ -127,6 +127,33 @@ def test_vitg_width_model():
     gate(*run_gpu(cfg, P, x)[:2], O.forward(x, P, cfg))
 
 
+def test_encoder_rejects_bad_calls_and_stays_usable():
+    """Calls with a batch outside [1, max_batch], a misaligned token buffer or a
+    NULL pointer return their status without launching anything; the model
+    then still gives the same tokens as before."""
+    cfg = synth.preset("vits16_224", img_h=48, img_w=32, dim=128, heads=2, mlp_hidden=256, depth=1,
+                       bf16_params=True)
+    P = synth.make_params(cfg)
+    enc = vit.Encoder(cfg, P, max_batch=2)
+    L = vit.lib()
+    x = f32_dev(synth.make_images(cfg, 3))
+    tok = torch.empty((3, enc.tokens, 128), device="cuda")
+    ref = host(enc.forward(x[:2].contiguous(), tokens_out=tok[:2]))
+    stream = vit._stream(None)
+    h = enc.handle
+    assert L.vit_forward(h, x.data_ptr(), 3, tok.data_ptr(), None, stream) == -3    # batch > max_batch
+    assert L.vit_forward(h, x.data_ptr(), 0, tok.data_ptr(), None, stream) == -3
+    assert L.vit_forward(h, x.data_ptr(), 1, tok.data_ptr() + 4, None, stream) == -1   # misaligned tokens
+    assert L.vit_forward(h, None, 1, tok.data_ptr(), None, stream) == -1
+    assert L.vit_descriptor(h, tok.data_ptr(), 3, tok.data_ptr(), stream) == -3
+    assert L.vit_patch_scores(h, x.data_ptr(), x.data_ptr(), 1, 0, tok.data_ptr(), None, None, stream) == -5
+    assert "max_classes" in vit.vit_last_error()
+    torch.cuda.synchronize()
+    again = host(enc.forward(x[:2].contiguous(), tokens_out=tok[:2]))
+    enc.close()
+    np.testing.assert_array_equal(again, ref)
+
+
 def test_layerscale_zero_isolates_embedding_and_final_norm():
     # bf16-representable images: the patch embedding is then exact products summed in fp32
     cfg = synth.preset("vits16_224", layerscale=0.0, bf16_params=True, depth=2)
