@@ -70,7 +70,9 @@ def test_layernorm_every_supported_width(dim):
 SHAPES = [(1, 64, 64), (5, 150, 384), (130, 384, 384), (446, 1152, 384), (1000, 1536, 384), (257, 384, 1536),
           (4101, 1024, 128), (300, 96, 768),
           (3000, 3000, 640),   # 128 x 128 tiles, ragged in M and N
-          (4100, 8200, 192)]   # 256 x 256 tiles (M N >= 32M), ragged in M and N
+          (4100, 8200, 192),   # 256 x 256 tiles (M N >= 32M), ragged in M and N
+          # 128 x 128 tiles whose last full row tile also takes the 1..32 rows after it
+          (4101, 4096, 128), (4128, 3072, 192), (3969, 2048, 256), (4100, 1024, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

@@ -452,10 +452,18 @@ struct AMapConv3 {
   uint32_t bytes;  // size of `in` in bytes
 };
 
-template <int BM, int BN, int BKT, int WGM, int WGN, int S, class Epi, class AM = AMapLinear, class MT = MmaBf16>
+// XR = 32: the workgroups of row tile xt_tm also compute the 1..32 rows at the
+// end of A that follow the last full row tile (M mod BM <= 32), with the W tile
+// they already hold; each wave takes a 32 x 32 block of those rows, at the
+// columns of its wm-th 32-column block.  This saves a row of tiles that would
+// each stream a whole W tile for a few rows.  Row tile 0 takes them: it is
+// dispatched first, so its longer workgroups do not form the kernel's tail.
+template <int BM, int BN, int BKT, int WGM, int WGN, int S, class Epi, class AM = AMapLinear, class MT = MmaBf16,
+          int XR = 0>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t* __restrict__ A,
                                                                   const bf16_t* __restrict__ W, int M, int N, int K,
-                                                                  int tiles_m, int tiles_n, Epi epi, AM am = {}) {
+                                                                  int tiles_m, int tiles_n, Epi epi, AM am = {},
+                                                                  int xt_tm = -1) {
   constexpr int NW = WGM * WGN;                     // waves per workgroup
   constexpr int WTM = BM / WGM, WTN = BN / WGN;     // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;       // 32x32 blocks per wave
@@ -469,7 +477,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   constexpr int L = TOT / NW;                       // ... at least (the waits count these)
   constexpr bool A_SPLIT = A_INS % NW == 0;         // instruction i of every wave reads the same operand
   constexpr int KS = BKT / MT::KPM;                 // MFMA k-steps per stage
-  constexpr int STAGE_BYTES = (BM + BN) * BKT * ES;
+  constexpr int STAGE_BYTES = (BM + BN + XR) * BKT * ES;  // A rows, W rows, then the extra A rows
+  static_assert(XR == 0 || (XR == 32 && !HasRowLN<Epi>::value && !HasTransposed<Epi>::value && !AM::kConv &&
+                            WGM == 2 && WTN == 64 && XR / (64 / (BKT * MT::ES / 16)) <= WGM * WGN),
+                "extra rows: plain row epilogues, one 32-column block per wave");
   static_assert(CPR == 4 || CPR == 8 || CPR == 16, "BK");
   static_assert(!AM::kConv || ES == 2, "implicit convolution reads bf16 activations");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
@@ -482,6 +493,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+  const bool xt = XR > 0 && tm == xt_tm;  // workgroup-uniform
+  const int xr0 = tiles_m * BM;             // first of the extra rows
 
   static_assert(!AM::kConv || A_SPLIT, "implicit convolution needs whole A instructions per wave");
   uint32_t a_bytes = (uint32_t)((size_t)M * K * ES);
@@ -519,6 +532,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
       }
     }
   }
+  // extra rows: instruction x (of XR / RPI) is wave x's; LDS block TOT + x
+  uint32_t gx_off = 0;
+  if constexpr (XR > 0) {
+    const int row = wave * RPI + lane / CPR;
+    gx_off = (uint32_t)(xr0 + row) * (uint32_t)K * (uint32_t)ES + (uint32_t)swz_c<CPR>(row, lane % CPR) * 16u;
+  }
   auto issue = [&](auto stage, int kt) {
     const uint32_t blk = lds_addr(stage_lds<STAGE_BYTES, decltype(stage)::value>());
     const uint32_t koff = (uint32_t)kt * (BKT * ES);
@@ -548,19 +567,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
         dma16(is_a ? ra_src : rb_src, g_off[i] + koff, blk + (uint32_t)k * 1024u);
       }
     }
+    if constexpr (XR > 0) {
+      // rows past M come back as zeros through the range check
+      if (xt && wave_u < XR / RPI) dma16(ra_src, gx_off + koff, blk + (uint32_t)(TOT + wave_u) * 1024u);
+    }
   };
 
-  f32x16 acc[TM][TN];
+  f32x16 acc[TM][TN], acc_x;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc_x[e] = 0.f;
 
   const int KT = K / BKT;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  typename MT::Frag af[2][TM], bw[2][TN];
+  typename MT::Frag af[2][TM], bw[2][TN], ax[2];
   auto read = [&](auto stage, int buf, int ks) {
     const uint4* Ac = stage_lds<STAGE_BYTES, decltype(stage)::value>();
     const uint4* Bc = Ac + BM * CPR;
@@ -575,12 +600,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
       const int r = wn * WTN + j * 32 + lrow;
       bw[buf][j] = MT::frag(Bc[r * CPR + swz_c<CPR>(r, qd)], Bc[r * CPR + swz_c<CPR>(r, qd + MT::CPF - 1)]);
     }
+    if constexpr (XR > 0) {
+      if (xt) {
+        const uint4* Xc = Bc + BN * CPR;
+        ax[buf] = MT::frag(Xc[lrow * CPR + swz_c<CPR>(lrow, qd)], Xc[lrow * CPR + swz_c<CPR>(lrow, qd + MT::CPF - 1)]);
+      }
+    }
   };
   auto mma = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = MT::mma(af[buf][i], bw[buf][j], acc[i][j]);
+    // columns wn * WTN + wm * 32 + [0, 32): the wm-th of the wave's B blocks,
+    // chosen by a select (an index by the runtime wm would go through memory)
+    if constexpr (XR > 0) {
+      if (xt) acc_x = MT::mma(ax[buf], wm ? bw[buf][1] : bw[buf][0], acc_x);
+    }
   };
   // wait until at most `later` stages of this wave's loads are in flight
   // (the ones issued after the stage being waited for); with L the smaller
@@ -756,16 +792,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
     const int n_rd = lane_ok ? n : n0;
     const int nvalid_rd = lane_ok ? nvalid : min(4, N - n0);
     const typename Epi::Col cc = epi.col4(n_rd, nvalid_rd);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) stage[((e >> 2) * 8 + lhalf * 4 + (e & 3)) * LD + j * 32 + lrow] = acc[i][j][e];
-      __syncthreads();
+    // One staged 32-row block (rows row0 + [0, 32)): this lane's 4 columns at
+    // column nl (ok: inside the block and the matrix), with the read-side
+    // column nl_rd / count nv_rd and the column constants c.
+    auto emit = [&](int row0, int nl, int nv, bool ok, int nl_rd, int nv_rd, const typename Epi::Col& c) {
       float v[PASSES][4];
       typename Epi::Row rw[PASSES];
-      const int mb = m0 + wm * WTM + i * 32 + lane / LPR;
+      const int mb = row0 + lane / LPR;
 #pragma unroll
       for (int pass = 0; pass < PASSES; ++pass) {
         const int r = min(pass * RPP + lane / LPR, 31);
@@ -774,17 +807,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
         v[pass][1] = t.y;
         v[pass][2] = t.z;
         v[pass][3] = t.w;
-        rw[pass] = epi.pre(min(mb + pass * RPP, M - 1), n_rd, nvalid_rd);
+        rw[pass] = epi.pre(min(mb + pass * RPP, M - 1), nl_rd, nv_rd);
       }
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): every read of this block is in
 #pragma unroll
-      for (int pass = 0; pass < PASSES; ++pass) epi.finish4(v[pass], cc, rw[pass]);
+      for (int pass = 0; pass < PASSES; ++pass) epi.finish4(v[pass], c, rw[pass]);
 #pragma unroll
       for (int pass = 0; pass < PASSES; ++pass) {
         const int r = pass * RPP + lane / LPR;
-        if (lane_ok && r < 32 && mb + pass * RPP < M) write4_any(epi, mb + pass * RPP, n, v[pass], nvalid, cc, 0);
+        if (ok && r < 32 && mb + pass * RPP < M) write4_any(epi, mb + pass * RPP, nl, v[pass], nv, c, 0);
       }
+    };
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) stage[((e >> 2) * 8 + lhalf * 4 + (e & 3)) * LD + j * 32 + lrow] = acc[i][j][e];
       __syncthreads();
+      emit(m0 + wm * WTM + i * 32, n, nvalid, lane_ok, n_rd, nvalid_rd, cc);
+      __syncthreads();
+    }
+    if constexpr (XR > 0) {
+      if (xt) {  // workgroup-uniform
+        // the extra rows: staged in the first 32 columns of the wave's area
+#pragma unroll
+        for (int e = 0; e < 16; ++e) stage[((e >> 2) * 8 + lhalf * 4 + (e & 3)) * LD + lrow] = acc_x[e];
+        __syncthreads();
+        const int nx = n0 + wn * WTN + wm * 32 + cl;
+        const int nvx = min(4, N - nx);
+        const bool okx = lane < RPP * LPR && cl < 32 && nvx > 0;
+        const int nx_rd = okx ? nx : n0;
+        const int nvx_rd = okx ? nvx : min(4, N - n0);
+        const typename Epi::Col ccx = epi.col4(nx_rd, nvx_rd);
+        emit(xr0, nx, nvx, okx, nx_rd, nvx_rd, ccx);
+      }
     }
   }
 }
@@ -795,12 +852,30 @@ struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, S = S_;
 };
 
+// 128-row tiles with plain row epilogues can take up to 32 rows past the last
+// full row tile (see gemm_bf16_kernel's XR).
+template <class C, class Epi, class AM, class MT>
+constexpr bool takes_extra_rows() {
+  return C::BM == 128 && C::WGM == 2 && C::BN / C::WGN == 64 && !HasRowLN<Epi>::value && !HasTransposed<Epi>::value &&
+         !AM::kConv && std::is_same<MT, MmaBf16>::value;
+}
+
 template <class C, class Epi, class AM = AMapLinear, class MT = MmaBf16>
 hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s, AM am = {}) {
   const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
   if (K % C::BK != 0) return hipErrorInvalidValue;
+  if constexpr (takes_extra_rows<C, Epi, AM, MT>()) {
+    const int rem = M % C::BM;
+    if (M > C::BM && rem > 0 && rem <= 32) {  // row tile 0 also computes the rem rows after the last full one
+      const int full = M / C::BM;
+      hipLaunchKernelGGL((gemm_bf16_kernel<C::BM, C::BN, C::BK, C::WGM, C::WGN, C::S, Epi, AM, MT, 32>),
+                         dim3(full * tiles_n), dim3(64 * C::WGM * C::WGN), 0, s, A, W, M, N, K, full, tiles_n, epi, am,
+                         0);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemm_bf16_kernel<C::BM, C::BN, C::BK, C::WGM, C::WGN, C::S, Epi, AM, MT>), dim3(tiles_m * tiles_n),
-                     dim3(64 * C::WGM * C::WGN), 0, s, A, W, M, N, K, tiles_m, tiles_n, epi, am);
+                     dim3(64 * C::WGM * C::WGN), 0, s, A, W, M, N, K, tiles_m, tiles_n, epi, am, -1);
   return hipGetLastError();
 }
 
