@@ -342,7 +342,7 @@ def summarize_mfma(csv_path, simds=1024, clock_ghz=2.4):
         c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     B, N, D, Hm = 32, 446, 384, 1536
     M = B * N
-    ops = [("qkv", "EpiQKV", 2.0 * M * D * 3 * D), ("attention", "attention_kernel<4, false>", 4.0 * B * N * N * D),
+    ops = [("qkv", "EpiQKV", 2.0 * M * D * 3 * D), ("attention", "attention_kernel<4>", 4.0 * B * N * N * D),
            ("out_proj", "EpiResidualLN", 2.0 * M * D * D), ("fc1", "EpiGeluBf16", 2.0 * M * D * Hm),
            ("fc2", "EpiResidualLN", 2.0 * M * Hm * D)]
     print("| Op | dispatches | dispatch us | hardware GFLOP (MOPS x 512) | algorithmic GFLOP | MFMA instr. | "

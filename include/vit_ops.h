@@ -90,11 +90,10 @@ int vit_op_qkv(const void* h, const void* wqkv, const float* bqkv, int batch, in
  *   q, k, vt as produced by vit_op_qkv (the columns >= tokens of vt are
  *   ignored, whatever they hold); o [batch, tokens, heads*64] bf16 (heads
  *   merged in channel order).
- *   work, work_bytes: device scratch for fp32 partial results; with at least
- *   vit_op_attention_workspace(batch, tokens, heads) bytes the last, partly
- *   filled query tile of every head may be spread over key ranges (better
- *   load balance on long sequences).  NULL or too small: not spread.  The
- *   result is the same up to fp32 rounding of the merge. */
+ *   work, work_bytes: reserved; the kernel needs no scratch memory
+ *   (vit_op_attention_workspace returns 0 for every shape) and ignores them,
+ *   so NULL and 0 are fine.  Every query's output comes from one pass over
+ *   all keys, so an image's result does not depend on the batch it is in. */
 size_t vit_op_attention_workspace(int batch, int tokens, int heads);
 int vit_op_attention(const void* q, const void* k, const void* vt, int batch, int tokens, int heads,
                      void* o, void* work, size_t work_bytes, void* stream);

@@ -373,7 +373,7 @@ def test_graph_replay_matches_eager():
     """The forward (with taps and the descriptor) captured as a HIP graph and
     replayed on new inputs, with eager work and synchronisations between the
     replays, reproduces the eager results bit for bit on every replay
-    (DINOv2-S/14 @518, 1370 tokens: the attention tail split is in the graph)."""
+    (DINOv2-S/14 @518, 1370 tokens: a partly filled last query tile)."""
     cfg = synth.preset("vits14_518")
     say("graph replay, DINOv2-S/14 @518 b2 with taps")
     P = synth.make_params(cfg)

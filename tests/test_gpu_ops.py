@@ -215,12 +215,12 @@ def _attention_case(batch, tokens, heads, q_scale=1.0, k_spike=None, use_work=Tr
     return q, k, v, got
 
 
-# the last cases split the partly filled last query tile over key ranges
+# use_work passes a (reserved, ignored) scratch buffer; the result must not change
 @pytest.mark.parametrize("batch,tokens,heads,use_work", [
     (1, 1, 1, True), (1, 5, 1, True), (2, 31, 2, True), (1, 64, 1, True), (1, 65, 3, True), (2, 127, 1, True),
     (1, 129, 2, True), (2, 201, 6, True), (1, 446, 6, True), (1, 1370, 2, True), (1, 1370, 2, False),
     (1, 4101, 2, True), (1, 4101, 2, False), (2, 2053, 3, True), (1, 1100, 1, True),
-    # split tail of the last query tile: 33..64 rows (two waves), one row, none
+    # last query tile with 33..64 rows (two busy waves), one row, none
     (1, 1064, 2, True), (2, 1153, 1, True), (1, 1024, 1, True), (1, 1280, 2, True)])
 def test_attention_matches_oracle(batch, tokens, heads, use_work):
     say(f"attention batch={batch} tokens={tokens} heads={heads} work={use_work}")

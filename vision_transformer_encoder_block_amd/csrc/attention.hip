@@ -38,26 +38,19 @@ __device__ __forceinline__ int vt_tok(int p) { return (p & ~12) | ((p & 4) << 1)
 // ds_read_b128 cover all 64 banks.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// One workgroup: NW waves x 32 query rows starting at q_first + 32 NW qt (full
-// pass, qt from full_coords) or at q_first (partial pass), against the keys of
-// [key_first, key_end).  The full pass writes the normalised output; the
-// partial pass writes this key range's running max, sum and unnormalised
-// output per row, merged afterwards by combine_kernel.
+// One workgroup: NW waves x 32 query rows starting at 32 NW qt, against all
+// N keys; it writes the normalised output of its rows.
 struct AttnArgs {
   const bf16_t* Q;
   const bf16_t* K;
   const bf16_t* Vt;
   bf16_t* O;
-  float* part;     // partial pass: [B, H, splits, rows, 66] (m, l, o[64])
   int N, H, nv;
-  int q_first;     // first query row of the launch
-  int part_rows;   // partial pass: rows per (b, h) in `part`
-  int keys_per_split;
-  int qtiles;      // full pass: query tiles per (b, h); the grid is 1-D
+  int qtiles;      // query tiles per (b, h); the grid is 1-D
   int B;
 };
 
-// Full pass: workgroup id -> (query tile, head, image).  Workgroups are handed
+// Workgroup id -> (query tile, head, image).  Workgroups are handed
 // to the 8 XCDs round-robin by id; the ids are renumbered so that each XCD
 // gets a contiguous run of (image, head) pairs and all query tiles of a pair
 // meet the same K and V^T in that XCD's L2.
@@ -77,7 +70,7 @@ __device__ __forceinline__ void full_coords(int bid, int qtiles, int H, int B, i
 
 // At most 168 VGPRs (3 waves per SIMD): three 4-wave workgroups per CU keep
 // e.g. a ViT-S/16 @336 batch of 32 (768 workgroups) resident in one round.
-template <int NW, bool kPartial>
+template <int NW>
 __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a) {
   constexpr int S = 3;         // K / V^T tile stages in LDS
   constexpr int IPW = 8 / NW;  // DMA instructions per wave per K (or V^T) tile
@@ -87,22 +80,15 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
 
   const int N = a.N, H = a.H, nv = a.nv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int qt = 0, h, b;
-  if constexpr (kPartial) {
-    h = blockIdx.y, b = blockIdx.z;
-  } else {
-    full_coords(blockIdx.x, a.qtiles, H, a.B, qt, h, b);
-  }
+  int qt, h, b;
+  full_coords(blockIdx.x, a.qtiles, H, a.B, qt, h, b);
   const size_t bh = (size_t)b * H + h;
   const bf16_t* Qp = a.Q + bh * N * 64;
   const bf16_t* Kp = a.K + bh * N * 64;
   const bf16_t* Vp = a.Vt + bh * 64 * nv;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const int split = kPartial ? blockIdx.x : 0;
-  const int qrow = a.q_first + qt * 32 * NW + wave * 32 + lrow;
-  const bool idle = __builtin_amdgcn_readfirstlane(a.q_first + qt * 32 * NW + wave * 32) >= N;
-  const int key_first = kPartial ? split * a.keys_per_split : 0;
-  const int key_end = kPartial ? min(N, key_first + a.keys_per_split) : N;
+  const int qrow = qt * 32 * NW + wave * 32 + lrow;
+  const bool idle = __builtin_amdgcn_readfirstlane(qt * 32 * NW + wave * 32) >= N;
 
   // rows past N read as zeros through the buffer range checks
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qp, (uint32_t)N * 128u);
@@ -186,20 +172,18 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
     mneg[2] = lhalf == 0 ? h2 : (__bf16)0.f;
   };
 
-  // key ranges start on a tile boundary; only the global last tile is ragged
-  const int t_first = key_first / KT;
-  const int nt = (key_end + KT - 1) / KT - t_first;
+  const int nt = (N + KT - 1) / KT;  // key tiles; only the last is ragged
 #pragma unroll
   for (int i = 0; i < S - 1; ++i)
-    if (i < nt) issue(t_first + i, i);
-  // Every load so far is waited for here (tile t_first, which is needed, and
-  // the tiles issued with it): the explicit vmcnt(0) also tells the compiler
-  // that the Q fragments have landed, so it places no vmcnt waits for them in
-  // the loop, where they would also wait for the K / V^T tiles in flight.
+    if (i < nt) issue(i, i);
+  // Every load so far is waited for here (tile 0, which is needed, and the
+  // tiles issued with it): the explicit vmcnt(0) also tells the compiler that
+  // the Q fragments have landed, so it places no vmcnt waits for them in the
+  // loop, where they would also wait for the K / V^T tiles in flight.
   wait_vm<0>();
   barrier_keep_loads();
-  if ((t_first + 1) * KT > N) {
-    fix_last(t_first, 0);
+  if (KT > N) {
+    fix_last(0, 0);
     __syncthreads();
   }
 
@@ -209,7 +193,7 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
   // first and leaves the CU with fewer waves to hide latency for the rest.
   __builtin_amdgcn_s_setprio(3);
   for (int i = 0; i < nt; ++i) {
-    const int t = t_first + i;
+    const int t = i;
     if (4 * i >= nt && 4 * (i - 1) < nt) __builtin_amdgcn_s_setprio(2);
     if (2 * i >= nt && 2 * (i - 1) < nt) __builtin_amdgcn_s_setprio(1);
     if (4 * i >= 3 * nt && 4 * (i - 1) < 3 * nt) __builtin_amdgcn_s_setprio(0);
@@ -234,7 +218,7 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) vf[db][ks] = as_bf16x8(Vs[r * 8 + swz(r, ks * 2 + lhalf)]);
       }
-      // s = S^T - m_run (the first tile of the range runs with m_run = 0)
+      // s = S^T - m_run (the first tile runs with m_run = 0)
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -266,12 +250,12 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
       mt = half_swap_max(mt);
       // Lazy rescaling: the reference max m_run only moves (and O, l are only
       // rescaled) when some query's tile max exceeds it by more than 8, so
-      // p = 2^(s - m_run) <= 2^8; the first tile of the range always sets it.
+      // p = 2^(s - m_run) <= 2^8; the first tile always sets it.
       // Numerator and denominator share m_run, so the final O / l is unchanged.
       float shift = 0.f;
-      if (t == t_first || __builtin_amdgcn_ballot_w64(mt > 8.0f)) {
-        shift = t == t_first ? mt : fmaxf(mt, 0.f);
-        const float alpha = t == t_first ? 0.f : __builtin_amdgcn_exp2f(-shift);
+      if (t == 0 || __builtin_amdgcn_ballot_w64(mt > 8.0f)) {
+        shift = t == 0 ? mt : fmaxf(mt, 0.f);
+        const float alpha = t == 0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
         l_run *= alpha;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -323,130 +307,36 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
     }
   }
 
-  if constexpr (kPartial) {
-    // per row: max, sum (both halves) and the unnormalised output
-    const float l = half_swap_sum(l_run);
-    const int row_t = qrow - a.q_first;
-    if (qrow < N) {
-      float* pp = a.part + (((size_t)bh * gridDim.x + split) * a.part_rows + row_t) * 66;
-      if (lhalf == 0) {
-        pp[0] = m_run;
-        pp[1] = l;
+  const float l = half_swap_sum(l_run);
+  const float inv = 1.0f / l;
+  if (qrow < N) {
+    bf16_t* op = a.O + ((size_t)b * N + qrow) * (size_t)(H * 64) + h * 64;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = db * 32 + i * 8 + lhalf * 4;
+        uint2 u = make_uint2(pack_bf16x2(o[db][i * 4 + 0] * inv, o[db][i * 4 + 1] * inv),
+                             pack_bf16x2(o[db][i * 4 + 2] * inv, o[db][i * 4 + 3] * inv));
+        *reinterpret_cast<uint2*>(op + d) = u;
       }
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = db * 32 + i * 8 + lhalf * 4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pp[2 + d + j] = o[db][i * 4 + j];
-        }
-    }
-  } else {
-    const float l = half_swap_sum(l_run);
-    const float inv = 1.0f / l;
-    if (qrow < N) {
-      bf16_t* op = a.O + ((size_t)b * N + qrow) * (size_t)(H * 64) + h * 64;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = db * 32 + i * 8 + lhalf * 4;
-          uint2 u = make_uint2(pack_bf16x2(o[db][i * 4 + 0] * inv, o[db][i * 4 + 1] * inv),
-                               pack_bf16x2(o[db][i * 4 + 2] * inv, o[db][i * 4 + 3] * inv));
-          *reinterpret_cast<uint2*>(op + d) = u;
-        }
-    }
   }
-}
-
-// Merge the key-range partials of the tail rows: M = max m_i,
-// O = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.  One thread per (row, channel).
-__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part, int splits, int rows, int q_first,
-                                                     int N, int H, bf16_t* __restrict__ O) {
-  const int d = threadIdx.x;
-  const int row_t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const size_t bh = (size_t)b * H + h;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part[((bh * splits + s) * rows + row_t) * 66]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float* pp = part + ((bh * splits + s) * rows + row_t) * 66;
-    const float w = __builtin_amdgcn_exp2f(pp[0] - M);
-    L += w * pp[1];
-    acc += w * pp[2 + d];
-  }
-  O[((size_t)b * N + q_first + row_t) * (size_t)(H * 64) + h * 64 + d] = f2bf(acc / L);
-}
-
-// Tail split: on long sequences the last, partly filled query tile of every
-// head would run as a full-length workgroup that mostly idles and, on many
-// shapes, forms an extra round of workgroups (e.g. 4101 tokens x 16 heads =
-// 528 tiles on 256 CUs).  Its rows are instead processed against up to 16 key
-// ranges by small workgroups and merged by combine_kernel.  The decision and
-// the number of ranges depend on the sequence length only, so an image gives
-// bit-identical results at every batch size.
-constexpr int kMaxSplits = 16;
-constexpr int kSplitMinTokens = 1024;
-
-struct TailPlan {
-  int full_rows = 0;   // rows covered by the full-tile pass
-  int tail_rows = 0;   // rows handled by the split pass (< 128)
-  int waves = 0;       // waves per split workgroup (32 rows each)
-  int splits = 0;
-  int keys_per_split = 0;
-};
-
-TailPlan plan_tail(int tokens) {
-  TailPlan p;
-  p.full_rows = tokens;
-  const int full = tokens / QT, tail = tokens - full * QT;
-  if (tokens < kSplitMinTokens || tail == 0) return p;
-  p.full_rows = full * QT;
-  p.tail_rows = tail;
-  p.waves = tail <= 32 ? 1 : (tail <= 64 ? 2 : 4);
-  const int want = std::min(kMaxSplits, (tokens + KT - 1) / KT);
-  p.keys_per_split = ((tokens + want - 1) / want + KT - 1) / KT * KT;
-  p.splits = (tokens + p.keys_per_split - 1) / p.keys_per_split;
-  return p;
 }
 
 }  // namespace
 
-// Bytes of the split-pass partials (pure host function).
-size_t attention_workspace_bytes(int batch, int tokens, int heads) {
-  const TailPlan p = plan_tail(tokens);
-  return p.tail_rows ? (size_t)batch * heads * p.splits * p.tail_rows * 66 * sizeof(float) : 0;
-}
+// Every query tile runs against the whole key range in one pass (a partly
+// filled last tile included: its idle waves only take part in the loads and
+// barriers), so no workspace is needed.
+size_t attention_workspace_bytes(int, int, int) { return 0; }
 
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
-                            int heads, int nv, uint16_t* o, float* work, size_t work_bytes, hipStream_t s) {
+                            int heads, int nv, uint16_t* o, float*, size_t, hipStream_t s) {
   if (batch <= 0 || tokens <= 0 || heads <= 0 || nv < tokens || nv % 64 != 0) return hipErrorInvalidValue;
   if ((size_t)nv * 128 >= (1ull << 32)) return hipErrorInvalidValue;
-  TailPlan p = plan_tail(tokens);
-  if (p.tail_rows && (work == nullptr || work_bytes < attention_workspace_bytes(batch, tokens, heads))) {
-    p.full_rows = tokens;  // no workspace: the last tile stays in the main pass
-    p.tail_rows = 0;
-  }
-  const int qtiles = (p.full_rows + QT - 1) / QT;
-  AttnArgs a{q, k, vt, o, work, tokens, heads, nv, 0, 0, 0, qtiles, batch};
-  hipLaunchKernelGGL((attention_kernel<4, false>), dim3(qtiles * heads * batch), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.tail_rows == 0) return e;
-  a.q_first = p.full_rows;
-  a.part_rows = p.tail_rows;
-  a.keys_per_split = p.keys_per_split;
-  const dim3 pgrid(p.splits, heads, batch);
-  if (p.waves == 1)
-    hipLaunchKernelGGL((attention_kernel<1, true>), pgrid, dim3(64), 0, s, a);
-  else if (p.waves == 2)
-    hipLaunchKernelGGL((attention_kernel<2, true>), pgrid, dim3(128), 0, s, a);
-  else
-    hipLaunchKernelGGL((attention_kernel<4, true>), pgrid, dim3(256), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(p.tail_rows, heads, batch), dim3(64), 0, s, (const float*)work, p.splits,
-                     p.tail_rows, p.full_rows, tokens, heads, o);
+  const int qtiles = (tokens + QT - 1) / QT;
+  AttnArgs a{q, k, vt, o, tokens, heads, nv, qtiles, batch};
+  hipLaunchKernelGGL((attention_kernel<4>), dim3(qtiles * heads * batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

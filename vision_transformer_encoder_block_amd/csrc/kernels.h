@@ -111,8 +111,8 @@ hipError_t launch_assemble(float* x, int batch, int tokens, int dim, const float
 hipError_t launch_pos_resample(const float* pos_in, int gh, int gw, float* pos_out, int th, int tw, int dim,
                                hipStream_t s);
 
-// Attention core (see vit_op_attention).  `work` (fp32 partials of the tail
-// split) may be null, in which case the split is not used.
+// Attention core (see vit_op_attention).  `work` / `work_bytes` are reserved:
+// the kernel needs no workspace (attention_workspace_bytes returns 0).
 size_t attention_workspace_bytes(int batch, int tokens, int heads);
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
                             int heads, int nv, uint16_t* o, float* work, size_t work_bytes, hipStream_t s);

@@ -81,8 +81,7 @@ struct WeightLayout {
 };
 
 struct WorkLayout {
-  size_t x, h, q, k, vt, o, f, cols, attn, crops, feats, clsb, cos, corners, total;
-  size_t attn_bytes;
+  size_t x, h, q, k, vt, o, f, cols, crops, feats, clsb, cos, corners, total;
   int ldc_cos;
 };
 
@@ -234,9 +233,6 @@ int build_plan(const vit_config* c, Plan& pl) {
   s.o = take(rows * D * 2);
   s.f = take(rows * Hm * 2);
   s.cols = take(prows * pl.kpad * 2);
-  s.attn_bytes = std::max(vit::attention_workspace_bytes(c->max_batch, pl.main.N, pl.heads),
-                          pl.nwin ? vit::attention_workspace_bytes(pl.nwin, pl.win.N, pl.heads) : (size_t)0);
-  s.attn = take(std::max<size_t>(s.attn_bytes, 4));
   s.ldc_cos = round_up(std::max(c->max_classes, 1), 4);
   if (c->max_classes > 0) {
     const size_t frows = std::max((size_t)pl.main.P, prow_win);
@@ -275,7 +271,6 @@ struct vit_model {
   std::vector<BlockW> blocks;
   float* x = nullptr;
   uint16_t *h = nullptr, *q = nullptr, *k = nullptr, *vt = nullptr, *o = nullptr, *f = nullptr, *cols = nullptr;
-  float* attn = nullptr;
   float *crops = nullptr, *cos = nullptr;
   uint16_t *feats = nullptr, *clsb = nullptr;
   int* corners = nullptr;
@@ -322,7 +317,7 @@ int run_encoder(vit_model* m, const Geom& g, const float* images, int batch, flo
     eq.heads = pl.heads;
     eq.nv = g.nv;
     VIT_HIP(vit::launch_gemm(m->h, w.wqkv, M, 3 * D, D, eq, st), "qkv");
-    VIT_HIP(vit::launch_attention(m->q, m->k, m->vt, batch, N, pl.heads, g.nv, m->o, m->attn, pl.ws.attn_bytes, st),
+    VIT_HIP(vit::launch_attention(m->q, m->k, m->vt, batch, N, pl.heads, g.nv, m->o, nullptr, 0, st),
             "attention");
     vit::EpiParams eo;
     eo.kind = fuse_ln ? vit::EPI_RESIDUAL_LN : vit::EPI_RESIDUAL;
@@ -520,7 +515,6 @@ int vit_create(const vit_config* cfg, const float* host_params, size_t host_floa
   m->o = (uint16_t*)(S + ws.o);
   m->f = (uint16_t*)(S + ws.f);
   m->cols = (uint16_t*)(S + ws.cols);
-  m->attn = (float*)(S + ws.attn);
   if (pl.cfg.max_classes > 0) {
     m->crops = pl.nwin ? (float*)(S + ws.crops) : nullptr;
     m->feats = (uint16_t*)(S + ws.feats);
