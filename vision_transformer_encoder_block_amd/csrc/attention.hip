@@ -192,7 +192,9 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
   // arbiter otherwise favours the oldest waves; their workgroup finishes
   // first and leaves the CU with fewer waves to hide latency for the rest.
   __builtin_amdgcn_s_setprio(3);
-  for (int i = 0; i < nt; ++i) {
+  // One key tile; the first is peeled off the loop (first == true: the tile
+  // max always sets m_run).
+  auto step = [&](int i, bool first) __attribute__((always_inline)) {
     const int t = i;
     if (4 * i >= nt && 4 * (i - 1) < nt) __builtin_amdgcn_s_setprio(2);
     if (2 * i >= nt && 2 * (i - 1) < nt) __builtin_amdgcn_s_setprio(1);
@@ -205,88 +207,115 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
       // S^T for keys t*64 + kb*32 + [0, 32): element e <-> key 8*(e/4) + 4*lhalf + e%4.
       // All K fragments are read before the MFMAs, and the V fragments right
       // after them, so the LDS latency of both hides under MFMA and softmax work.
-      bf16x8 kf[2][4], vf[2][4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int r = kb * 32 + lrow;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kf[kb][ks] = as_bf16x8(Ks[r * 8 + swz(r, ks * 2 + lhalf)]);
-      }
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const int r = db * 32 + lrow;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) vf[db][ks] = as_bf16x8(Vs[r * 8 + swz(r, ks * 2 + lhalf)]);
-      }
-      // s = S^T - m_run (the first tile runs with m_run = 0)
+      bf16x8 vf[2][4];
       f32x16 s[2];
+      // s = S^T - m_run (the first tile runs with m_run = 0); keys past N
+      // (last tile only) get -inf.  The V fragments are read right after the
+      // K fragments on the first call.
+      auto logits = [&](bool read_v) {
+        bf16x8 kf[2][4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
+          const int r = kb * 32 + lrow;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+          for (int ks = 0; ks < 4; ++ks) kf[kb][ks] = as_bf16x8(Ks[r * 8 + swz(r, ks * 2 + lhalf)]);
+        }
+        if (read_v) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) s[kb] = mfma32x32x16(kf[kb][ks], qf[ks], s[kb]);
-        s[kb] = mfma32x32x16(ones, mneg, s[kb]);
-      }
-      if ((t + 1) * KT > N) {
+          for (int db = 0; db < 2; ++db) {
+            const int r = db * 32 + lrow;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int ks = 0; ks < 4; ++ks) vf[db][ks] = as_bf16x8(Vs[r * 8 + swz(r, ks * 2 + lhalf)]);
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) s[kb] = mfma32x32x16(kf[kb][ks], qf[ks], s[kb]);
+          s[kb] = mfma32x32x16(ones, mneg, s[kb]);
+        }
+        if ((t + 1) * KT > N) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int key = t * KT + kb * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
+              if (key >= N) s[kb][e] = -INFINITY;
+            }
+        }
+      };
+      // probabilities p = 2^s, packed as the B operand of the 4 key steps of
+      // P V; returns this lane's sum of its 32 (a tree of pairwise adds)
+      bf16x8 pf[4];
+      auto probs = [&]() {
+        float ps[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[kb][half * 8 + e]);
+            ps[kb * 2 + half] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            uint4 u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                 pack_bf16x2(p[6], p[7]));
+            pf[kb * 2 + half] = as_bf16x8(u);
+          }
+        }
+        return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      };
+      // The tile max moves the reference max m_run (and rescales O and l)
+      // only when some query's tile max exceeds it by more than 8, so every
+      // p = 2^(s - m_run) <= 2^8; the first tile always sets it.  Numerator and
+      // denominator share m_run, so the final O / l is unchanged.
+      auto rescale_by_max = [&]() {
+        // tile max of this lane's 32 logits: maxima of groups of three
+        // (v_max3_f32), then of the group maxima (17 instructions, depth 4)
+        auto sv = [&](int f) { return s[f >> 4][f & 15]; };
+        float g3[11];
+#pragma unroll
+        for (int i = 0; i < 10; ++i) g3[i] = fmaxf(fmaxf(sv(3 * i), sv(3 * i + 1)), sv(3 * i + 2));
+        g3[10] = fmaxf(sv(30), sv(31));
+        const float u0 = fmaxf(fmaxf(g3[0], g3[1]), g3[2]), u1 = fmaxf(fmaxf(g3[3], g3[4]), g3[5]);
+        const float u2 = fmaxf(fmaxf(g3[6], g3[7]), g3[8]), u3 = fmaxf(g3[9], g3[10]);
+        float mt = fmaxf(fmaxf(fmaxf(u0, u1), u2), u3);
+        mt = half_swap_max(mt);
+        if (t == 0 || __builtin_amdgcn_ballot_w64(mt > 8.0f)) {
+          const float shift = t == 0 ? mt : fmaxf(mt, 0.f);
+          const float alpha = t == 0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
+          l_run *= alpha;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int key = t * KT + kb * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
-            if (key >= N) s[kb][e] = -INFINITY;
+            o[0][e] *= alpha;
+            o[1][e] *= alpha;
           }
-      }
-      // tile max of this lane's 32 logits: maxima of groups of three
-      // (v_max3_f32), then of the group maxima (17 instructions, depth 4)
-      auto sv = [&](int f) { return s[f >> 4][f & 15]; };
-      float g3[11];
+          m_run += shift;
+          set_mneg(m_run);
 #pragma unroll
-      for (int i = 0; i < 10; ++i) g3[i] = fmaxf(fmaxf(sv(3 * i), sv(3 * i + 1)), sv(3 * i + 2));
-      g3[10] = fmaxf(sv(30), sv(31));
-      const float u0 = fmaxf(fmaxf(g3[0], g3[1]), g3[2]), u1 = fmaxf(fmaxf(g3[3], g3[4]), g3[5]);
-      const float u2 = fmaxf(fmaxf(g3[6], g3[7]), g3[8]), u3 = fmaxf(g3[9], g3[10]);
-      float mt = fmaxf(fmaxf(fmaxf(u0, u1), u2), u3);
-      mt = half_swap_max(mt);
-      // Lazy rescaling: the reference max m_run only moves (and O, l are only
-      // rescaled) when some query's tile max exceeds it by more than 8, so
-      // p = 2^(s - m_run) <= 2^8; the first tile always sets it.
-      // Numerator and denominator share m_run, so the final O / l is unchanged.
-      float shift = 0.f;
-      if (t == 0 || __builtin_amdgcn_ballot_w64(mt > 8.0f)) {
-        shift = t == 0 ? mt : fmaxf(mt, 0.f);
-        const float alpha = t == 0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
-        l_run *= alpha;
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          o[0][e] *= alpha;
-          o[1][e] *= alpha;
+            for (int e = 0; e < 16; ++e) s[kb][e] -= shift;
         }
-        m_run += shift;
-        set_mneg(m_run);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) s[kb][e] -= shift;
+      };
+      // After the first tile, probabilities first, against the current m_run:
+      // the tile max is only needed when some p may exceed 2^8, and a lane's
+      // sum of its 32 p exceeding 2^8 is necessary for that (rare once m_run
+      // has settled).  Such a tile is recomputed from the K tile still in
+      // LDS, with the max-based rescale above; as the rescale decision is the
+      // max test either way, the results do not depend on which path ran.
+      logits(true);
+      float lsum = first ? 0.f : probs();
+      if (first || __builtin_amdgcn_ballot_w64(lsum > 256.0f)) {
+        // read K again rather than keep s or the K fragments in registers
+        // through the fast path (the clobber stops the compiler reusing them)
+        asm volatile("" ::: "memory");
+        logits(false);
+        rescale_by_max();
+        lsum = probs();
       }
-      // probabilities, packed as the B operand of the 4 key steps of P V; their
-      // sum as a tree of pairwise adds
-      bf16x8 pf[4];
-      float ps[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float p[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[kb][half * 8 + e]);
-          ps[kb * 2 + half] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-          uint4 u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                               pack_bf16x2(p[6], p[7]));
-          pf[kb * 2 + half] = as_bf16x8(u);
-        }
-      }
-      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      l_run += lsum;
       // O^T[d, q] += V^T[d, keys] P^T[keys, q]; d = db*32 + row of the MFMA
 #pragma unroll
       for (int db = 0; db < 2; ++db)
@@ -305,7 +334,9 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
         __syncthreads();
       }
     }
-  }
+  };
+  step(0, true);
+  for (int i = 1; i < nt; ++i) step(i, false);
 
   const float l = half_swap_sum(l_run);
   const float inv = 1.0f / l;
