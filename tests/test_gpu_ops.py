@@ -234,16 +234,46 @@ def test_attention_matches_oracle(batch, tokens, heads, use_work):
             assert np.all(err <= 2 ** -8 * np.abs(ref) + 2 ** -7 * vmax), (b, h, err.max())
 
 
-def test_attention_large_logits_stay_finite():
+# the spike in the first key tile, or in the third (it then moves the running max mid-row)
+@pytest.mark.parametrize("spike", [3, 150])
+def test_attention_large_logits_stay_finite(spike):
     # spike logit ~ 64 * 5000 * 8 * ln2 = 1.8e6, far beyond fp16's 65504; it wins every row
-    say("attention large logits")
-    q, k, v, got = _attention_case(1, 200, 2, q_scale=5000.0, k_spike=3)
+    say(f"attention large logits, spike at key {spike}")
+    q, k, v, got = _attention_case(1, 200, 2, q_scale=5000.0, k_spike=spike)
     assert np.isfinite(got).all()
     for h in range(2):
         ref, smax = O.sdpa(q[0, h], k[0, h], v[0, h], math.log(2.0))
         assert smax > 1e6
-        np.testing.assert_array_equal(ref, np.broadcast_to(v[0, h, 3], ref.shape))
+        np.testing.assert_array_equal(ref, np.broadcast_to(v[0, h, spike], ref.shape))
         np.testing.assert_allclose(got[0, :, h], ref, atol=2 ** -8 * np.abs(ref).max() + 1e-6)
+
+
+# Logits (log2 units) about `jump` higher in every key tile after the first, for
+# every query: 5 leaves each p <= 2^8 but lane sums of 32 p far above 2^8; 12
+# and 40 exceed the running max by more than 8 and move it on the second tile.
+@pytest.mark.parametrize("jump", [5.0, 12.0, 40.0])
+def test_attention_rising_logits(jump):
+    say(f"attention rising logits, jump {jump}")
+    batch, tokens, heads = 1, 300, 2
+    e = RNG.choice([-1.0, 1.0], size=64)
+    qr = e + 0.05 * RNG.standard_normal((batch, heads, tokens, 64))
+    kr = 0.02 * RNG.standard_normal((batch, heads, tokens, 64))
+    kr[:, :, 64:] += jump / 64.0 * e
+    vr = RNG.standard_normal((batch, heads, tokens, 64))
+    nv = (tokens + 63) // 64 * 64
+    q_d, q = bf16_dev(qr)
+    k_d, k = bf16_dev(kr)
+    v_d, v = bf16_dev(vr)
+    vt = torch.zeros((batch, heads, 64, nv), dtype=torch.bfloat16, device="cuda")
+    vt[:, :, :, torch.from_numpy(vt_position(np.arange(tokens))).cuda()] = v_d.transpose(2, 3)
+    o = torch.empty((batch, tokens, heads * 64), dtype=torch.bfloat16, device="cuda")
+    vit.vit_op_attention(q_d, k_d, vt, batch, tokens, heads, o, None)
+    got = host(o).reshape(batch, tokens, heads, 64)
+    for h in range(heads):
+        ref, _ = O.sdpa(q[0, h], k[0, h], v[0, h], math.log(2.0))
+        vmax = np.abs(v[0, h]).max()
+        err = np.abs(got[0, :, h] - ref)
+        assert np.all(err <= 2 ** -8 * np.abs(ref) + 2 ** -7 * vmax), (h, err.max())
 
 
 # ------------------------------------------------------------------ frame preprocessing
