@@ -162,7 +162,10 @@ def test_linear_residual_ln(M, K):
 
 # ------------------------------------------------------------------ QKV head split
 
-@pytest.mark.parametrize("batch,tokens,heads", [(1, 5, 1), (2, 201, 6), (1, 446, 6), (3, 70, 2)])
+# the last three: 128-row tiles with a ragged last row tile of 5, 32 and 5 rows
+# (ViT-L/16 @1024 b1), V^T columns included
+@pytest.mark.parametrize("batch,tokens,heads", [(1, 5, 1), (2, 201, 6), (1, 446, 6), (3, 70, 2),
+                                                (1, 133, 16), (2, 80, 10), (1, 4101, 16)])
 def test_qkv_split(batch, tokens, heads):
     say(f"qkv batch={batch} tokens={tokens} heads={heads}")
     D = 64 * heads
