@@ -165,4 +165,18 @@ __host__ __device__ __forceinline__ void bilinear_tap(int i, int n_in, int n_out
   i1 = i0 + 1 < n_in - 1 ? i0 + 1 : n_in - 1;
 }
 
+// Division by a runtime constant for 0 <= n < 2^31 (multiply-high + shift).
+struct FastDiv {
+  uint32_t mul, shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1u << s) < d) ++s;
+  uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1;
+  return FastDiv{uint32_t(m), s};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.mul) + n) >> f.shift; }
+
 }  // namespace vit

@@ -9,22 +9,47 @@
 namespace vit {
 namespace {
 
-// One thread writes 8 consecutive columns (16 bytes) of one patch row.  The
-// (c, ky, kx) of the first column is decoded once and then stepped; when the
-// 8 columns lie in one image row (vec4: p a multiple of 8, W a multiple of 4
-// and img 16-byte aligned, checked on the host) they are two float4 loads.
-__global__ __launch_bounds__(256) void patchify_kernel(const float* __restrict__ img, int batch, int H, int W, int p,
-                                                       int kpad, bool vec4, bf16_t* __restrict__ out) {
-  const int gw = W / p, gh = H / p;
-  const int chunks = kpad / 8;
-  const size_t total = (size_t)batch * gh * gw * chunks;
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int ch = (int)(idx % chunks);
-  const size_t prow = idx / chunks;
-  const int gx = (int)(prow % gw);
-  const int gy = (int)((prow / gw) % gh);
-  const int b = (int)(prow / ((size_t)gw * gh));
+struct PatchArgs {
+  const float* img;
+  bf16_t* out;
+  int H, W, p, kpad, gw, gh;
+  uint32_t per_image;   // patch rows x 16-byte chunks of one image
+  int patch_blocks;     // workgroups per image for the patch matrix
+  FastDiv div_chunks, div_gw, div_pp, div_p;
+  bool vec4;
+  // token rows 0..regs (null x: none)
+  float* x;
+  int tokens, dim, regs;
+  const float* cls;
+  const float* pos0;
+  const float* reg;
+};
+
+// grid (patch_blocks [+ 1 + regs], batch).  In the patch blocks one thread
+// writes 8 consecutive columns (16 bytes) of one patch row.  The (c, ky, kx)
+// of the first column is decoded once and then stepped; when the 8 columns
+// lie in one image row (vec4: p a multiple of 8, W a multiple of 4 and img
+// 16-byte aligned, checked on the host) they are two float4 loads.  Index
+// arithmetic is 32-bit with multiply-high divisions (per-image counts below
+// 2^31, checked on the host).  The blocks after them write the CLS row (CLS +
+// pos[0]) and the register rows of the token sequence, which the patch
+// embedding GEMM leaves alone.
+__global__ __launch_bounds__(256) void patchify_kernel(PatchArgs a) {
+  const int b = blockIdx.y;
+  if ((int)blockIdx.x >= a.patch_blocks) {
+    const int r = blockIdx.x - a.patch_blocks;  // 0 = CLS, 1..regs = registers
+    float* row = a.x + ((size_t)b * a.tokens + r) * a.dim;
+    for (int c = threadIdx.x; c < a.dim; c += blockDim.x)
+      row[c] = r == 0 ? a.cls[c] + a.pos0[c] : a.reg[(size_t)(r - 1) * a.dim + c];
+    return;
+  }
+  const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
+  if (idx >= a.per_image) return;
+  const int p = a.p, W = a.W, H = a.H;
+  const uint32_t prow = fdiv(idx, a.div_chunks);
+  const int ch = (int)(idx - prow * (uint32_t)(a.kpad / 8));
+  const uint32_t gy = fdiv(prow, a.div_gw);
+  const int gx = (int)(prow - gy * (uint32_t)a.gw);
   const int kvalid = 3 * p * p;
   const int k0 = ch * 8;
   float v[8];
@@ -32,11 +57,11 @@ __global__ __launch_bounds__(256) void patchify_kernel(const float* __restrict__
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = 0.f;
   } else {
-    int c = k0 / (p * p);
-    int r = k0 - c * p * p;
-    int ky = r / p, kx = r - ky * p;
-    const float* base = img + (size_t)b * 3 * H * W + (size_t)(gy * p) * W + gx * p;
-    if (vec4 && k0 + 8 <= kvalid) {
+    int c = (int)fdiv((uint32_t)k0, a.div_pp);
+    const int r = k0 - c * p * p;
+    int ky = (int)fdiv((uint32_t)r, a.div_p), kx = r - ky * p;
+    const float* base = a.img + (size_t)b * 3 * H * W + (size_t)(gy * p) * W + gx * p;
+    if (a.vec4 && k0 + 8 <= kvalid) {
       const float4* src = reinterpret_cast<const float4*>(base + ((size_t)c * H + ky) * W + kx);
       const float4 lo = src[0], hi = src[1];
       v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
@@ -57,17 +82,7 @@ __global__ __launch_bounds__(256) void patchify_kernel(const float* __restrict__
   }
   uint4 u = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                        pack_bf16x2(v[6], v[7]));
-  *reinterpret_cast<uint4*>(out + prow * kpad + ch * 8) = u;
-}
-
-__global__ __launch_bounds__(256) void assemble_kernel(float* __restrict__ x, int tokens, int dim,
-                                                       const float* __restrict__ cls, const float* __restrict__ pos0,
-                                                       const float* __restrict__ reg, int regs) {
-  const int b = blockIdx.y;
-  const int r = blockIdx.x;  // 0 = CLS, 1..regs = registers
-  float* row = x + ((size_t)b * tokens + r) * dim;
-  for (int c = threadIdx.x; c < dim; c += blockDim.x)
-    row[c] = r == 0 ? cls[c] + pos0[c] : reg[(size_t)(r - 1) * dim + c];
+  *reinterpret_cast<uint4*>(a.out + ((size_t)b * a.gh * a.gw + prow) * a.kpad + ch * 8) = u;
 }
 
 // Cubic-convolution weight (a = -0.75) of a tap at distance d.
@@ -225,19 +240,28 @@ __global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_patchify(const float* img, int batch, int H, int W, int p, int kpad, uint16_t* out,
+hipError_t launch_patchify(const float* img, int batch, int H, int W, int p, int kpad, uint16_t* out, float* x,
+                           int tokens, int dim, const float* cls, const float* pos0, const float* reg, int regs,
                            hipStream_t s) {
-  if (kpad % 8 != 0 || kpad < 3 * p * p) return hipErrorInvalidValue;
-  const size_t total = (size_t)batch * (H / p) * (W / p) * (kpad / 8);
-  const bool vec4 = (p % 8) == 0 && (W % 4) == 0 && (reinterpret_cast<uintptr_t>(img) % 16) == 0;
-  hipLaunchKernelGGL(patchify_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, img, batch, H, W, p,
-                     kpad, vec4, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_assemble(float* x, int batch, int tokens, int dim, const float* cls, const float* pos0,
-                           const float* reg, int regs, hipStream_t s) {
-  hipLaunchKernelGGL(assemble_kernel, dim3(1 + regs, batch), dim3(256), 0, s, x, tokens, dim, cls, pos0, reg, regs);
+  if (batch < 1 || batch > 65535 || p < 1 || kpad % 8 != 0 || kpad < 3 * p * p || regs < 0) return hipErrorInvalidValue;
+  const int gw = W / p, gh = H / p;
+  const size_t per_image = (size_t)gh * gw * (kpad / 8);
+  if (per_image >= (1ull << 31)) return hipErrorInvalidValue;
+  PatchArgs a{};
+  a.img = img;
+  a.out = reinterpret_cast<bf16_t*>(out);
+  a.H = H, a.W = W, a.p = p, a.kpad = kpad, a.gw = gw, a.gh = gh;
+  a.per_image = (uint32_t)per_image;
+  a.patch_blocks = (int)((per_image + 255) / 256);
+  a.div_chunks = make_fastdiv((uint32_t)(kpad / 8));
+  a.div_gw = make_fastdiv((uint32_t)(gw > 0 ? gw : 1));
+  a.div_pp = make_fastdiv((uint32_t)(p * p));
+  a.div_p = make_fastdiv((uint32_t)p);
+  a.vec4 = (p % 8) == 0 && (W % 4) == 0 && (reinterpret_cast<uintptr_t>(img) % 16) == 0;
+  a.x = x, a.tokens = tokens, a.dim = dim, a.regs = regs, a.cls = cls, a.pos0 = pos0, a.reg = reg;
+  const int blocks = a.patch_blocks + (x ? 1 + regs : 0);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(patchify_kernel, dim3((unsigned)blocks, (unsigned)batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -31,20 +31,6 @@ namespace {
 
 constexpr int BK = 64;
 
-// Division by a runtime constant for 0 <= n < 2^31 (multiply-high + shift).
-struct FastDiv {
-  uint32_t mul, shift;
-};
-
-FastDiv make_fastdiv(uint32_t d) {
-  uint32_t s = 0;
-  while ((1u << s) < d) ++s;
-  uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1;
-  return FastDiv{uint32_t(m), s};
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.mul) + n) >> f.shift; }
-
 // Column of token t in vt: bits 2 and 3 exchanged (see vit_op_qkv).
 __device__ __forceinline__ int vt_pos(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 

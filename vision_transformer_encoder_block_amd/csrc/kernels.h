@@ -98,13 +98,12 @@ hipError_t launch_preprocess(const uint8_t* frames, int batch, int sh, int sw, b
                              hipStream_t s);
 
 // im2col of fp32 images [batch, 3, H, W] into bf16 [batch * gh * gw, kpad]
-// with columns in (c, ky, kx) order, zero beyond 3 p^2.
-hipError_t launch_patchify(const float* img, int batch, int H, int W, int p, int kpad, uint16_t* out,
+// with columns in (c, ky, kx) order, zero beyond 3 p^2.  With x non-null the
+// same launch also writes token rows 0..regs of every image of x [batch,
+// tokens, dim]: CLS + pos0, then the registers reg [regs, dim].
+hipError_t launch_patchify(const float* img, int batch, int H, int W, int p, int kpad, uint16_t* out, float* x,
+                           int tokens, int dim, const float* cls, const float* pos0, const float* reg, int regs,
                            hipStream_t s);
-
-// Rows 0..R of every image: CLS + pos[0], then the registers.
-hipError_t launch_assemble(float* x, int batch, int tokens, int dim, const float* cls, const float* pos0,
-                           const float* reg, int regs, hipStream_t s);
 
 // Bicubic (a = -0.75, half-pixel centres, clamped taps) resampling of the
 // patch rows of a position table; row 0 copied.

@@ -287,7 +287,10 @@ int run_encoder(vit_model* m, const Geom& g, const float* images, int batch, flo
   const int D = pl.D, Hm = pl.Hm, N = g.N;
   const int M = batch * N;
   const float eps = pl.cfg.ln_eps;
-  VIT_HIP(vit::launch_patchify(images, batch, g.img_h, g.img_w, pl.p, pl.kpad, m->cols, st), "patchify");
+  // im2col of the images, and the CLS and register rows of x (the patch GEMM writes the others)
+  VIT_HIP(vit::launch_patchify(images, batch, g.img_h, g.img_w, pl.p, pl.kpad, m->cols, m->x, N, D, m->cls, g.pos,
+                               m->reg, pl.R, st),
+          "patchify");
   vit::EpiParams pe;
   pe.kind = vit::EPI_PATCH;
   pe.bias = m->patch_b;
@@ -298,7 +301,6 @@ int run_encoder(vit_model* m, const Geom& g, const float* images, int batch, flo
   pe.patches = g.P;
   pe.regs = pl.R;
   VIT_HIP(vit::launch_gemm(m->cols, m->patch_w, batch * g.P, D, pl.kpad, pe, st), "patch embedding");
-  VIT_HIP(vit::launch_assemble(m->x, batch, N, D, m->cls, g.pos, m->reg, pl.R, st), "token assembly");
   int tap_i = 0;
   // For D = 384 the residual GEMMs also apply the LayerNorm that follows them
   // (out projection -> LN2, fc2 -> LN1 of the next block), so h arrives ready.
