@@ -16,7 +16,10 @@
 // running max and sum all fp32: logits of ~2.5e6 (the DINOv3 attention sink)
 // stay finite.  The reference max m is moved lazily (only when a tile max
 // exceeds it by more than 8), which keeps every p <= 2^8 and skips most
-// rescales of the output accumulators.
+// rescales of the output accumulators.  After the first tile the
+// probabilities are formed before any tile max; the max is taken (and the
+// tile recomputed) only where a lane's sum of p exceeds 2^8, which any p above
+// 2^8 implies, so the outputs are those of the max-first order.
 // K and V^T tiles of 64 keys are staged in LDS (double-buffered, 16-byte
 // chunks XOR-swizzled by row) and shared by the 4 waves of a workgroup; rows
 // past the sequence end are read as zeros through buffer range checks.
