@@ -73,7 +73,7 @@ typedef struct vit_config {
   float ln_eps;              /* LayerNorm epsilon (1e-6) */
   unsigned tap_mask;         /* bit l-1 set: emit a tap after block l (l <= depth + extra_blocks) */
   int pos_grid_h, pos_grid_w;/* grid of the stored position table (1 + gh*gw rows) */
-  int window, window_stride; /* slide-mode window side and stride in pixels; 0 = no slide mode */
+  int window, window_stride; /* slide-mode window side and stride in pixels (1 <= stride <= window); 0 = no slide mode */
   int max_classes;           /* largest class count for vit_patch_scores; 0 = no scoring */
 } vit_config;
 

@@ -89,14 +89,11 @@ int vit_op_qkv(const void* h, const void* wqkv, const float* bqkv, int batch, in
  * the logits stay fp32, model card "Build BF16, not FP16").
  *   q, k, vt as produced by vit_op_qkv (the columns >= tokens of vt are
  *   ignored, whatever they hold); o [batch, tokens, heads*64] bf16 (heads
- *   merged in channel order).
- *   work, work_bytes: reserved; the kernel needs no scratch memory
- *   (vit_op_attention_workspace returns 0 for every shape) and ignores them,
- *   so NULL and 0 are fine.  Every query's output comes from one pass over
- *   all keys, so an image's result does not depend on the batch it is in. */
-size_t vit_op_attention_workspace(int batch, int tokens, int heads);
+ *   merged in channel order).  No scratch memory is used.  Every query's
+ *   output comes from one pass over all keys, so an image's result does not
+ *   depend on the batch it is in. */
 int vit_op_attention(const void* q, const void* k, const void* vt, int batch, int tokens, int heads,
-                     void* o, void* work, size_t work_bytes, void* stream);
+                     void* o, void* stream);
 
 /* ---- low-precision (fp8) linear layer -------------------------------------
  * The encoder's Linear layers (LibreYOLO DINOv2 diagram, "Encoder block") with

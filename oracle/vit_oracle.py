@@ -153,6 +153,11 @@ def softmax_rows(s: np.ndarray) -> np.ndarray:
         return e / e.sum(axis=-1, keepdims=True)
 
 
+def attention_weights(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """One head's softmax over keys of scale * q k^T: [N, M], rows summing to 1."""
+    return softmax_rows((q @ k.T) * scale)
+
+
 def sdpa(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, logit_format: str | None = None):
     """One head: softmax over keys of scale * q k^T, times v; q [N, c], k [M, c], v [M, c'].
 

@@ -9,6 +9,8 @@ margin exceeds twice that tolerance; elsewhere the GPU's label must be one of th
 classes within the tolerance of the oracle's best.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -229,18 +231,33 @@ def test_vits14_518_b8_taps():
 
 @pytest.mark.parametrize("name", ["vits16_224", "vits16_336"])
 def test_layerscale_one_sensitivity(name):
-    """The full ViT-S workloads with LayerScale 1.0 (every block's bf16 rounding
-    reaches the output): errors are reported, and only finiteness is required;
-    the workloads' gates apply to LayerScale 1e-5."""
+    """The full ViT-S workloads with LayerScale 1.0, where every block's bf16
+    roundings reach the output (with 1e-5 the blocks hardly move it).
+
+    Bounds from bf16 propagation: the final tokens are LayerNormed, unit scale
+    per row.  The patch embedding and each block carry about one bf16 rounding
+    (rms 2^-8/sqrt(3) relative) of the row into the residual stream, and the
+    contributions add independently, so the rms error stays below
+    sqrt(L + 1) 2^-8 / sqrt(3) (8.1e-3 at 12 blocks).  The largest error of
+    roughly Gaussian errors over 77k-171k values is 4.5-5.5 times their rms:
+    the max bound is 6 times the rms bound.  The descriptor cosine bound is
+    1e-4 from 1 (an rms error of 8e-3 over unit-scale rows gives 1 - cos of
+    about 3e-5)."""
     cfg = synth.preset(name, layerscale=1.0)
     P = synth.make_params(cfg)
     x = synth.make_images(cfg, 1)
     ref = O.forward(x, P, cfg)
     tok, desc, _ = run_gpu(cfg, P, x)
     assert np.isfinite(tok).all() and np.isfinite(desc).all()
-    err = np.abs(tok - ref["tokens"]).max()
-    rms = np.sqrt(np.mean((tok - ref["tokens"]) ** 2))
-    say(f"  {name} LS=1: max|tokens err| = {err:.3e}, rms {rms:.3e}, desc cos = {cosine(desc[0], ref['desc'][0]):.6f}")
+    err = np.abs(tok - ref["tokens"])
+    rms = float(np.sqrt(np.mean(err ** 2)))
+    cos = cosine(desc[0], ref["desc"][0])
+    rms_bound = math.sqrt(cfg["depth"] + 1) * 2 ** -8 / math.sqrt(3)
+    say(f"  {name} LS=1: max|tokens err| = {err.max():.3e} (bound {6 * rms_bound:.2e}), rms {rms:.3e} "
+        f"(bound {rms_bound:.2e}), desc cos = {cos:.7f}")
+    assert rms <= rms_bound
+    assert err.max() <= 6 * rms_bound
+    assert cos >= 0.9999
 
 
 @pytest.fixture(scope="module")
@@ -248,19 +265,34 @@ def vitl():
     cfg = synth.preset("vitl16_1024")
     P = synth.make_params(cfg)
     x = synth.make_images(cfg, 4)
-    return cfg, P, x
+    return cfg, P, x, {}
+
+
+def _vitl_ref(vitl):
+    """The oracle on all four ViT-L/16 @1024 images, computed once per module."""
+    cfg, P, x, cache = vitl
+    if "ref" not in cache:
+        say("  oracle: ViT-L/16 @1024, 4 images")
+        cache["ref"] = O.forward(x, P, cfg)
+    return cache["ref"]
 
 
 def test_vitl16_1024_b1(vitl):
-    cfg, P, x = vitl
+    cfg, P, x, cache = vitl
     say("ViT-L/16 @1024 b1")
-    ref = O.forward(x[:1], P, cfg)
-    gate(*run_gpu(cfg, P, x[:1])[:2], ref)
+    ref = _vitl_ref(vitl)
+    tok, desc, _ = run_gpu(cfg, P, x[:1])
+    gate(tok, desc, {"tokens": ref["tokens"][:1], "desc": ref["desc"][:1]})
+    cache["b1_image0"] = tok[0]
 
 
-def test_vitl16_1024_b4_batch_invariance(vitl):
-    cfg, P, x = vitl
-    say("ViT-L/16 @1024 b4 vs b1")
+def test_vitl16_1024_b4(vitl):
+    """Batch 4 against the oracle image by image (the b4 GEMMs tile the 16404
+    rows differently from b1: other tile shapes and 20 extra rows), and bit for
+    bit against the same images run alone."""
+    cfg, P, x, cache = vitl
+    say("ViT-L/16 @1024 b4")
+    ref = _vitl_ref(vitl)
     enc = vit.Encoder(cfg, P, max_batch=4)
     xd = f32_dev(x)
     t4 = enc.forward(xd)
@@ -268,9 +300,13 @@ def test_vitl16_1024_b4_batch_invariance(vitl):
     t1 = enc.forward(xd[1:2].contiguous())
     a4, a1, dd = host(t4), host(t1), host(d4)
     enc.close()
-    assert np.isfinite(a4).all()
+    for b in range(4):
+        err = np.abs(a4[b] - ref["tokens"][b]).max()
+        say(f"  image {b}: max|tokens err| = {err:.3e}, desc cos = {cosine(dd[b], ref['desc'][b]):.7f}")
+    gate(a4, dd, ref)
     np.testing.assert_array_equal(a4[1], a1[0])
-    np.testing.assert_allclose(np.linalg.norm(dd, axis=1), 1.0, atol=1e-5)
+    if "b1_image0" in cache:
+        np.testing.assert_array_equal(a4[0], cache["b1_image0"])
 
 
 # ------------------------------------------------------------------ zero-shot scoring

@@ -100,6 +100,13 @@ def test_plan_rejects_bad_configs(L):
     assert plan(tap_mask=1 << 12) == -1   # block 13 of 12
     assert plan(window=100, window_stride=50) == -2
     assert "multiple" in vit.vit_last_error()
+    # a stride past the window would leave pixels that no window covers
+    base5 = vit.vit_config_preset(5).as_dict()
+    c5 = vit.VitConfig(**{**base5, "window_stride": 500})
+    assert lib.vit_plan(ctypes.byref(c5), ctypes.byref(out)) == -2
+    assert "window_stride" in vit.vit_last_error()
+    c5 = vit.VitConfig(**{**base5, "window_stride": 384})
+    assert lib.vit_plan(ctypes.byref(c5), ctypes.byref(out)) == 0
     assert lib.vit_plan(None, ctypes.byref(out)) == -1
     assert lib.vit_config_preset(9, ctypes.byref(vit.VitConfig())) == -1
 
@@ -123,9 +130,8 @@ def test_create_and_calls_validate_before_touching_the_device(L):
     assert lib.vit_patch_scores(None, fake, fake, 1, 0, fake, None, None, None) == -1
     assert lib.vit_op_linear(fake, fake, fake, 4, 4, 63, 0, None, fake, None) == -2
     assert lib.vit_op_layernorm(fake, 4, 100, fake, fake, ctypes.c_float(1e-6), fake, 0, None) == -2
-    assert lib.vit_op_attention(None, fake, fake, 1, 4, 1, fake, None, 0, None) == -1
-    for shape in [(1, 446, 6), (2, 1370, 6), (1, 4101, 16), (64, 4101, 64)]:
-        assert vit.vit_op_attention_workspace(*shape) == 0         # one pass, no scratch
+    assert lib.vit_op_attention(None, fake, fake, 1, 4, 1, fake, None) == -1
+    assert lib.vit_op_attention(fake, fake, fake, 0, 4, 1, fake, None) == -2
     f = ctypes.c_float(1e-6)
     assert lib.vit_op_linear_residual_ln(fake, fake, fake, fake, 4, 384, 64, fake, fake, fake, f, None, None) == -1
     assert lib.vit_op_linear_residual_ln(fake, fake, fake, fake, 4, 384, 60, fake, fake, fake, f, fake, None) == -2

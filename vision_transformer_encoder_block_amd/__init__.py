@@ -22,7 +22,7 @@ __all__ = [
     "LibraryMissing", "VitError", "VitConfig", "VitSizes", "lib", "config_from_dict", "pack_params",
     "vit_config_preset", "vit_plan", "vit_create", "vit_forward", "vit_descriptor", "vit_patch_scores",
     "vit_destroy", "vit_last_error", "vit_op_layernorm", "vit_op_linear", "vit_op_qkv", "vit_op_attention",
-    "vit_op_attention_workspace", "vit_op_preprocess", "vit_op_linear_residual_ln",
+    "vit_op_preprocess", "vit_op_linear_residual_ln",
     "Encoder", "EncoderGraph", "EPI_BIAS_BF16", "EPI_GELU_BF16", "EPI_RESIDUAL", "EPI_BIAS_F32",
     "HeadConfig", "HeadSizes", "head_config_preset", "head_config", "head_plan", "pack_head_params", "SemanticHead",
     "vit_op_conv3x3", "vit_op_absmax", "vit_op_quantize_fp8", "vit_op_linear_fp8",
@@ -83,8 +83,7 @@ _SIGNATURES = {
     "vit_op_layernorm": (_I, [_P, _I, _I, _P, _P, ctypes.c_float, _P, _I, _P]),
     "vit_op_linear": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "vit_op_qkv": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
-    "vit_op_attention": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, ctypes.c_size_t, _P]),
-    "vit_op_attention_workspace": (ctypes.c_size_t, [_I, _I, _I]),
+    "vit_op_attention": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "vit_op_preprocess": (_I, [_P, _I, _I, _I, _I, _P, _I, _I, _P]),
     "vit_op_linear_residual_ln": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P, _P, ctypes.c_float, _P, _P]),
     "vit_head_config_preset": (_I, [_P]),
@@ -210,14 +209,9 @@ def vit_op_qkv(h, wqkv, bqkv, batch, tokens, heads, q, k, vt, stream=None):
                                                  _ptr(k), _ptr(vt), _stream(stream)))
 
 
-def vit_op_attention_workspace(batch, tokens, heads) -> int:
-    return lib().vit_op_attention_workspace(batch, tokens, heads)
-
-
-def vit_op_attention(q, k, vt, batch, tokens, heads, o, work=None, stream=None):
-    nbytes = 0 if work is None else work.numel() * work.element_size()
+def vit_op_attention(q, k, vt, batch, tokens, heads, o, stream=None):
     return _check("vit_op_attention", lib().vit_op_attention(_ptr(q), _ptr(k), _ptr(vt), batch, tokens, heads,
-                                                             _ptr(o), _ptr(work), nbytes, _stream(stream)))
+                                                             _ptr(o), _stream(stream)))
 
 
 # ------------------------------------------------------------------ marshalling helpers

@@ -362,10 +362,8 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
 // Every query tile runs against the whole key range in one pass (a partly
 // filled last tile included: its idle waves only take part in the loads and
 // barriers), so no workspace is needed.
-size_t attention_workspace_bytes(int, int, int) { return 0; }
-
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
-                            int heads, int nv, uint16_t* o, float*, size_t, hipStream_t s) {
+                            int heads, int nv, uint16_t* o, hipStream_t s) {
   if (batch <= 0 || tokens <= 0 || heads <= 0 || nv < tokens || nv % 64 != 0) return hipErrorInvalidValue;
   if ((size_t)nv * 128 >= (1ull << 32)) return hipErrorInvalidValue;
   const int qtiles = (tokens + QT - 1) / QT;

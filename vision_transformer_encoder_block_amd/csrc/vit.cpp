@@ -142,6 +142,10 @@ int build_plan(const vit_config* c, Plan& pl) {
   if (c->window > 0) {
     if (c->window % c->patch || c->window > c->img_h || c->window > c->img_w || c->window_stride < 1)
       return fail(VIT_ERR_SHAPE, "window must be a multiple of patch, fit the image, and stride >= 1");
+    // a stride longer than the window leaves pixels no window covers (their
+    // overlap count would be 0)
+    if (c->window_stride > c->window)
+      return fail(VIT_ERR_SHAPE, "window_stride must not exceed window (every pixel needs a window)");
     make_geom(pl, c->window, c->window, pl.win);
     const auto ys = window_starts(c->img_h, c->window, c->window_stride);
     const auto xs = window_starts(c->img_w, c->window, c->window_stride);
@@ -319,7 +323,7 @@ int run_encoder(vit_model* m, const Geom& g, const float* images, int batch, flo
     eq.heads = pl.heads;
     eq.nv = g.nv;
     VIT_HIP(vit::launch_gemm(m->h, w.wqkv, M, 3 * D, D, eq, st), "qkv");
-    VIT_HIP(vit::launch_attention(m->q, m->k, m->vt, batch, N, pl.heads, g.nv, m->o, nullptr, 0, st),
+    VIT_HIP(vit::launch_attention(m->q, m->k, m->vt, batch, N, pl.heads, g.nv, m->o, st),
             "attention");
     vit::EpiParams eo;
     eo.kind = fuse_ln ? vit::EPI_RESIDUAL_LN : vit::EPI_RESIDUAL;
@@ -722,17 +726,12 @@ int vit_op_qkv(const void* h, const void* wqkv, const float* bqkv, int batch, in
   return VIT_OK;
 }
 
-size_t vit_op_attention_workspace(int batch, int tokens, int heads) {
-  if (batch < 1 || tokens < 1 || heads < 1) return 0;
-  return vit::attention_workspace_bytes(batch, tokens, heads);
-}
-
 int vit_op_attention(const void* q, const void* k, const void* vt, int batch, int tokens, int heads, void* o,
-                     void* work, size_t work_bytes, void* stream) {
+                     void* stream) {
   if (!q || !k || !vt || !o) return fail(VIT_ERR_ARG, "NULL pointer");
   if (batch < 1 || tokens < 1 || heads < 1 || heads > 64) return fail(VIT_ERR_SHAPE, "bad batch/tokens/heads");
   VIT_HIP(vit::launch_attention((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, batch, tokens, heads,
-                                round_up(tokens, 64), (uint16_t*)o, (float*)work, work_bytes, (hipStream_t)stream),
+                                round_up(tokens, 64), (uint16_t*)o, (hipStream_t)stream),
           "attention");
   return VIT_OK;
 }
