@@ -54,19 +54,45 @@ def flops_per_image(cfg: dict) -> dict:
 
 
 def time_gpu(fn, steps, warmup):
+    """`warmup` untimed calls, then exactly `steps` calls between a device
+    synchronisation on either side, each bracketed by its own pair of HIP events
+    on the current stream (the stream the library launches on).  Returns the
+    per-call times in ms (median, p10, p90, mean) and the host wall time per
+    call."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    start.record()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return dict(median=float(np.median(ms)), p10=float(np.percentile(ms, 10)), p90=float(np.percentile(ms, 90)),
+                mean=float(ms.mean()), wall=wall)
+
+
+def time_loop(fn, steps, warmup):
+    """Average duration in ms of one call among `steps` back-to-back calls, from
+    one pair of HIP events around them on the current stream.  Used for single
+    kernels of a few microseconds, whose launches run back to back the way they
+    do inside a forward: an event pair around every launch would add its own
+    gaps (2-6 us per launch measured) to each one."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
     for _ in range(steps):
         fn()
-    stop.record()
+    b.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return start.elapsed_time(stop) / steps, wall / steps * 1e3
+    return a.elapsed_time(b) / steps
 
 
 def bench_workload(name, batch, steps, warmup):
@@ -85,17 +111,19 @@ def bench_workload(name, batch, steps, warmup):
         enc.descriptor(tok, desc_out=desc)
 
     # eager: one launch per kernel from Python
-    eager_ms, _ = time_gpu(step, steps, warmup)
+    eager = time_gpu(step, steps, warmup)
     # the same step recorded once as a HIP graph and replayed (the serving path)
     graph = vit.EncoderGraph(enc, x, tok, desc_out=desc)
-    ms, wall_ms = time_gpu(graph.replay, steps, warmup)
+    t = time_gpu(graph.replay, steps, warmup)
     torch.cuda.synchronize()
     assert torch.isfinite(desc).all().item(), "non-finite descriptor"
     fl = flops_per_image(cfg)
+    ms = t["median"]
     tflops = fl["total"] * batch / (ms * 1e-3) / 1e12
-    res = dict(images_per_s=batch / (ms * 1e-3), ms_per_step=ms, wall_ms_per_step=wall_ms, tflops=tflops,
+    res = dict(images_per_s=batch / (ms * 1e-3), ms_per_step=ms, ms_per_step_p10=t["p10"], ms_per_step_p90=t["p90"],
+               ms_per_step_mean=t["mean"], wall_ms_per_step=t["wall"], tflops=tflops,
                frac_bf16_peak=tflops / PEAK_BF16_TFLOPS, gflop_per_image=fl["total"] / 1e9,
-               eager_images_per_s=batch / (eager_ms * 1e-3), eager_ms_per_step=eager_ms)
+               eager_images_per_s=batch / (eager["median"] * 1e-3), eager_ms_per_step=eager["median"])
     del graph
     return cfg, enc, res
 
@@ -109,8 +137,8 @@ def bench_preprocess(batch=32, src=(720, 1280), dst=(336, 336), steps=50, warmup
     g = torch.Generator(device="cuda").manual_seed(5000)
     frames = torch.randint(0, 256, (batch,) + src + (3,), dtype=torch.uint8, device="cuda", generator=g)
     out = torch.empty((batch, 3) + dst, dtype=torch.float32, device="cuda")
-    ms, _ = time_gpu(lambda: vit.vit_op_preprocess(frames, batch, src[0], src[1], True, out, dst[0], dst[1]),
-                     steps, warmup)
+    ms = time_loop(lambda: vit.vit_op_preprocess(frames, batch, src[0], src[1], True, out, dst[0], dst[1]),
+                   steps, warmup)
     nbytes = batch * (src[0] * src[1] * 3 + 3 * dst[0] * dst[1] * 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": f"{batch} BGR frames {src[1]}x{src[0]} -> {dst[1]}x{dst[0]} ImageNet-normalised",
@@ -170,13 +198,22 @@ def kernel_breakdown(cfg, batch, steps=20, warmup=5):
     }
     out = {}
     for name, (fn, per_step, flops, nbytes, bound) in ops.items():
-        ms, _ = time_gpu(fn, steps, warmup)
+        ms = time_loop(fn, steps, warmup)
         out[name] = dict(ms=ms, launches_per_step=per_step, ms_per_step=ms * per_step, flops=flops,
-                         bytes=nbytes, bound=bound)
+                         bytes=nbytes, bound=bound, tflops=flops / (ms * 1e-3) / 1e12,
+                         gbs=nbytes / (ms * 1e-3) / 1e9)
     return out
 
 
-def roofline(breakdown, kernel_names):
+def breakdown_table(bd):
+    """Per-op summary for the JSON line: time per launch and per step, TFLOP/s
+    and algorithmic HBM GB/s (bytes the op must move at least, per launch)."""
+    return {n: {"us_per_launch": round(b["ms"] * 1e3, 2), "launches_per_step": b["launches_per_step"],
+                "ms_per_step": round(b["ms_per_step"], 4), "tflops": round(b["tflops"], 1),
+                "hbm_gbs": round(b["gbs"], 1)} for n, b in bd.items()}
+
+
+def roofline(breakdown, kernel_names, workload):
     name = max(breakdown, key=lambda n: breakdown[n]["ms_per_step"])
     b = breakdown[name]
     if b["bound"] == "mfma":
@@ -188,7 +225,7 @@ def roofline(breakdown, kernel_names):
         rl = dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s", frac=achieved / PEAK_HBM_GBS)
     rl["kernel"] = kernel_names.get(name, name)
     rl["avg_launch_us"] = b["ms"] * 1e3
-    rl["traffic"] = traffic_for(name)
+    rl["traffic"] = traffic_for(workload, name)
     return name, rl
 
 
@@ -203,19 +240,22 @@ def _source_digest():
     return h.hexdigest()[:16]
 
 
-def traffic_for(op):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources (else null)."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    if not os.path.exists(path):
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def traffic_for(workload, op):
+    """HBM bytes per launch of `op` at `workload` from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources (else null)."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
     try:
-        t = json.load(open(path))
+        t = json.load(open(TRAFFIC_JSON))
     except ValueError:
         return None
-    if t.get("source_digest") != _source_digest():
+    w = t.get("workloads", {}).get(workload)
+    if w is None or w.get("source_digest") != _source_digest():
         return None
-    entry = t.get("ops", {}).get(op)
+    entry = w.get("ops", {}).get(op)
     return None if entry is None else entry.get("bytes_per_launch")
 
 
@@ -257,20 +297,32 @@ def copy_calibration(mib=256, reps=3):
     return mib
 
 
-# op -> (kernel-name substring, grid size at ViT-S/16@336 b32 or None)
+# Per workload: op -> predicate on the kernel name selecting its dispatches in a
+# counter run of that workload's per-op loops (bench.py --breakdown-only).
+# Residual GEMMs that share one kernel (out-proj and fc2) are told apart by
+# FETCH_SIZE: fc2 reads an A operand 4x longer.
+def _has(*subs, without=()):
+    return lambda k: all(x in k for x in subs) and not any(x in k for x in without)
+
+
 PMC_OPS = {
-    "fc1": ("EpiGeluBf16", None),
-    "attention": ("attention_kernel", None),
-    "layernorm": ("layernorm_kernel", None),
-    "qkv": ("EpiQKV", None),
-    "residual_ln": ("EpiResidualLN", None),
+    "vits16_336_b32": {"fc1": _has("EpiGeluBf16"), "attention": _has("attention_kernel"),
+                       "layernorm": _has("layernorm_kernel"), "qkv": _has("EpiQKV"),
+                       "out_proj|fc2": _has("EpiResidualLN")},
+    "vitl16_1024_b1": {"fc1": _has("EpiGeluBf16"), "attention": _has("attention_kernel"),
+                       "layernorm": _has("layernorm_kernel"), "qkv": _has("EpiQKV"),
+                       "out_proj|fc2": _has("EpiResidual", without=("EpiResidualLN",))},
 }
 
+WORKLOADS = {"vits16_336_b32": ("vits16_336", 32), "vitl16_1024_b1": ("vitl16_1024", 1)}
 
-def summarize_pmc(fetch_csv, write_csv, copy_mib=256):
-    """Per-dispatch HBM bytes of the block kernels from two rocprofv3 --pmc runs
-    (FETCH_SIZE, WRITE_SIZE in KiB), scaled by the same counters on a plain copy
-    of known size; written to profiles/hbm_traffic.json with the source digest."""
+
+def summarize_pmc(fetch_csv, write_csv, workload, copy_mib=256):
+    """Per-dispatch HBM bytes of one workload's block kernels from two rocprofv3
+    --pmc runs (FETCH_SIZE, WRITE_SIZE in KiB) of `bench.py --breakdown-only
+    WORKLOAD --copy-calibration`, scaled by the same counters on a plain copy of
+    known size; stored under the workload in profiles/hbm_traffic.json with the
+    kernel source digest."""
     import csv
 
     def load(path, counter):
@@ -283,74 +335,85 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib=256):
 
     fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
 
-    def avg(table, sub):
-        vals = [v for k, vs in table.items() if sub in k for v in vs]
-        return sum(vals) / len(vals) if vals else None
+    def vals(table, pred):
+        return [v for k, vs in table.items() if pred(k) for v in vs]
+
+    def avg(xs):
+        return sum(xs) / len(xs) if xs else None
 
     def copy_avg(table):
-        vals = [v for k, vs in table.items() if ("copy" in k.lower() or "elementwise" in k.lower()) for v in vs]
-        vals = sorted(vals)[-3:]  # the three large calibration copies
-        return sum(vals) / len(vals) if vals else None
+        xs = sorted(vals(table, lambda k: "copy" in k.lower() or "elementwise" in k.lower()))[-3:]
+        return avg(xs)  # the three large calibration copies
 
     expect_kib = copy_mib * 1024.0
     cf, cw = copy_avg(fetch), copy_avg(write)
-    scale_f = expect_kib / cf if cf else None
-    scale_w = expect_kib / cw if cw else None
-    out = {"source_digest": _source_digest(), "copy_mib": copy_mib, "copy_fetch_kib": cf, "copy_write_kib": cw,
-           "scale_fetch": scale_f, "scale_write": scale_w, "ops": {}}
-    for op, (sub, _) in PMC_OPS.items():
-        f, w = avg(fetch, sub), avg(write, sub)
-        if f is None or w is None or scale_f is None or scale_w is None:
+    if not cf or not cw:
+        raise SystemExit("no calibration copy in the counter runs (run with --copy-calibration)")
+    scale_f, scale_w = expect_kib / cf, expect_kib / cw
+    ops = {}
+    for op, pred in PMC_OPS[workload].items():
+        f, w = vals(fetch, pred), vals(write, pred)
+        if not f or not w:
             continue
-        out["ops"][op] = {"kernel_substring": sub, "fetch_kib": f, "write_kib": w,
-                          "bytes_per_launch": (f * scale_f + w * scale_w) * 1024.0}
-    # out-proj and fc2 share the residual + LayerNorm kernel; they write the same
-    # bytes (x and the normalised rows) but fc2 reads a 4x longer A operand, so
-    # the dispatches split into two clusters by FETCH_SIZE
-    rl = [v for k, vs in fetch.items() if "EpiResidualLN" in k for v in vs]
-    w_rl = avg(write, "EpiResidualLN")
-    if rl and w_rl is not None and scale_f and scale_w:
-        mid = (min(rl) + max(rl)) / 2
-        for op, grp in (("out_proj", [v for v in rl if v < mid]), ("fc2", [v for v in rl if v >= mid])):
-            if grp:
-                f = sum(grp) / len(grp)
-                out["ops"][op] = {"kernel_substring": "EpiResidualLN (FETCH cluster)", "fetch_kib": f,
-                                  "write_kib": w_rl, "bytes_per_launch": (f * scale_f + w_rl * scale_w) * 1024.0}
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    json.dump(out, open(path, "w"), indent=1)
-    print(json.dumps(out, indent=1))
+        if op == "out_proj|fc2":
+            mid = (min(f) + max(f)) / 2
+            groups = (("out_proj", [v for v in f if v < mid]), ("fc2", [v for v in f if v >= mid]))
+            kname = "FETCH cluster"
+        else:
+            groups = ((op, f),)
+            kname = None
+        for name, grp in groups:
+            if not grp:
+                continue
+            fk, wk = avg(grp), avg(w)
+            ops[name] = {"dispatches": len(grp), "fetch_kib": fk, "write_kib": wk,
+                         "bytes_per_launch": (fk * scale_f + wk * scale_w) * 1024.0}
+            if kname:
+                ops[name]["note"] = kname
+    doc = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    doc.setdefault("workloads", {})
+    doc.pop("ops", None)
+    doc["workloads"][workload] = {"source_digest": _source_digest(), "copy_mib": copy_mib, "copy_fetch_kib": cf,
+                                  "copy_write_kib": cw, "scale_fetch": scale_f, "scale_write": scale_w, "ops": ops}
+    json.dump(doc, open(TRAFFIC_JSON, "w"), indent=1)
+    print(json.dumps(doc["workloads"][workload], indent=1))
 
 
-def summarize_mfma(csv_path, simds=1024, clock_ghz=2.4):
-    """Matrix-core utilisation of the ViT-S/16@336 b32 block kernels from one
+def summarize_mfma(csv_path, workload, simds=1024, clock_ghz=2.4):
+    """Matrix-core utilisation of one workload's block kernels from one
     rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16,
-    SQ_INSTS_MFMA, SQ_INSTS_VALU_TRANS_F32) of this script's per-op loops.  The
-    loops also hold other workloads' dispatches of the same kernels, so each op
-    takes the dispatch cluster whose hardware FLOP count (MOPS x 512) is nearest
-    its algorithmic FLOPs at this workload.  A busy cycle is one SIMD's full-rate
-    MFMA cycle (1024 bf16 FLOPs), so utilisation = busy SIMD-cycles / (SIMDs x
-    dispatch duration x clock), the duration taken from the dispatch's own
+    SQ_INSTS_MFMA, SQ_INSTS_VALU_TRANS_F32) of `bench.py --breakdown-only
+    WORKLOAD`.  Kernels shared by two ops (out-proj and fc2) are told apart by
+    their hardware FLOP count (MOPS x 512), taking the dispatch cluster nearest
+    each op's algorithmic FLOPs.  A busy cycle is one SIMD's full-rate MFMA
+    cycle (1024 bf16 FLOPs), so utilisation = busy SIMD-cycles / (SIMDs x
+    dispatch duration x clock), the duration from the dispatch's own
     timestamps and the clock the one the dense peak is quoted at.  Prints a
     markdown table."""
     import csv
     import math
+    import synth
     per = {}
     for r in csv.DictReader(open(csv_path)):
         c = per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {})
         c["dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    B, N, D, Hm = 32, 446, 384, 1536
+    name, B = WORKLOADS[workload]
+    cfg = synth.preset(name)
+    D, Hm = cfg["dim"], cfg["mlp_hidden"]
+    N = synth.tokens(cfg)
     M = B * N
-    ops = [("qkv", "EpiQKV", 2.0 * M * D * 3 * D), ("attention", "attention_kernel<4>", 4.0 * B * N * N * D),
-           ("out_proj", "EpiResidualLN", 2.0 * M * D * D), ("fc1", "EpiGeluBf16", 2.0 * M * D * Hm),
-           ("fc2", "EpiResidualLN", 2.0 * M * Hm * D)]
+    pm = PMC_OPS[workload]
+    ops = [("qkv", pm["qkv"], 2.0 * M * D * 3 * D), ("attention", pm["attention"], 4.0 * B * N * N * D),
+           ("out_proj", pm["out_proj|fc2"], 2.0 * M * D * D), ("fc1", pm["fc1"], 2.0 * M * D * Hm),
+           ("fc2", pm["out_proj|fc2"], 2.0 * M * Hm * D)]
     print("| Op | dispatches | dispatch us | hardware GFLOP (MOPS x 512) | algorithmic GFLOP | MFMA instr. | "
           "MFMA busy % | transcendental instr. |")
     print("|---|---|---|---|---|---|---|---|")
-    for op, sub, fl in ops:
+    for op, pred, fl in ops:
         groups = {}
-        for (name, _), c in per.items():
-            if sub in name and "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+        for (kname, _), c in per.items():
+            if pred(kname) and "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
                 groups.setdefault(round(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]), []).append(c)
         if not groups:
             continue
@@ -363,12 +426,22 @@ def summarize_mfma(csv_path, simds=1024, clock_ghz=2.4):
 
 
 KERNEL_NAMES = {
-    "qkv": "gemm_bf16_kernel<EpiQKV>",
-    "attention": "attention_kernel",
-    "out_proj": "gemm_bf16_kernel<EpiResidualLN> (out-proj + LN2)",
-    "fc1": "gemm_bf16_kernel<EpiGeluBf16>",
-    "fc2": "gemm_bf16_kernel<EpiResidualLN> (fc2 + next LN1)",
-    "layernorm": "layernorm_kernel<3,32,false>",
+    "vits16_336_b32": {
+        "qkv": "gemm_bf16_kernel<EpiQKV>",
+        "attention": "attention_kernel",
+        "out_proj": "gemm_bf16_kernel<EpiResidualLN> (out-proj + LN2)",
+        "fc1": "gemm_bf16_kernel<EpiGeluBf16>",
+        "fc2": "gemm_bf16_kernel<EpiResidualLN> (fc2 + next LN1)",
+        "layernorm": "layernorm_kernel (block 1 LN1, final norm)",
+    },
+    "vitl16_1024_b1": {
+        "qkv": "gemm_bf16_kernel<EpiQKV>",
+        "attention": "attention_kernel",
+        "out_proj": "gemm_bf16_kernel<EpiResidual> (out-proj)",
+        "fc1": "gemm_bf16_kernel<EpiGeluBf16>",
+        "fc2": "gemm_bf16_kernel<EpiResidual> (fc2)",
+        "layernorm": "layernorm_kernel (LN1, LN2)",
+    },
 }
 
 
@@ -400,8 +473,8 @@ def bench_head(steps=30, warmup=5):
         enc.forward(x, with_taps=True, tokens_out=tok, taps_out=taps)
         head.forward(taps, logits_out=logits)
 
-    ms_all, _ = time_gpu(both, steps, warmup)
-    ms_head, _ = time_gpu(lambda: head.forward(taps, logits_out=logits), steps, warmup)
+    ms_all = time_gpu(both, steps, warmup)["median"]
+    ms_head = time_loop(lambda: head.forward(taps, logits_out=logits), steps, warmup)
     torch.cuda.synchronize()
     assert torch.isfinite(logits).all().item(), "non-finite logits"
     fl = head_flops(hcfg, B)
@@ -413,7 +486,8 @@ def bench_head(steps=30, warmup=5):
     xin = torch.randn(M, 5 * H2, device="cuda").to(torch.bfloat16)
     wk = (torch.randn(H2, 9 * H2, device="cuda") * 0.05).to(torch.bfloat16)
     cout = torch.empty(M, H2, device="cuda")
-    ms_conv, _ = time_gpu(lambda: vit.vit_op_conv3x3(xin, 5 * H2, H2, H2, B, 37, 37, wk, None, H2, cout), steps, warmup)
+    ms_conv = time_loop(lambda: vit.vit_op_conv3x3(xin, 5 * H2, H2, H2, B, 37, 37, wk, None, H2, cout), steps,
+                        warmup)
     conv_tf = 2.0 * M * H2 * 9 * H2 / (ms_conv * 1e-3) / 1e12
     return {"workload": "DINOv2-S/14 @518 b8, taps 3/6/9/12 -> semantic head -> 19 x 518 x 518 logits",
             "images_per_s": B / (ms_all * 1e-3), "ms_per_step": ms_all, "head_ms": ms_head,
@@ -438,10 +512,11 @@ def bench_fp8(steps=30, warmup=5):
         qw = torch.randint(0, 0x7F, (N, K), dtype=torch.uint8, device="cuda", generator=g)
         bias = torch.zeros(N, device="cuda")
         out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        ms8, _ = time_gpu(lambda: vit.vit_op_linear_fp8(qa, qw, M, N, K, 1.0, bias, out), steps, warmup)
+        ms8 = time_loop(lambda: vit.vit_op_linear_fp8(qa, qw, M, N, K, 1.0, bias, out), steps, warmup)
         a = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
         w = torch.randn(N, K, device="cuda", generator=g).to(torch.bfloat16)
-        ms16, _ = time_gpu(lambda: vit.vit_op_linear(a, w, bias, M, N, K, vit.EPI_BIAS_BF16, None, out), steps, warmup)
+        ms16 = time_loop(lambda: vit.vit_op_linear(a, w, bias, M, N, K, vit.EPI_BIAS_BF16, None, out), steps,
+                         warmup)
         fl = 2.0 * M * N * K
         res[name] = {"shape": [M, N, K], "fp8_us": ms8 * 1e3, "fp8_tflops": fl / (ms8 * 1e-3) / 1e12,
                      "fp8_frac_peak": fl / (ms8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
@@ -477,16 +552,20 @@ def main():
     ap.add_argument("--head-only", action="store_true",
                     help="run only the semantic-head leg (DINOv2-S/14 @518 b8 + head) and print its JSON")
     ap.add_argument("--fp8-only", action="store_true", help="run only the fp8 linear leg and print its JSON")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="host only: turn two rocprofv3 --pmc CSVs into profiles/hbm_traffic.json")
-    ap.add_argument("--summarize-mfma", metavar="CSV",
-                    help="host only: matrix-core utilisation table from a rocprofv3 --pmc CSV")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "WORKLOAD"),
+                    help="host only: turn two rocprofv3 --pmc CSVs of --breakdown-only WORKLOAD into "
+                         "profiles/hbm_traffic.json")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("CSV", "WORKLOAD"),
+                    help="host only: matrix-core utilisation table from a rocprofv3 --pmc CSV of "
+                         "--breakdown-only WORKLOAD")
+    ap.add_argument("--breakdown-only", choices=sorted(WORKLOADS),
+                    help="run only the per-op timing loops of one workload and print their JSON (for counter runs)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
     if args.summarize_mfma:
-        summarize_mfma(args.summarize_mfma)
+        summarize_mfma(*args.summarize_mfma)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the encoder path is single-GPU (images are independent, "
@@ -503,6 +582,12 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration()
+    if args.breakdown_only:
+        name, batch = WORKLOADS[args.breakdown_only]
+        import synth
+        bd = kernel_breakdown(synth.preset(name), batch, args.steps, args.warmup)
+        print(json.dumps(breakdown_table(bd)), flush=True)
+        return
     log("ViT-S/16 @336 b32 ...")
     cfg, enc, small = bench_workload("vits16_336", 32, args.steps, args.warmup)
     enc.close()
@@ -525,8 +610,17 @@ def main():
     log("kernel breakdown ...")
     bd = kernel_breakdown(cfg, 32)
     for n, b in bd.items():
-        log(f"  {n:10s} {b['ms'] * 1e3:9.1f} us/launch  x{b['launches_per_step']:3d} = {b['ms_per_step']:.3f} ms/step")
-    dom, rl = roofline(bd, KERNEL_NAMES)
+        log(f"  {n:10s} {b['ms'] * 1e3:9.1f} us/launch  x{b['launches_per_step']:3d} = {b['ms_per_step']:.3f} ms/step"
+            f"  {b['tflops']:7.1f} TFLOP/s  {b['gbs']:7.1f} GB/s")
+    dom, rl = roofline(bd, KERNEL_NAMES["vits16_336_b32"], "vits16_336_b32")
+    bd_l = rl_l = None
+    if large:
+        log("kernel breakdown, ViT-L/16 @1024 b1 ...")
+        bd_l = kernel_breakdown(cfg_l, 1)
+        for n, b in bd_l.items():
+            log(f"  {n:10s} {b['ms'] * 1e3:9.1f} us/launch  x{b['launches_per_step']:3d} = "
+                f"{b['ms_per_step']:.3f} ms/step  {b['tflops']:7.1f} TFLOP/s  {b['gbs']:7.1f} GB/s")
+        _, rl_l = roofline(bd_l, KERNEL_NAMES["vitl16_1024_b1"], "vitl16_1024_b1")
     out = {
         "metric": METRIC,
         "value": small["images_per_s"],
@@ -535,6 +629,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": small["ms_per_step"],
+        "ms_per_step_p10": small["ms_per_step_p10"],
+        "ms_per_step_p90": small["ms_per_step_p90"],
+        "ms_per_step_mean": small["ms_per_step_mean"],
+        "timing": "median of per-step HIP event pairs (p10/p90 and mean beside it); images/s from the median",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -547,12 +645,16 @@ def main():
         "tflops": small["tflops"],
         "pct_bf16_peak": 100 * small["frac_bf16_peak"],
         "roofline": rl,
-        "kernels_ms_per_step": {n: round(b["ms_per_step"], 4) for n, b in bd.items()},
+        "kernels": breakdown_table(bd),
     }
     if large:
         out["vitl16_1024_b1"] = {"images_per_s": large["images_per_s"], "ms_per_step": large["ms_per_step"],
+                                 "ms_per_step_p10": large["ms_per_step_p10"],
+                                 "ms_per_step_p90": large["ms_per_step_p90"],
+                                 "ms_per_step_mean": large["ms_per_step_mean"],
                                  "eager_images_per_s": large["eager_images_per_s"],
-                                 "tflops": large["tflops"], "pct_bf16_peak": 100 * large["frac_bf16_peak"]}
+                                 "tflops": large["tflops"], "pct_bf16_peak": 100 * large["frac_bf16_peak"],
+                                 "roofline": rl_l, "kernels": breakdown_table(bd_l)}
     out["preprocess"] = pre
     if not args.no_cpu:
         hd["cpu_baseline"] = head_cpu_baseline()
