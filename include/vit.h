@@ -104,6 +104,9 @@ int vit_plan(const vit_config* cfg, vit_sizes* out);
  * (device, >= weight_bytes) and binding `d_workspace` (device,
  * >= workspace_bytes).  Linear and patch weights are rounded to bf16 (nearest
  * even).  The workspace is cleared.  Synchronises `stream` before returning.
+ * d_workspace may be NULL with workspace_bytes 0: the model then runs only
+ * through vit_forward_static (vit_forward and vit_patch_scores return
+ * VIT_ERR_ARG).  The model belongs to the device current at this call.
  *
  * Blob layout (fp32, row-major, concatenated in this order; Linear weights
  * are [out, in] as in torch.nn.Linear):
@@ -131,6 +134,31 @@ int vit_create(const vit_config* cfg, const float* host_params, size_t host_floa
  * Enqueue only. */
 int vit_forward(vit_model* m, const float* d_images, int batch, float* d_tokens, float* d_taps,
                 void* stream);
+
+/* Size of the library's static activation array (per device), see
+ * vit_forward_static. */
+#define VIT_STATIC_SCRATCH_BYTES (96u * 1024u * 1024u)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as vit_forward, same arguments and outputs (bit-identical), but the
+ * activations live in a static device array of VIT_STATIC_SCRATCH_BYTES
+ * (96 MiB) inside the library instead of the workspace bound at vit_create,
+ * which may be NULL.  Nothing is allocated: each device that the library runs
+ * on holds its own array from loading until the process ends, its address
+ * taken once when the first model is created on that device.
+ *   Limit: batch images need at most vit_plan's workspace_bytes with
+ *   max_batch = batch (ViT-L/16 @1024: 94.2 MiB at batch 1; ViT-S/16 @336:
+ *   4.2 MiB per image); a batch beyond 96 MiB returns VIT_ERR_SIZE, before
+ *   anything is enqueued.
+ *   Every call on one device shares that device's array and leaves its
+ *   activations there: calls that overlap on one device (several streams or
+ *   threads, or several models) race and must be serialised by the caller.
+ *   The forward reads no activation it has not written in the same call, so
+ *   the array needs no clearing.
+ * Enqueue only. */
+int vit_forward_static(vit_model* m, const float* d_images, int batch, float* d_tokens, float* d_taps,
+                       void* stream);
 
 /* CLS descriptor: d_desc[b] = tokens[b,0,:] / max(||tokens[b,0,:]||_2, 1e-12)
  * (model card, "Model I/O": the descriptor is the CLS token; "Usage":

@@ -126,6 +126,7 @@ def test_create_and_calls_validate_before_touching_the_device(L):
     assert lib.vit_create(ctypes.byref(c), blob.ctypes.data_as(ctypes.c_void_p), blob.size, fake,
                           s.weight_bytes - 1, fake, s.workspace_bytes, None, ctypes.byref(h)) == -3
     assert lib.vit_forward(None, fake, 1, fake, None, None) == -1
+    assert lib.vit_forward_static(None, fake, 1, fake, None, None) == -1
     assert lib.vit_descriptor(None, fake, 1, fake, None) == -1
     assert lib.vit_patch_scores(None, fake, fake, 1, 0, fake, None, None, None) == -1
     assert lib.vit_op_linear(fake, fake, fake, 4, 4, 63, 0, None, fake, None) == -2

@@ -20,7 +20,7 @@ import numpy as np
 
 __all__ = [
     "LibraryMissing", "VitError", "VitConfig", "VitSizes", "lib", "config_from_dict", "pack_params",
-    "vit_config_preset", "vit_plan", "vit_create", "vit_forward", "vit_descriptor", "vit_patch_scores",
+    "vit_config_preset", "vit_plan", "vit_create", "vit_forward", "vit_forward_static", "vit_descriptor", "vit_patch_scores",
     "vit_destroy", "vit_last_error", "vit_op_layernorm", "vit_op_linear", "vit_op_qkv", "vit_op_attention",
     "vit_op_preprocess", "vit_op_linear_residual_ln",
     "Encoder", "EncoderGraph", "EPI_BIAS_BF16", "EPI_GELU_BF16", "EPI_RESIDUAL", "EPI_BIAS_F32",
@@ -77,6 +77,7 @@ _SIGNATURES = {
     "vit_create": (_I, [ctypes.POINTER(VitConfig), _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P,
                         ctypes.POINTER(_P)]),
     "vit_forward": (_I, [_P, _P, _I, _P, _P, _P]),
+    "vit_forward_static": (_I, [_P, _P, _I, _P, _P, _P]),
     "vit_descriptor": (_I, [_P, _P, _I, _P, _P]),
     "vit_patch_scores": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _P]),
     "vit_destroy": (_I, [_P]),
@@ -159,13 +160,19 @@ def vit_create(cfg: VitConfig, blob: np.ndarray, d_weights, d_workspace, stream=
     _check("vit_create", lib().vit_create(
         ctypes.byref(cfg), blob.ctypes.data_as(ctypes.c_void_p), blob.size, _ptr(d_weights),
         d_weights.numel() * d_weights.element_size(), _ptr(d_workspace),
-        d_workspace.numel() * d_workspace.element_size(), _stream(stream), ctypes.byref(handle)))
+        0 if d_workspace is None else d_workspace.numel() * d_workspace.element_size(), _stream(stream),
+        ctypes.byref(handle)))
     return handle
 
 
 def vit_forward(handle, d_images, batch, d_tokens, d_taps=None, stream=None):
     return _check("vit_forward", lib().vit_forward(handle, _ptr(d_images), batch, _ptr(d_tokens), _ptr(d_taps),
                                                    _stream(stream)))
+
+
+def vit_forward_static(handle, d_images, batch, d_tokens, d_taps=None, stream=None):
+    return _check("vit_forward_static", lib().vit_forward_static(handle, _ptr(d_images), batch, _ptr(d_tokens),
+                                                                 _ptr(d_taps), _stream(stream)))
 
 
 def vit_descriptor(handle, d_tokens, batch, d_desc, stream=None):
@@ -245,14 +252,16 @@ class Encoder:
     """A created model with torch-owned weight and workspace buffers on one device."""
 
     def __init__(self, cfg: dict | VitConfig, params: dict | np.ndarray, max_batch: int | None = None,
-                 device: str = "cuda", stream=None):
+                 device: str = "cuda", stream=None, workspace: bool = True):
+        """workspace=False binds no workspace: only forward_static can run."""
         import torch
         self.cfg = cfg if isinstance(cfg, VitConfig) else config_from_dict(cfg, max_batch)
         self.sizes = vit_plan(self.cfg)
         blob = params if isinstance(params, np.ndarray) else pack_params(params)
         self.device = torch.device(device)
         self.weights = torch.empty(self.sizes.weight_bytes, dtype=torch.uint8, device=self.device)
-        self.workspace = torch.empty(self.sizes.workspace_bytes, dtype=torch.uint8, device=self.device)
+        self.workspace = (torch.empty(self.sizes.workspace_bytes, dtype=torch.uint8, device=self.device)
+                          if workspace else None)
         self.handle = vit_create(self.cfg, blob, self.weights, self.workspace, stream)
 
     @property
@@ -269,6 +278,21 @@ class Encoder:
             taps_out = torch.empty((B, self.sizes.taps, c.dim, c.img_h // c.patch, c.img_w // c.patch),
                                    dtype=torch.float32, device=self.device)
         vit_forward(self.handle, images, B, tokens_out, taps_out if with_taps else None, stream)
+        return (tokens_out, taps_out) if with_taps else tokens_out
+
+    def forward_static(self, images, with_taps: bool = False, tokens_out=None, taps_out=None, stream=None):
+        """forward() with the activations in the library's static device array
+        (vit_forward_static): the library allocates nothing; the outputs are
+        torch buffers made here unless given."""
+        import torch
+        B = images.shape[0]
+        c = self.cfg
+        if tokens_out is None:
+            tokens_out = torch.empty((B, self.sizes.tokens, c.dim), dtype=torch.float32, device=self.device)
+        if with_taps and taps_out is None:
+            taps_out = torch.empty((B, self.sizes.taps, c.dim, c.img_h // c.patch, c.img_w // c.patch),
+                                   dtype=torch.float32, device=self.device)
+        vit_forward_static(self.handle, images, B, tokens_out, taps_out if with_taps else None, stream)
         return (tokens_out, taps_out) if with_taps else tokens_out
 
     def descriptor(self, tokens, desc_out=None, stream=None):

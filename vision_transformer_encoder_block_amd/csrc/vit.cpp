@@ -2,12 +2,15 @@
 // buffer planning, weight packing (fp32 blob -> bf16 GEMM operands, fp32 vectors),
 // the per-block launch sequence on the caller's stream, and the per-op entry
 // points.  The library never allocates device memory: weights and workspace are
-// caller-owned buffers carved into 256-byte-aligned regions.
+// caller-owned buffers carved into 256-byte-aligned regions.  The one exception
+// is vit_forward_static, whose activations live in a file-scope device array
+// of fixed size (for callers that cannot allocate).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -85,6 +88,17 @@ struct WorkLayout {
   int ldc_cos;
 };
 
+// Device pointers of the encoder's activations (one set of buffers per forward).
+struct Acts {
+  float* x = nullptr;                     // residual stream fp32 [rows, D]
+  uint16_t* h = nullptr;                  // LayerNorm output bf16 [rows, D]
+  uint16_t *q = nullptr, *k = nullptr;    // bf16 [images, heads, N, 64]
+  uint16_t* vt = nullptr;                 // bf16 [images, heads, 64, nv]
+  uint16_t* o = nullptr;                  // attention output bf16 [rows, D]
+  uint16_t* f = nullptr;                  // MLP hidden bf16 [rows, Hm]
+  uint16_t* cols = nullptr;               // im2col bf16 [patch rows, kpad]
+};
+
 struct Plan {
   vit_config cfg;
   int D, Hm, R, p, kpad, L, heads;
@@ -96,6 +110,40 @@ struct Plan {
   WeightLayout wl;
   WorkLayout ws;
 };
+
+// Offsets of the activation buffers for `rows` token rows, `vt_elems` V^T
+// values and `prows` patch rows, from byte 0 of a region; returns the end.
+size_t layout_acts(const Plan& pl, size_t rows, size_t vt_elems, size_t prows, WorkLayout& s) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  const size_t D = pl.D, Hm = pl.Hm;
+  s.x = take(rows * D * 4);
+  s.h = take(rows * D * 2);
+  s.q = take(rows * D * 2);
+  s.k = take(rows * D * 2);
+  s.vt = take(vt_elems * 2);
+  s.o = take(rows * D * 2);
+  s.f = take(rows * Hm * 2);
+  s.cols = take(prows * pl.kpad * 2);
+  return off;
+}
+
+Acts acts_at(char* base, const WorkLayout& s) {
+  Acts a;
+  a.x = (float*)(base + s.x);
+  a.h = (uint16_t*)(base + s.h);
+  a.q = (uint16_t*)(base + s.q);
+  a.k = (uint16_t*)(base + s.k);
+  a.vt = (uint16_t*)(base + s.vt);
+  a.o = (uint16_t*)(base + s.o);
+  a.f = (uint16_t*)(base + s.f);
+  a.cols = (uint16_t*)(base + s.cols);
+  return a;
+}
 
 int make_geom(const Plan& pl, int img_h, int img_w, Geom& g) {
   g.img_h = img_h;
@@ -220,7 +268,6 @@ int build_plan(const vit_config* c, Plan& pl) {
 
   // workspace
   WorkLayout& s = pl.ws;
-  off = 0;
   const size_t rows_main = (size_t)c->max_batch * pl.main.N;
   const size_t rows_win = (size_t)pl.nwin * (pl.nwin ? pl.win.N : 0);
   const size_t rows = std::max(rows_main, rows_win);
@@ -229,14 +276,7 @@ int build_plan(const vit_config* c, Plan& pl) {
   const size_t prow_main = (size_t)c->max_batch * pl.main.P;
   const size_t prow_win = pl.nwin ? (size_t)pl.nwin * pl.win.P : 0;
   const size_t prows = std::max(prow_main, prow_win);
-  s.x = take(rows * D * 4);
-  s.h = take(rows * D * 2);
-  s.q = take(rows * D * 2);
-  s.k = take(rows * D * 2);
-  s.vt = take(std::max(vt_main, vt_win) * 2);
-  s.o = take(rows * D * 2);
-  s.f = take(rows * Hm * 2);
-  s.cols = take(prows * pl.kpad * 2);
+  off = layout_acts(pl, rows, std::max(vt_main, vt_win), prows, s);
   s.ldc_cos = round_up(std::max(c->max_classes, 1), 4);
   if (c->max_classes > 0) {
     const size_t frows = std::max((size_t)pl.main.P, prow_win);
@@ -268,43 +308,71 @@ struct BlockW {
 
 struct vit_model {
   Plan pl;
+  int device = 0;        // the device holding the weights (current at vit_create)
   char* wbase = nullptr;
-  char* sbase = nullptr;
+  char* sbase = nullptr;  // bound workspace, or NULL (then only vit_forward_static runs)
   const uint16_t* patch_w = nullptr;
   const float *patch_b = nullptr, *cls = nullptr, *reg = nullptr, *norm_g = nullptr, *norm_b = nullptr;
   std::vector<BlockW> blocks;
-  float* x = nullptr;
-  uint16_t *h = nullptr, *q = nullptr, *k = nullptr, *vt = nullptr, *o = nullptr, *f = nullptr, *cols = nullptr;
+  Acts act;               // activations in the bound workspace
   float *crops = nullptr, *cos = nullptr;
   uint16_t *feats = nullptr, *clsb = nullptr;
   int* corners = nullptr;
 };
 
+// ------------------------------------------------------------------ static scratch
+// The activations of vit_forward_static.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is taken once per
+// device with hipGetSymbolAddress (that device current) and only that address
+// is passed to kernels.
+static constexpr size_t kScratchBytes = (size_t)VIT_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on `dev`, which must be the current device;
+// resolved on the first call for that device.
+int scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(VIT_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+    if (!p || (uintptr_t)p % kAlign) return fail(VIT_ERR_HIP, "static scratch address is not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VIT_OK;
+}
 
 // Patch embedding, blocks and the final step for `batch` images of geometry g.
 // final_feats == false: final LayerNorm into tokens_out (fp32 [batch, N, D]);
 // final_feats == true: LayerNorm + L2 of the patch rows into m->feats (bf16).
-int run_encoder(vit_model* m, const Geom& g, const float* images, int batch, float* tokens_out, float* taps,
-                bool final_feats, hipStream_t st) {
+int run_encoder(vit_model* m, const Acts& a, const Geom& g, const float* images, int batch, float* tokens_out,
+                float* taps, bool final_feats, hipStream_t st) {
   const Plan& pl = m->pl;
   const int D = pl.D, Hm = pl.Hm, N = g.N;
   const int M = batch * N;
   const float eps = pl.cfg.ln_eps;
   // im2col of the images, and the CLS and register rows of x (the patch GEMM writes the others)
-  VIT_HIP(vit::launch_patchify(images, batch, g.img_h, g.img_w, pl.p, pl.kpad, m->cols, m->x, N, D, m->cls, g.pos,
+  VIT_HIP(vit::launch_patchify(images, batch, g.img_h, g.img_w, pl.p, pl.kpad, a.cols, a.x, N, D, m->cls, g.pos,
                                m->reg, pl.R, st),
           "patchify");
   vit::EpiParams pe;
   pe.kind = vit::EPI_PATCH;
   pe.bias = m->patch_b;
   pe.pos = g.pos;
-  pe.out = m->x;
+  pe.out = a.x;
   pe.ldc = D;
   pe.tokens = N;
   pe.patches = g.P;
   pe.regs = pl.R;
-  VIT_HIP(vit::launch_gemm(m->cols, m->patch_w, batch * g.P, D, pl.kpad, pe, st), "patch embedding");
+  VIT_HIP(vit::launch_gemm(a.cols, m->patch_w, batch * g.P, D, pl.kpad, pe, st), "patch embedding");
   int tap_i = 0;
   // For D = 384 the residual GEMMs also apply the LayerNorm that follows them
   // (out projection -> LN2, fc2 -> LN1 of the next block), so h arrives ready.
@@ -312,64 +380,64 @@ int run_encoder(vit_model* m, const Geom& g, const float* images, int batch, flo
   for (int l = 0; l < pl.L; ++l) {
     const BlockW& w = m->blocks[l];
     if (!fuse_ln || l == 0)
-      VIT_HIP(vit::launch_layernorm(m->x, M, D, w.ln1_g, w.ln1_b, eps, m->h, false, st), "ln1");
+      VIT_HIP(vit::launch_layernorm(a.x, M, D, w.ln1_g, w.ln1_b, eps, a.h, false, st), "ln1");
     vit::EpiParams eq;
     eq.kind = vit::EPI_QKV;
     eq.bias = w.bqkv;
-    eq.q = m->q;
-    eq.k = m->k;
-    eq.vt = m->vt;
+    eq.q = a.q;
+    eq.k = a.k;
+    eq.vt = a.vt;
     eq.tokens = N;
     eq.heads = pl.heads;
     eq.nv = g.nv;
-    VIT_HIP(vit::launch_gemm(m->h, w.wqkv, M, 3 * D, D, eq, st), "qkv");
-    VIT_HIP(vit::launch_attention(m->q, m->k, m->vt, batch, N, pl.heads, g.nv, m->o, st),
+    VIT_HIP(vit::launch_gemm(a.h, w.wqkv, M, 3 * D, D, eq, st), "qkv");
+    VIT_HIP(vit::launch_attention(a.q, a.k, a.vt, batch, N, pl.heads, g.nv, a.o, st),
             "attention");
     vit::EpiParams eo;
     eo.kind = fuse_ln ? vit::EPI_RESIDUAL_LN : vit::EPI_RESIDUAL;
     eo.bias = w.bo;
     eo.ls = w.ls1;
-    eo.out = m->x;
+    eo.out = a.x;
     eo.ldc = D;
     eo.ln_g = w.ln2_g;
     eo.ln_b = w.ln2_b;
     eo.eps = eps;
-    eo.h = m->h;
-    VIT_HIP(vit::launch_gemm(m->o, w.wo, M, D, D, eo, st), "out projection");
-    if (!fuse_ln) VIT_HIP(vit::launch_layernorm(m->x, M, D, w.ln2_g, w.ln2_b, eps, m->h, false, st), "ln2");
+    eo.h = a.h;
+    VIT_HIP(vit::launch_gemm(a.o, w.wo, M, D, D, eo, st), "out projection");
+    if (!fuse_ln) VIT_HIP(vit::launch_layernorm(a.x, M, D, w.ln2_g, w.ln2_b, eps, a.h, false, st), "ln2");
     vit::EpiParams e1;
     e1.kind = vit::EPI_GELU_BF16;
     e1.bias = w.b1;
-    e1.out = m->f;
+    e1.out = a.f;
     e1.ldc = Hm;
-    VIT_HIP(vit::launch_gemm(m->h, w.w1, M, Hm, D, e1, st), "fc1");
+    VIT_HIP(vit::launch_gemm(a.h, w.w1, M, Hm, D, e1, st), "fc1");
     vit::EpiParams e2;
     const bool fuse_next = fuse_ln && l + 1 < pl.L;
     e2.kind = fuse_next ? vit::EPI_RESIDUAL_LN : vit::EPI_RESIDUAL;
     e2.bias = w.b2;
     e2.ls = w.ls2;
-    e2.out = m->x;
+    e2.out = a.x;
     e2.ldc = D;
     if (fuse_next) {
       e2.ln_g = m->blocks[l + 1].ln1_g;
       e2.ln_b = m->blocks[l + 1].ln1_b;
       e2.eps = eps;
-      e2.h = m->h;
+      e2.h = a.h;
     }
-    VIT_HIP(vit::launch_gemm(m->f, w.w2, M, D, Hm, e2, st), "fc2");
+    VIT_HIP(vit::launch_gemm(a.f, w.w2, M, D, Hm, e2, st), "fc2");
     if (taps && l < 32 && ((pl.cfg.tap_mask >> l) & 1u)) {
       const size_t per_img = (size_t)pl.ntaps * D * g.P;
-      VIT_HIP(vit::launch_tap(m->x, batch, N, 1 + pl.R, g.P, D, m->norm_g, m->norm_b, eps,
+      VIT_HIP(vit::launch_tap(a.x, batch, N, 1 + pl.R, g.P, D, m->norm_g, m->norm_b, eps,
                               taps + (size_t)tap_i * D * g.P, per_img, st),
               "tap");
       ++tap_i;
     }
   }
   if (final_feats) {
-    VIT_HIP(vit::launch_ln_l2(m->x, batch, N, 1 + pl.R, g.P, D, m->norm_g, m->norm_b, eps, m->feats, st),
+    VIT_HIP(vit::launch_ln_l2(a.x, batch, N, 1 + pl.R, g.P, D, m->norm_g, m->norm_b, eps, m->feats, st),
             "patch features");
   } else {
-    VIT_HIP(vit::launch_layernorm(m->x, M, D, m->norm_g, m->norm_b, eps, tokens_out, true, st), "final norm");
+    VIT_HIP(vit::launch_layernorm(a.x, M, D, m->norm_g, m->norm_b, eps, tokens_out, true, st), "final norm");
   }
   return VIT_OK;
 }
@@ -418,16 +486,28 @@ int vit_create(const vit_config* cfg, const float* host_params, size_t host_floa
   Plan pl;
   int r = build_plan(cfg, pl);
   if (r) return r;
-  if (!host_params || !d_weights || !d_workspace) return fail(VIT_ERR_ARG, "NULL parameter or buffer pointer");
+  if (!host_params || !d_weights) return fail(VIT_ERR_ARG, "NULL parameter or weight pointer");
+  // no workspace (NULL, 0 bytes): only vit_forward_static, whose activations
+  // live in the library's static array, can run on the model
+  const bool bound = d_workspace != nullptr;
+  if (!bound && workspace_bytes != 0) return fail(VIT_ERR_ARG, "NULL workspace with a nonzero size");
   if (host_floats != pl.host_floats)
     return fail(VIT_ERR_SIZE, "parameter blob has " + std::to_string(host_floats) + " floats, expected " +
                                   std::to_string(pl.host_floats));
   if (weight_bytes < pl.wl.total) return fail(VIT_ERR_SIZE, "weight buffer smaller than vit_plan's weight_bytes");
-  if (workspace_bytes < pl.ws.total) return fail(VIT_ERR_SIZE, "workspace smaller than vit_plan's workspace_bytes");
+  if (bound && workspace_bytes < pl.ws.total)
+    return fail(VIT_ERR_SIZE, "workspace smaller than vit_plan's workspace_bytes");
   if (((uintptr_t)d_weights | (uintptr_t)d_workspace) % kAlign)
     return fail(VIT_ERR_ARG, "device buffers must be 256-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   if (vit::prepare_gemm() != hipSuccess) return fail(VIT_ERR_HIP, "GEMM tables could not be set up");
+  int device = 0;
+  VIT_HIP(hipGetDevice(&device), "hipGetDevice");
+  {  // the static scratch's address on this device, resolved once at set-up
+    void* unused = nullptr;
+    r = scratch_on(device, &unused);
+    if (r) return r;
+  }
 
   const size_t D = pl.D, Hm = pl.Hm, R = pl.R, p = pl.p;
   const WeightLayout& wl = pl.wl;
@@ -481,6 +561,7 @@ int vit_create(const vit_config* cfg, const float* host_params, size_t host_floa
   auto* m = new (std::nothrow) vit_model();
   if (!m) return fail(VIT_ERR_ARG, "out of host memory");
   m->pl = pl;
+  m->device = device;
   m->wbase = (char*)d_weights;
   m->sbase = (char*)d_workspace;
   char* W = m->wbase;
@@ -513,15 +594,8 @@ int vit_create(const vit_config* cfg, const float* host_params, size_t host_floa
   }
   char* S = m->sbase;
   const WorkLayout& ws = pl.ws;
-  m->x = (float*)(S + ws.x);
-  m->h = (uint16_t*)(S + ws.h);
-  m->q = (uint16_t*)(S + ws.q);
-  m->k = (uint16_t*)(S + ws.k);
-  m->vt = (uint16_t*)(S + ws.vt);
-  m->o = (uint16_t*)(S + ws.o);
-  m->f = (uint16_t*)(S + ws.f);
-  m->cols = (uint16_t*)(S + ws.cols);
-  if (pl.cfg.max_classes > 0) {
+  if (bound) m->act = acts_at(S, ws);
+  if (bound && pl.cfg.max_classes > 0) {
     m->crops = pl.nwin ? (float*)(S + ws.crops) : nullptr;
     m->feats = (uint16_t*)(S + ws.feats);
     m->clsb = (uint16_t*)(S + ws.clsb);
@@ -535,8 +609,10 @@ int vit_create(const vit_config* cfg, const float* host_params, size_t host_floa
   };
   hipError_t e = hipMemcpyAsync(d_weights, stage.data(), wl.total, hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return bail(hip_fail(e, "weight upload"));
-  e = hipMemsetAsync(d_workspace, 0, pl.ws.total, st);
-  if (e != hipSuccess) return bail(hip_fail(e, "workspace clear"));
+  if (bound) {
+    e = hipMemsetAsync(d_workspace, 0, pl.ws.total, st);
+    if (e != hipSuccess) return bail(hip_fail(e, "workspace clear"));
+  }
   const float* pos_native = (const float*)(W + wl.pos_native);
   if (wl.pos_main != wl.pos_native) {
     e = vit::launch_pos_resample(pos_native, pl.cfg.pos_grid_h, pl.cfg.pos_grid_w, (float*)(W + wl.pos_main),
@@ -562,7 +638,30 @@ int vit_forward(vit_model* m, const float* d_images, int batch, float* d_tokens,
   if (!m || !d_images || !d_tokens) return fail(VIT_ERR_ARG, "NULL model, image or token pointer");
   if (batch < 1 || batch > m->pl.cfg.max_batch) return fail(VIT_ERR_SIZE, "batch must be in [1, max_batch]");
   if ((uintptr_t)d_tokens % 16) return fail(VIT_ERR_ARG, "d_tokens must be 16-byte aligned");
-  return run_encoder(m, m->pl.main, d_images, batch, d_tokens, d_taps, false, (hipStream_t)stream);
+  if (!m->sbase) return fail(VIT_ERR_ARG, "model created without a workspace (use vit_forward_static)");
+  return run_encoder(m, m->act, m->pl.main, d_images, batch, d_tokens, d_taps, false, (hipStream_t)stream);
+}
+
+int vit_forward_static(vit_model* m, const float* d_images, int batch, float* d_tokens, float* d_taps,
+                       void* stream) {
+  if (!m || !d_images || !d_tokens) return fail(VIT_ERR_ARG, "NULL model, image or token pointer");
+  if (batch < 1 || batch > m->pl.cfg.max_batch) return fail(VIT_ERR_SIZE, "batch must be in [1, max_batch]");
+  if ((uintptr_t)d_tokens % 16) return fail(VIT_ERR_ARG, "d_tokens must be 16-byte aligned");
+  const Plan& pl = m->pl;
+  WorkLayout s;
+  const size_t need = layout_acts(pl, (size_t)batch * pl.main.N, (size_t)batch * pl.D * pl.main.nv,
+                                  (size_t)batch * pl.main.P, s);
+  if (need > kScratchBytes)
+    return fail(VIT_ERR_SIZE, "batch " + std::to_string(batch) + " needs " + std::to_string(need) +
+                                  " bytes of activations; the static scratch holds " + std::to_string(kScratchBytes));
+  void* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    base = m->device >= 0 && m->device < kMaxDevices ? g_scratch_ptr[m->device] : nullptr;
+  }
+  if (!base) return fail(VIT_ERR_HIP, "static scratch not resolved for the model's device");
+  return run_encoder(m, acts_at((char*)base, s), pl.main, d_images, batch, d_tokens, d_taps, false,
+                     (hipStream_t)stream);
 }
 
 int vit_descriptor(vit_model* m, const float* d_tokens, int batch, float* d_desc, void* stream) {
@@ -582,6 +681,7 @@ int vit_patch_scores(vit_model* m, const float* d_image, const float* d_class_em
   if (classes < 1 || classes > pl.cfg.max_classes) return fail(VIT_ERR_SIZE, "classes must be in [1, max_classes]");
   if (mode != 0 && mode != 1) return fail(VIT_ERR_ARG, "mode must be 0 (whole) or 1 (slide)");
   if (mode == 1 && pl.nwin == 0) return fail(VIT_ERR_UNSUPPORTED, "model created without a slide window");
+  if (!m->sbase) return fail(VIT_ERR_ARG, "model created without a workspace");
   hipStream_t st = (hipStream_t)stream;
   const int D = pl.D, H = pl.cfg.img_h, W = pl.cfg.img_w, ldc = pl.ws.ldc_cos;
   VIT_HIP(vit::launch_to_bf16(d_class_emb, (size_t)classes * D, m->clsb, st), "class embeddings");
@@ -590,7 +690,7 @@ int vit_patch_scores(vit_model* m, const float* d_image, const float* d_class_em
   ec.out = m->cos;
   ec.ldc = ldc;
   if (mode == 0) {
-    int r = run_encoder(m, pl.main, d_image, 1, nullptr, nullptr, true, st);
+    int r = run_encoder(m, m->act, pl.main, d_image, 1, nullptr, nullptr, true, st);
     if (r) return r;
     VIT_HIP(vit::launch_gemm(m->feats, m->clsb, pl.main.P, classes, D, ec, st), "scores");
     VIT_HIP(vit::launch_upsample_argmax(m->cos, pl.main.gh, pl.main.gw, classes, ldc, H, W, d_labels, d_dense, st),
@@ -599,7 +699,7 @@ int vit_patch_scores(vit_model* m, const float* d_image, const float* d_class_em
   } else {
     const int side = pl.cfg.window;
     VIT_HIP(vit::launch_crops(d_image, H, W, m->corners, pl.nwin, side, m->crops, st), "crops");
-    int r = run_encoder(m, pl.win, m->crops, pl.nwin, nullptr, nullptr, true, st);
+    int r = run_encoder(m, m->act, pl.win, m->crops, pl.nwin, nullptr, nullptr, true, st);
     if (r) return r;
     VIT_HIP(vit::launch_gemm(m->feats, m->clsb, pl.nwin * pl.win.P, classes, D, ec, st), "scores");
     VIT_HIP(vit::launch_slide_merge(m->cos, pl.nwin, m->corners, pl.win.gh, classes, ldc, side, H, W, d_labels, d_dense,
