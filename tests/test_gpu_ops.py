@@ -74,7 +74,9 @@ SHAPES = [(1, 64, 64), (5, 150, 384), (130, 384, 384), (446, 1152, 384), (1000, 
           (3000, 3000, 640),   # 128 x 128 tiles, ragged in M and N
           (4100, 8200, 192),   # 256 x 256 tiles (M N >= 32M), ragged in M and N
           # 128 x 128 tiles whose last full row tile also takes the 1..32 rows after it
-          (4101, 4096, 128), (4128, 3072, 192), (3969, 2048, 256), (4100, 1024, 1024)]
+          (4101, 4096, 128), (4128, 3072, 192), (3969, 2048, 256), (4100, 1024, 1024),
+          # 256 x 256 tiles (>= 224 of them, W of >= 4M values) with 5 or 32 such rows
+          (1285, 16384, 256), (1056, 16384, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

@@ -18,7 +18,8 @@
 // ids are remapped so that each XCD (8 per chip, own L2) owns a contiguous
 // range of tiles, grouped along M.  Tile shapes were chosen by measurement on
 // MI355X: small tiles with several workgroups resident per CU beat large tiles
-// on the encoder's shapes (K = 384..4096, M = 4101..16404).
+// on most of the encoder's shapes (K = 384..4096, M = 4101..16404); 256 x 256
+// tiles win where they fill whole rounds of the CUs.
 #include "common.h"
 #include "kernels.h"
 
@@ -838,12 +839,12 @@ struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, S = S_;
 };
 
-// 128-row tiles with plain row epilogues can take up to 32 rows past the last
-// full row tile (see gemm_bf16_kernel's XR).
+// 128- and 256-row tiles with plain row epilogues can take up to 32 rows past
+// the last full row tile (see gemm_bf16_kernel's XR).
 template <class C, class Epi, class AM, class MT>
 constexpr bool takes_extra_rows() {
-  return C::BM == 128 && C::WGM == 2 && C::BN / C::WGN == 64 && !HasRowLN<Epi>::value && !HasTransposed<Epi>::value &&
-         !AM::kConv && std::is_same<MT, MmaBf16>::value;
+  return (C::BM == 128 || C::BM == 256) && C::WGM == 2 && C::BN / C::WGN == 64 && !HasRowLN<Epi>::value &&
+         !HasTransposed<Epi>::value && !AM::kConv && std::is_same<MT, MmaBf16>::value;
 }
 
 template <class C, class Epi, class AM = AMapLinear, class MT = MmaBf16>
@@ -883,6 +884,17 @@ hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const
                     AM am = {}) {
   const long mid_tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
   if ((long)M * N >= 32L * 1024 * 1024) return run<CfgBig>(A, W, M, N, K, epi, s, am);
+  if constexpr (takes_extra_rows<CfgBig, Epi, AM, MmaBf16>()) {
+    // 256 x 256 tiles, the rows past the last full row tile taken by row tile
+    // 0, when they fill at least 7/8 of the CUs and W holds >= 4M values:
+    // half the operand bytes per FLOP of 128 x 128 (ViT-L/16 b1 fc1, 4101 x
+    // 4096 x 1024: 16 x 16 tiles, 45.9 -> 42.3 us; b4 fc2, 16404 x 1024 x 4096:
+    // 138.6 -> 132.9 us; b4 out-proj with W of 1M values was slower, 47.1 ->
+    // 49.1 us; same-process A/B, outputs bit-identical)
+    const long big_tiles = (long)(M / 256) * ((N + 255) / 256);
+    if (M > 256 && M % 256 <= 32 && (long)K * N >= 4L * 1024 * 1024 && big_tiles >= 224)
+      return run<CfgBig>(A, W, M, N, K, epi, s, am);
+  }
   if (mid_tiles < 256) {  // fewer 128 x 128 tiles than compute units: 64 x 128, or 64 x 64 if that too is short
     const long small_tiles = (long)((M + 63) / 64) * ((N + 127) / 128);
     if (small_tiles >= 256) return run<CfgSmall>(A, W, M, N, K, epi, s, am);
