@@ -525,6 +525,36 @@ def bench_fp8(steps=30, warmup=5):
     return res
 
 
+def gemm_vs_library(steps=30, warmup=5):
+    """The library's GEMM (bias epilogue, bf16 out) against hipBLASLt, reached
+    through torch.nn.functional.linear in bf16 with the same bias, on the
+    encoder's Linear shapes (ViT-L/16 @1024 b1, ViT-S/16 @336 b32); the same
+    process and inputs, back-to-back launches timed as a loop average."""
+    import torch
+    import vision_transformer_encoder_block_amd as vit
+    g = torch.Generator(device="cuda").manual_seed(11)
+    shapes = [("ViT-L b1 qkv", 4101, 3072, 1024), ("ViT-L b1 out-proj", 4101, 1024, 1024),
+              ("ViT-L b1 fc1", 4101, 4096, 1024), ("ViT-L b1 fc2", 4101, 1024, 4096),
+              ("ViT-S b32 qkv", 14272, 1152, 384), ("ViT-S b32 out-proj", 14272, 384, 384),
+              ("ViT-S b32 fc1", 14272, 1536, 384), ("ViT-S b32 fc2", 14272, 384, 1536)]
+    rows = []
+    for name, M, N, K in shapes:
+        a = (torch.randn(M, K, generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+        w = (torch.randn(N, K, generator=g, device="cuda") * 0.05).to(torch.bfloat16)
+        bias = torch.randn(N, generator=g, device="cuda") * 0.1
+        bias16 = bias.to(torch.bfloat16)
+        out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        ours = time_loop(lambda: vit.vit_op_linear(a, w, bias, M, N, K, vit.EPI_BIAS_BF16, None, out), steps, warmup)
+        lib = time_loop(lambda: torch.nn.functional.linear(a, w, bias16), steps, warmup)
+        fl = 2.0 * M * N * K
+        rows.append({"op": name, "shape": [M, N, K], "ours_us": round(ours * 1e3, 2), "hipblaslt_us": round(lib * 1e3, 2),
+                     "ours_tflops": round(fl / (ours * 1e-3) / 1e12, 1),
+                     "hipblaslt_tflops": round(fl / (lib * 1e-3) / 1e12, 1)})
+        log(json.dumps(rows[-1]))
+        del a, w, out
+    return rows
+
+
 def head_cpu_baseline(images=8):
     """The head's oracle (float64 NumPy), untuned, on DINOv2-S/14 @518 stand-in taps."""
     import synth
@@ -552,6 +582,8 @@ def main():
     ap.add_argument("--head-only", action="store_true",
                     help="run only the semantic-head leg (DINOv2-S/14 @518 b8 + head) and print its JSON")
     ap.add_argument("--fp8-only", action="store_true", help="run only the fp8 linear leg and print its JSON")
+    ap.add_argument("--gemm-vs-library", action="store_true",
+                    help="run only the comparison of the library's GEMM with hipBLASLt (through torch) and print it")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "WORKLOAD"),
                     help="host only: turn two rocprofv3 --pmc CSVs of --breakdown-only WORKLOAD into "
                          "profiles/hbm_traffic.json")
@@ -579,6 +611,9 @@ def main():
         return
     if args.fp8_only:
         print(json.dumps(bench_fp8(args.steps, args.warmup)), flush=True)
+        return
+    if args.gemm_vs_library:
+        print(json.dumps(gemm_vs_library(args.steps, args.warmup)), flush=True)
         return
     if args.copy_calibration:
         copy_calibration()

@@ -308,6 +308,10 @@ struct HasRowLN : std::false_type {};
 template <class E>
 struct HasRowLN<E, std::void_t<decltype(E::kD)>> : std::true_type {};
 template <class E, class = void>
+struct HasChanLN : std::false_type {};
+template <class E>
+struct HasChanLN<E, std::void_t<decltype(E::kC)>> : std::true_type {};
+template <class E, class = void>
 struct HasTransposed : std::false_type {};
 template <class E>
 struct HasTransposed<E, std::void_t<decltype(&E::tile_transposed)>> : std::true_type {};
@@ -325,6 +329,24 @@ struct EpiResidualLN {
   const float* b;
   float eps;
   bf16_t* h;   // [M, kD] bf16
+};
+
+// Channel LayerNorm of whole rows (N = kC channels of a pixel), the semantic
+// head's ConvX block: y = LN(acc + bias) (biased variance, eps inside the
+// square root, affine), then SiLU y / (1 + e^-y) if `silu`, then a second
+// LayerNorm if g2 is non-null; bf16 into out[m * ld + c0 + n].
+template <int C>
+struct EpiChanLN {
+  static constexpr int kC = C;
+  const float* bias;  // may be null
+  const float* g;
+  const float* b;
+  float eps;
+  bool silu;
+  const float* g2;    // may be null
+  const float* b2;
+  bf16_t* out;
+  int ld, c0;
 };
 
 // Patch rows of the embedding GEMM: row m = b * patches + i goes to residual
@@ -465,7 +487,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   constexpr bool A_SPLIT = A_INS % NW == 0;         // instruction i of every wave reads the same operand
   constexpr int KS = BKT / MT::KPM;                 // MFMA k-steps per stage
   constexpr int STAGE_BYTES = (BM + BN + XR) * BKT * ES;  // A rows, W rows, then the extra A rows
-  static_assert(XR == 0 || (XR == 32 && !HasRowLN<Epi>::value && !HasTransposed<Epi>::value && !AM::kConv &&
+  static_assert(XR == 0 || (XR == 32 && !HasRowLN<Epi>::value && !HasChanLN<Epi>::value && !HasTransposed<Epi>::value && !AM::kConv &&
                             WGM == 2 && WTN == 64 && XR / (64 / (BKT * MT::ES / 16)) <= WGM * WGN),
                 "extra rows: plain row epilogues, one 32-column block per wave");
   static_assert(CPR == 4 || CPR == 8 || CPR == 16, "BK");
@@ -646,6 +668,72 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   __syncthreads();
 
   // accumulator element e of block (i, j): row 8*(e/4) + 4*lhalf + e%4, column lrow
+  if constexpr (HasChanLN<Epi>::value) {
+    // Whole pixel rows: stage acc + bias of the BM x kC tile (row stride
+    // kC + 4 floats), then the waves normalise the rows two at a time (32
+    // lanes per row, kC / 128 float4 per lane).
+    constexpr int D = Epi::kC;
+    static_assert(BN == D && BM == 32 * WGM && TM == 1, "row tile shape");
+    constexpr int LDR = D + 4;
+    constexpr int RPS = 32 * LDR * 4 <= STAGE_BYTES ? 32 : 16;  // staged rows per stage buffer
+    static_assert(RPS * LDR * 4 <= STAGE_BYTES && BM <= RPS * S, "staging must fit in the stage LDS");
+    constexpr int LPR = 32, V4 = D / (4 * LPR), PAIRS = BM / 2, PASSES = (PAIRS + NW - 1) / NW;
+    float* rows_lds[S];
+    static_for<0, S>([&](auto c) { rows_lds[decltype(c)::value] = reinterpret_cast<float*>(stage_lds<STAGE_BYTES, decltype(c)::value>()); });
+    auto row_ptr = [&](int r) { return rows_lds[r / RPS] + (r % RPS) * LDR; };
+    {
+      float bcol[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bcol[j] = epi.bias ? epi.bias[wn * WTN + j * 32 + lrow] : 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          row_ptr(wm * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3))[wn * WTN + j * 32 + lrow] = acc[0][j][e] + bcol[j];
+    }
+    __syncthreads();
+    const int sl = lane & 31;
+    const bool second = epi.g2 != nullptr;  // uniform
+    float4 gv[V4], bv[V4], g2v[V4], b2v[V4];
+#pragma unroll
+    for (int i = 0; i < V4; ++i) {
+      gv[i] = reinterpret_cast<const float4*>(epi.g)[sl + LPR * i];
+      bv[i] = reinterpret_cast<const float4*>(epi.b)[sl + LPR * i];
+      g2v[i] = second ? reinterpret_cast<const float4*>(epi.g2)[sl + LPR * i] : make_float4(1.f, 1.f, 1.f, 1.f);
+      b2v[i] = second ? reinterpret_cast<const float4*>(epi.b2)[sl + LPR * i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float4 v[PASSES][V4];
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const float* src = row_ptr(min(pass * NW + wave, PAIRS - 1) * 2 + (lane >> 5));
+#pragma unroll
+      for (int i = 0; i < V4; ++i) v[pass][i] = *reinterpret_cast<const float4*>(src + 4 * (sl + LPR * i));
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      if (PAIRS % NW != 0 && pass * NW + wave >= PAIRS) break;  // wave-uniform
+      const int m = m0 + (pass * NW + wave) * 2 + (lane >> 5);
+      ln_group_normalize<V4, LPR>(v[pass], gv, bv, epi.eps, D);
+      if (epi.silu) {
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+          float4& t = v[pass][i];
+          t = make_float4(t.x / (1.f + expf(-t.x)), t.y / (1.f + expf(-t.y)), t.z / (1.f + expf(-t.z)),
+                          t.w / (1.f + expf(-t.w)));
+        }
+      }
+      if (second) ln_group_normalize<V4, LPR>(v[pass], g2v, b2v, epi.eps, D);
+      if (m < M) {
+        bf16_t* orow = epi.out + (size_t)m * epi.ld + epi.c0;
+#pragma unroll
+        for (int i = 0; i < V4; ++i)
+          reinterpret_cast<uint2*>(orow)[sl + LPR * i] =
+              make_uint2(pack_bf16x2(v[pass][i].x, v[pass][i].y), pack_bf16x2(v[pass][i].z, v[pass][i].w));
+      }
+    }
+    return;
+  }
   if constexpr (HasRowLN<Epi>::value) {
     // Whole rows: stage acc + bias of the BM x kD tile (row stride kD + 4
     // floats; RPS consecutive rows per pipeline stage buffer), then the waves
@@ -752,7 +840,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
       return;
     }
   }
-  if constexpr (!HasRowLN<Epi>::value) {
+  if constexpr (!HasRowLN<Epi>::value && !HasChanLN<Epi>::value) {
     // Each wave stages one 32-row block of its tile at a time (row stride WTN + 8
     // floats: the two lane halves land on disjoint banks), then every lane
     // handles 4 consecutive columns of PASSES rows.  The staging areas live in
@@ -844,7 +932,7 @@ struct Cfg {
 template <class C, class Epi, class AM, class MT>
 constexpr bool takes_extra_rows() {
   return (C::BM == 128 || C::BM == 256) && C::WGM == 2 && C::BN / C::WGN == 64 && !HasRowLN<Epi>::value &&
-         !HasTransposed<Epi>::value && !AM::kConv && std::is_same<MT, MmaBf16>::value;
+         !HasChanLN<Epi>::value && !HasTransposed<Epi>::value && !AM::kConv && std::is_same<MT, MmaBf16>::value;
 }
 
 template <class C, class Epi, class AM = AMapLinear, class MT = MmaBf16>
@@ -945,6 +1033,26 @@ hipError_t dispatch_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, c
 
 using CfgRowLN = Cfg<64, EpiResidualLN::kD, 64, 2, 4, 2>;
 
+// Channel LayerNorm epilogue: 32 pixel rows x all kC channels per workgroup.
+template <int C, class AM>
+hipError_t run_chan_ln(const bf16_t* A, const bf16_t* W, int M, int K, const EpiParams& ep, hipStream_t s, AM am) {
+  const EpiChanLN<C> e{ep.bias, ep.ln_g, ep.ln_b, ep.eps, ep.silu, ep.ln2_g, ep.ln2_b, (bf16_t*)ep.out, ep.ldc, ep.c0};
+  return run<Cfg<32, C, 64, 1, 4, 2>>(A, W, M, C, K, e, s, am);
+}
+
+// Checks shared by the linear and convolution forms of EPI_CHAN_LN.
+template <class AM>
+hipError_t dispatch_chan_ln(const bf16_t* A, const bf16_t* W, int M, int N, int K, const EpiParams& ep, hipStream_t s,
+                            AM am = {}) {
+  auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  if (!chan_ln_fusable(N) || !ep.out || !ep.ln_g || !ep.ln_b || !al16(ep.ln_g) || !al16(ep.ln_b) ||
+      (ep.ln2_g && (!ep.ln2_b || !al16(ep.ln2_g) || !al16(ep.ln2_b))) || ep.ldc % 4 || ep.c0 % 4 || ep.c0 < 0 ||
+      ep.c0 + N > ep.ldc || reinterpret_cast<uintptr_t>(ep.out) % 8)
+    return hipErrorInvalidValue;
+  if (N == 128) return run_chan_ln<128>(A, W, M, K, ep, s, am);
+  return run_chan_ln<256>(A, W, M, K, ep, s, am);
+}
+
 // fp8 tiles, chosen by the same rules as the bf16 ones (no 256 x 256 tile:
 // its fp8 fragments would not fit the registers)
 template <class Epi>
@@ -1010,6 +1118,8 @@ hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, int M, int N, int K
       EpiResidualLN e{ep.bias, ep.ls, (float*)ep.out, ep.ln_g, ep.ln_b, ep.eps, (bf16_t*)ep.h};
       return run<CfgRowLN>(A, W, M, N, K, e, s);
     }
+    case EPI_CHAN_LN:
+      return dispatch_chan_ln(A, W, M, N, K, ep, s, AMapLinear{});
     case EPI_PATCH: {
       const bool vec = par16 && al(ep.pos, 16) && al(ep.out, 16);
       EpiPatch e{ep.bias, ep.pos, (float*)ep.out, ep.ldc, ep.tokens, ep.patches, ep.regs, make_fastdiv(ep.patches),
@@ -1050,6 +1160,8 @@ hipError_t launch_gemm_conv3(const uint16_t* in, int ld_in, int c0, int C, int b
       const bool vec = ep.ldc % 4 == 0 && par16 && al(ep.out, 16);
       return dispatch(in, W, (int)M, N, (int)K, EpiBiasF32{ep.bias, (float*)ep.out, ep.ldc, vec}, s, am);
     }
+    case EPI_CHAN_LN:
+      return dispatch_chan_ln(in, W, (int)M, N, (int)K, ep, s, am);
     default:
       return hipErrorInvalidValue;
   }

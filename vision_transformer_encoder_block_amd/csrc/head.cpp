@@ -266,27 +266,42 @@ int vit_head_forward(vit_head* h, const float* d_taps, int batch, float* d_logit
     return vit::launch_gemm_conv3(in, ld, c0, Cin, batch, c.grid_h, c.grid_w, bf(w, wo), N, f32_out(bias, outp, N), st);
   };
 
+  // ConvX blocks (conv, channel LayerNorm, SiLU; the output block adds the
+  // final LayerNorm): the GEMM epilogue normalises whole pixel rows and writes
+  // bf16 at column c0 of a row of width ld
+  auto convx = [&](size_t g_at, size_t b_at, uint16_t* outp, int ld, int c0, const float* g2 = nullptr,
+                   const float* b2 = nullptr) {
+    vit::EpiParams ep;
+    ep.kind = vit::EPI_CHAN_LN;
+    ep.ln_g = f32(w, g_at);
+    ep.ln_b = f32(w, b_at);
+    ep.eps = c.ln_eps;
+    ep.silu = true;
+    ep.ln2_g = g2;
+    ep.ln2_b = b2;
+    ep.out = outp;
+    ep.ldc = ld;
+    ep.c0 = c0;
+    return ep;
+  };
+  auto conv3x = [&](const uint16_t* in, int ld_in, int c0_in, size_t wo, const vit::EpiParams& ep) {
+    return vit::launch_gemm_conv3(in, ld_in, c0_in, H2, batch, c.grid_h, c.grid_w, bf(w, wo), H2, ep, st);
+  };
+
   // Projector P4
   HEAD_HIP(vit::launch_taps_cl(d_taps, batch, c.taps, c.dim, pl.P, x0, st), "taps to channels-last");
-  HEAD_HIP(gemm_f32(x0, pl.proj_w, W, T, nullptr, f), "projector conv");
-  HEAD_HIP(vit::launch_chan_ln(f, M, W, f32(w, pl.proj_g), f32(w, pl.proj_b), c.ln_eps, true, nullptr, nullptr, y,
-                               ldy, 0, st),
-           "projector LayerNorm");
+  HEAD_HIP(vit::launch_gemm(x0, bf(w, pl.proj_w), M, W, T, convx(pl.proj_g, pl.proj_b, y, ldy, 0), st),
+           "projector conv");
   for (int i = 0; i < kBottlenecks; ++i) {
     // input: b (channels H2 .. 2 H2) for the first, then the previous output
-    HEAD_HIP(conv3_f32(y, ldy, H2 * (i + 1), H2, pl.bn_w[i][0], H2, nullptr, f), "bottleneck conv 1");
-    HEAD_HIP(vit::launch_chan_ln(f, M, H2, f32(w, pl.bn_g[i][0]), f32(w, pl.bn_b[i][0]), c.ln_eps, true, nullptr,
-                                 nullptr, t, H2, 0, st),
-             "bottleneck LayerNorm 1");
-    HEAD_HIP(conv3_f32(t, H2, 0, H2, pl.bn_w[i][1], H2, nullptr, f), "bottleneck conv 2");
-    HEAD_HIP(vit::launch_chan_ln(f, M, H2, f32(w, pl.bn_g[i][1]), f32(w, pl.bn_b[i][1]), c.ln_eps, true, nullptr,
-                                 nullptr, y, ldy, H2 * (i + 2), st),
-             "bottleneck LayerNorm 2");
+    HEAD_HIP(conv3x(y, ldy, H2 * (i + 1), pl.bn_w[i][0], convx(pl.bn_g[i][0], pl.bn_b[i][0], t, H2, 0)),
+             "bottleneck conv 1");
+    HEAD_HIP(conv3x(t, H2, 0, pl.bn_w[i][1], convx(pl.bn_g[i][1], pl.bn_b[i][1], y, ldy, H2 * (i + 2))),
+             "bottleneck conv 2");
   }
-  HEAD_HIP(gemm_f32(y, pl.out_w, W, ldy, nullptr, f), "projector output conv");
-  HEAD_HIP(vit::launch_chan_ln(f, M, W, f32(w, pl.out_g), f32(w, pl.out_b), c.ln_eps, true, f32(w, pl.fin_g),
-                               f32(w, pl.fin_b), p4, W, 0, st),
-           "projector output LayerNorms");
+  HEAD_HIP(vit::launch_gemm(y, bf(w, pl.out_w), M, W, ldy,
+                            convx(pl.out_g, pl.out_b, p4, W, 0, f32(w, pl.fin_g), f32(w, pl.fin_b)), st),
+           "projector output conv");
   // Task head
   {
     vit::EpiParams ep;

@@ -6,7 +6,6 @@
 // neighbourhood in place).  What remains here is the data movement and the
 // per-pixel / per-group normalisations:
 //   taps_cl_kernel        channel-first fp32 taps -> channels-last bf16 concat
-//   chan_ln_kernel        channel LayerNorm (+ SiLU) (+ a second LayerNorm)
 //   groupnorm_gelu_kernel GroupNorm over (channels of a group x pixels) + GELU
 //   resize_nchw_kernel    bilinear resize of class-minor logits to [B, C, H, W]
 #include "common.h"
@@ -45,40 +44,6 @@ __global__ __launch_bounds__(256) void taps_cl_kernel(const float* __restrict__ 
       *reinterpret_cast<uint4*>(out + ((size_t)b * P + p0 + pl) * ldo + t * D + c0 + c) = u;
     }
   }
-}
-
-// Channel LayerNorm of rows of x [M, C] (C / 4 lanes per row, one float4
-// each), optionally SiLU and a second LayerNorm, written as bf16 to
-// out + m * ld_out + c0.  The statistics use the encoder's LayerNorm routine.
-template <int C>
-__global__ __launch_bounds__(256) void chan_ln_kernel(const float* __restrict__ x, int M, const float* __restrict__ g,
-                                                      const float* __restrict__ b, float eps, bool silu,
-                                                      const float* __restrict__ g2, const float* __restrict__ b2,
-                                                      uint16_t* __restrict__ out, int ld_out, int c0) {
-  constexpr int LPR = C / 4;
-  constexpr int RPW = 64 / LPR;          // rows per wave
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sl = lane % LPR;
-  const int m = (blockIdx.x * 4 + wave) * RPW + lane / LPR;
-  const int mc = min(m, M - 1);          // every lane joins the group sums
-  float4 v[1] = {reinterpret_cast<const float4*>(x + (size_t)mc * C)[sl]};
-  const float4 gg[1] = {reinterpret_cast<const float4*>(g)[sl]};
-  const float4 bb[1] = {reinterpret_cast<const float4*>(b)[sl]};
-  ln_group_normalize<1, LPR>(v, gg, bb, eps, C);
-  if (silu) {
-    v[0].x = v[0].x / (1.f + expf(-v[0].x));
-    v[0].y = v[0].y / (1.f + expf(-v[0].y));
-    v[0].z = v[0].z / (1.f + expf(-v[0].z));
-    v[0].w = v[0].w / (1.f + expf(-v[0].w));
-  }
-  if (g2) {
-    const float4 g2v[1] = {reinterpret_cast<const float4*>(g2)[sl]};
-    const float4 b2v[1] = {reinterpret_cast<const float4*>(b2)[sl]};
-    ln_group_normalize<1, LPR>(v, g2v, b2v, eps, C);
-  }
-  if (m < M)
-    *reinterpret_cast<uint2*>(out + (size_t)m * ld_out + c0 + sl * 4) =
-        make_uint2(pack_bf16x2(v[0].x, v[0].y), pack_bf16x2(v[0].z, v[0].w));
 }
 
 // GroupNorm (8 channels per group) over the P pixels of one image, then the
@@ -217,27 +182,6 @@ hipError_t launch_taps_cl(const float* taps, int batch, int ntaps, int D, int P,
   if (batch < 1 || ntaps < 1 || D % 64 || P < 1 || (long)batch * ntaps > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(taps_cl_kernel, dim3((P + 63) / 64, D / 64, batch * ntaps), dim3(256), 0, s, taps, ntaps, D, P,
                      out);
-  return hipGetLastError();
-}
-
-hipError_t launch_chan_ln(const float* x, int M, int C, const float* g, const float* b, float eps, bool silu,
-                          const float* g2, const float* b2, uint16_t* out, int ld_out, int c0, hipStream_t s) {
-  if (M < 1 || ld_out % 4 || c0 % 4 || c0 + C > ld_out) return hipErrorInvalidValue;
-  if (C == 256) {
-    const int rows_per_block = 4 * (64 / 64);
-    hipLaunchKernelGGL(chan_ln_kernel<256>, dim3((M + rows_per_block - 1) / rows_per_block), dim3(256), 0, s, x, M,
-                       g, b, eps, silu, g2, b2, out, ld_out, c0);
-  } else if (C == 128) {
-    const int rows_per_block = 4 * (64 / 32);
-    hipLaunchKernelGGL(chan_ln_kernel<128>, dim3((M + rows_per_block - 1) / rows_per_block), dim3(256), 0, s, x, M,
-                       g, b, eps, silu, g2, b2, out, ld_out, c0);
-  } else if (C == 64) {
-    const int rows_per_block = 4 * (64 / 16);
-    hipLaunchKernelGGL(chan_ln_kernel<64>, dim3((M + rows_per_block - 1) / rows_per_block), dim3(256), 0, s, x, M,
-                       g, b, eps, silu, g2, b2, out, ld_out, c0);
-  } else {
-    return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 

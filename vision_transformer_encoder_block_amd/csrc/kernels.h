@@ -16,6 +16,8 @@ enum EpiKind {
   EPI_QKV = 4,         // head split into q (scaled), k, vt (transposed, permuted)
   EPI_PATCH = 5,       // residual row of patch token: acc + bias[n] + pos[1 + i][n]
   EPI_RESIDUAL_LN = 6, // EPI_RESIDUAL, then h = LayerNorm(out row) in bf16 (N = 384 only)
+  EPI_CHAN_LN = 7,     // channel LayerNorm of the row (acc + bias), SiLU, optional second
+                       // LayerNorm; bf16 into out + m * ldc + c0 (N = 128 or 256)
 };
 
 struct EpiParams {
@@ -35,12 +37,20 @@ struct EpiParams {
   const float* pos = nullptr;
   int patches = 0;
   int regs = 0;
-  // EPI_RESIDUAL_LN
+  // EPI_RESIDUAL_LN, EPI_CHAN_LN
   const float* ln_g = nullptr;
   const float* ln_b = nullptr;
   float eps = 0.f;
   uint16_t* h = nullptr;
+  // EPI_CHAN_LN (out is bf16 here)
+  int c0 = 0;
+  bool silu = false;
+  const float* ln2_g = nullptr;  // second LayerNorm (after SiLU) if non-null
+  const float* ln2_b = nullptr;
 };
+
+// Widths for which launch_gemm / launch_gemm_conv3 fuse the channel LayerNorm.
+constexpr bool chan_ln_fusable(int n) { return n == 128 || n == 256; }
 
 // Widths for which launch_gemm fuses the LayerNorm after a residual update.
 constexpr bool residual_ln_fusable(int n) { return n == 384; }
@@ -117,10 +127,6 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
 // ---- semantic head (channels-last activations, one row per pixel)
 // Taps [batch, ntaps, D, P] fp32 (channel-first) -> out bf16 [batch * P, ntaps * D].
 hipError_t launch_taps_cl(const float* taps, int batch, int ntaps, int D, int P, uint16_t* out, hipStream_t s);
-// Channel LayerNorm of rows of x [M, C] fp32 (C = 64, 128 or 256), then SiLU if
-// `silu`, then a second LayerNorm if g2 != null; bf16 into out + m * ld_out + c0.
-hipError_t launch_chan_ln(const float* x, int M, int C, const float* g, const float* b, float eps, bool silu,
-                          const float* g2, const float* b2, uint16_t* out, int ld_out, int c0, hipStream_t s);
 // GroupNorm (C = 8 * groups) of x [batch * P, C] fp32 per image, affine, exact GELU -> bf16 [batch * P, C].
 hipError_t launch_groupnorm_gelu(const float* x, int batch, int P, int C, int groups, const float* g, const float* b,
                                  float eps, uint16_t* out, hipStream_t s);
