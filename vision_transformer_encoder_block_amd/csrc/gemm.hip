@@ -1037,6 +1037,8 @@ using CfgRowLN = Cfg<64, EpiResidualLN::kD, 64, 2, 4, 2>;
 template <int C, class AM>
 hipError_t run_chan_ln(const bf16_t* A, const bf16_t* W, int M, int K, const EpiParams& ep, hipStream_t s, AM am) {
   const EpiChanLN<C> e{ep.bias, ep.ln_g, ep.ln_b, ep.eps, ep.silu, ep.ln2_g, ep.ln2_b, (bf16_t*)ep.out, ep.ldc, ep.c0};
+  // 32-row tiles (about 1.3 workgroups per CU at 8 x 37 x 37 pixels) measured
+  // faster than 64-row ones for every conv of the head (b8: 288 vs 298 us)
   return run<Cfg<32, C, 64, 1, 4, 2>>(A, W, M, C, K, e, s, am);
 }
 
