@@ -113,6 +113,23 @@ int vit_head_destroy(vit_head* h);
 int vit_op_conv3x3(const void* in, int ld_in, int c0, int cin, int batch, int gh, int gw, const void* w,
                    const float* bias, int n_out, float* out, void* stream);
 
+/* One ConvX unit of the head (diagram: Conv2d without bias, channel
+ * LayerNorm, SiLU; the "Projector output ConvX" adds the final channel
+ * LayerNorm) as one GEMM whose epilogue normalises the n_out channels of each
+ * pixel:
+ *   y[m, :] = SiLU(LN(conv(in)[m, :]; g, b, eps)), then y = LN(y; g2, b2, eps) if g2 != NULL,
+ * with LN the biased-variance LayerNorm over the channels (eps inside the
+ * square root, per-channel affine), written as bf16 to out[m * ld_out + c0_out + n].
+ *   ksize 3: the 3x3 / stride 1 / zero-padding 1 convolution of vit_op_conv3x3
+ *            (same in, ld_in, c0, cin and w layout);
+ *   ksize 1: in [batch * gh * gw, cin] bf16 rows (ld_in == cin, c0 == 0), w [n_out, cin].
+ *   n_out 128 or 256; g, b (and g2, b2) device fp32 [n_out], 16-byte aligned; eps > 0;
+ *   out device bf16, 8-byte aligned; ld_out and c0_out multiples of 4, c0_out + n_out <= ld_out.
+ * Enqueue only. */
+int vit_op_convx(const void* in, int ld_in, int c0, int cin, int batch, int gh, int gw, int ksize, const void* w,
+                 int n_out, const float* g, const float* b, const float* g2, const float* b2, float eps, void* out,
+                 int ld_out, int c0_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -170,3 +170,67 @@ def test_conv3x3_matches_oracle(batch, gh, gw, ld, c0, cin, n_out, bias):
     err = np.abs(got - ref)
     say(f"max err / bound = {(err / bound).max():.3f}")
     assert (err <= bound).all()
+
+
+def _ln_error(z, e_max, g, eps):
+    """Bound on the change of LN(z) (channels on axis 1, per-channel affine g)
+    when every input of a row moves by at most e_max of that row: the mean moves
+    by <= e_max and sigma by <= e_max, so each output moves by
+    <= |g| (2 e_max + |y| e_max) / sigma, y the normalised value; plus the fp32
+    arithmetic of the statistics (2^-20 relative, generous)."""
+    mu = z.mean(axis=1, keepdims=True)
+    sig = np.sqrt(((z - mu) ** 2).mean(axis=1, keepdims=True) + eps)
+    y = (z - mu) / sig
+    return np.abs(g) * ((2 + np.abs(y)) * e_max / sig + 2.0 ** -20 * (1 + np.abs(y)))
+
+
+@pytest.mark.parametrize("ksize,batch,gh,gw,ld,c0,cin,n_out,second,ld_out,c0_out", [
+    (3, 2, 37, 37, 640, 128, 128, 128, False, 640, 384),   # a Bottleneck conv: C2f slice in, C2f slice out
+    (3, 1, 5, 7, 128, 0, 128, 128, False, 128, 0),          # Bottleneck conv 1 into its temporary
+    (1, 2, 9, 11, 1536, 0, 1536, 256, False, 640, 0),       # the projector conv (4 taps concatenated)
+    (1, 1, 37, 37, 640, 0, 640, 256, True, 256, 0),         # the output ConvX with the final LayerNorm
+    (3, 3, 1, 1, 256, 0, 256, 256, False, 256, 0),          # every neighbour is padding
+])
+def test_convx_matches_oracle(ksize, batch, gh, gw, ld, c0, cin, n_out, second, ld_out, c0_out):
+    """vit_op_convx (conv, channel LayerNorm, SiLU, optional second LayerNorm, in
+    one GEMM epilogue) against the oracle's conv_ln_silu.  Inputs and weights are
+    bf16 values: the conv's only error is its fp32 sum (<= taps cin 2^-24
+    sum |w x| per output), which each LayerNorm passes on scaled by 1/sigma and
+    SiLU by at most 1.1; the bf16 output adds 2^-8 |y|."""
+    require_gpu()
+    say(f"convx k{ksize} batch {batch} grid {gh}x{gw} cin {cin} -> {n_out} second LN {second}")
+    rng = np.random.default_rng(gh * 31 + cin + n_out)
+    M = batch * gh * gw
+    x = _round_bf16(rng.standard_normal((M, ld)))
+    w4 = _round_bf16(rng.standard_normal((n_out, cin, ksize, ksize)) * 0.05)
+    g = (1 + 0.02 * rng.standard_normal(n_out)).astype(np.float32)
+    b = (0.02 * rng.standard_normal(n_out)).astype(np.float32)
+    g2 = (1 + 0.02 * rng.standard_normal(n_out)).astype(np.float32)
+    b2 = (0.02 * rng.standard_normal(n_out)).astype(np.float32)
+    wk = w4.permute(0, 2, 3, 1).reshape(n_out, ksize * ksize * cin).contiguous()
+    out = torch.zeros((M, ld_out), dtype=torch.bfloat16, device="cuda")
+    dev = lambda a: torch.from_numpy(a).cuda()
+    vit.vit_op_convx(x.cuda(), ld, c0, cin, batch, gh, gw, ksize, wk.cuda(), n_out, dev(g), dev(b),
+                     dev(g2) if second else None, dev(b2) if second else None, H.HEAD_LN_EPS, out, ld_out, c0_out)
+    got = host(out)
+    xs = x.double().numpy()[:, c0:c0 + cin].reshape(batch, gh, gw, cin).transpose(0, 3, 1, 2)
+    w64 = w4.double().numpy()
+    pad = ksize // 2
+    conv = np.stack([H.conv2d(xs[i], w64, None, pad) for i in range(batch)]).transpose(0, 2, 3, 1).reshape(M, n_out)
+    absconv = np.stack([H.conv2d(np.abs(xs[i]), np.abs(w64), None, pad)
+                        for i in range(batch)]).transpose(0, 2, 3, 1).reshape(M, n_out)
+    e1 = (ksize * ksize * cin * 2.0 ** -24 * absconv).max(axis=1, keepdims=True)
+    # the oracle's ConvX on channels-first images, back to rows
+    ref = np.stack([H.conv_ln_silu(xs[i], w64, g, b, pad) for i in range(batch)])
+    bound = 1.1 * _ln_error(conv, e1, g.astype(np.float64)[None], H.HEAD_LN_EPS)
+    if second:
+        ref = np.stack([H.channel_layer_norm(ref[i], g2, b2) for i in range(batch)])
+        s = np.stack([H.conv_ln_silu(xs[i], w64, g, b, pad) for i in range(batch)]).transpose(0, 2, 3, 1).reshape(M, n_out)
+        bound = _ln_error(s, bound.max(axis=1, keepdims=True), g2.astype(np.float64)[None], H.HEAD_LN_EPS)
+    ref = ref.transpose(0, 2, 3, 1).reshape(M, n_out)
+    bound = bound + 2.0 ** -8 * np.abs(ref) + 1e-30
+    err = np.abs(got[:, c0_out:c0_out + n_out] - ref)
+    say(f"max err / bound = {(err / bound).max():.3f}")
+    assert (err <= bound).all()
+    # columns outside [c0_out, c0_out + n_out) are not written
+    assert not got[:, :c0_out].any() and not got[:, c0_out + n_out:].any()

@@ -25,7 +25,7 @@ __all__ = [
     "vit_op_preprocess", "vit_op_linear_residual_ln",
     "Encoder", "EncoderGraph", "EPI_BIAS_BF16", "EPI_GELU_BF16", "EPI_RESIDUAL", "EPI_BIAS_F32",
     "HeadConfig", "HeadSizes", "head_config_preset", "head_config", "head_plan", "pack_head_params", "SemanticHead",
-    "vit_op_conv3x3", "vit_op_absmax", "vit_op_quantize_fp8", "vit_op_linear_fp8",
+    "vit_op_conv3x3", "vit_op_convx", "vit_op_absmax", "vit_op_quantize_fp8", "vit_op_linear_fp8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvit.so")
@@ -94,6 +94,7 @@ _SIGNATURES = {
     "vit_head_forward": (_I, [_P, _P, _I, _P, _P, _P]),
     "vit_head_destroy": (_I, [_P]),
     "vit_op_conv3x3": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
+    "vit_op_convx": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, ctypes.c_float, _P, _I, _I, _P]),
     "vit_op_absmax": (_I, [_P, _I, ctypes.c_size_t, _P, _P]),
     "vit_op_quantize_fp8": (_I, [_P, _I, ctypes.c_size_t, ctypes.c_float, _P, _P]),
     "vit_op_linear_fp8": (_I, [_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _I, _P]),
@@ -411,6 +412,13 @@ def pack_head_params(P: dict) -> np.ndarray:
 def vit_op_conv3x3(x, ld_in, c0, cin, batch, gh, gw, w, bias, n_out, out, stream=None):
     return _check("vit_op_conv3x3", lib().vit_op_conv3x3(_ptr(x), ld_in, c0, cin, batch, gh, gw, _ptr(w), _ptr(bias),
                                                          n_out, _ptr(out), _stream(stream)))
+
+
+def vit_op_convx(x, ld_in, c0, cin, batch, gh, gw, ksize, w, n_out, g, b, g2, b2, eps, out, ld_out, c0_out,
+                 stream=None):
+    return _check("vit_op_convx", lib().vit_op_convx(_ptr(x), ld_in, c0, cin, batch, gh, gw, ksize, _ptr(w), n_out,
+                                                     _ptr(g), _ptr(b), _ptr(g2), _ptr(b2), eps, _ptr(out), ld_out,
+                                                     c0_out, _stream(stream)))
 
 
 def vit_op_absmax(x, n, amax, stream=None):

@@ -346,4 +346,39 @@ int vit_op_conv3x3(const void* in, int ld_in, int c0, int cin, int batch, int gh
   return VIT_OK;
 }
 
+int vit_op_convx(const void* in, int ld_in, int c0, int cin, int batch, int gh, int gw, int ksize, const void* w,
+                 int n_out, const float* g, const float* b, const float* g2, const float* b2, float eps, void* out,
+                 int ld_out, int c0_out, void* stream) {
+  if (!in || !w || !g || !b || !out || (g2 && !b2)) return report_error(VIT_ERR_ARG, "NULL pointer");
+  if (ksize != 1 && ksize != 3) return report_error(VIT_ERR_ARG, "ksize must be 1 or 3");
+  if (!vit::chan_ln_fusable(n_out)) return report_error(VIT_ERR_UNSUPPORTED, "n_out must be 128 or 256");
+  if (cin < 64 || cin % 64 || c0 < 0 || c0 % 8 || ld_in % 8 || c0 + cin > ld_in)
+    return report_error(VIT_ERR_SHAPE, "cin a positive multiple of 64, c0 and ld_in multiples of 8, c0 + cin <= ld_in");
+  if (ksize == 1 && (c0 != 0 || ld_in != cin)) return report_error(VIT_ERR_SHAPE, "ksize 1 reads whole rows: c0 = 0, ld_in = cin");
+  if (batch < 1 || gh < 1 || gw < 1) return report_error(VIT_ERR_SHAPE, "batch and grid must be >= 1");
+  if (ld_out % 4 || c0_out < 0 || c0_out % 4 || c0_out + n_out > ld_out)
+    return report_error(VIT_ERR_SHAPE, "ld_out and c0_out multiples of 4, c0_out + n_out <= ld_out");
+  if (!(eps > 0.f)) return report_error(VIT_ERR_ARG, "eps must be positive");
+  if ((uintptr_t)in % 16 || (uintptr_t)out % 8 || ((uintptr_t)g | (uintptr_t)b | (uintptr_t)g2 | (uintptr_t)b2) % 16)
+    return report_error(VIT_ERR_ARG, "in and the vectors must be 16-byte aligned, out 8-byte aligned");
+  vit::EpiParams ep;
+  ep.kind = vit::EPI_CHAN_LN;
+  ep.ln_g = g;
+  ep.ln_b = b;
+  ep.eps = eps;
+  ep.silu = true;
+  ep.ln2_g = g2;
+  ep.ln2_b = b2;
+  ep.out = out;
+  ep.ldc = ld_out;
+  ep.c0 = c0_out;
+  const int M = batch * gh * gw;
+  hipError_t e = ksize == 3 ? vit::launch_gemm_conv3((const uint16_t*)in, ld_in, c0, cin, batch, gh, gw,
+                                                     (const uint16_t*)w, n_out, ep, (hipStream_t)stream)
+                            : vit::launch_gemm((const uint16_t*)in, (const uint16_t*)w, M, n_out, cin, ep,
+                                               (hipStream_t)stream);
+  HEAD_HIP(e, "convx");
+  return VIT_OK;
+}
+
 }  // extern "C"
