@@ -234,7 +234,10 @@ def _gate_heads(q, k, v, got):
     (1, 1, 1), (1, 5, 1), (2, 31, 2), (1, 64, 1), (1, 65, 3), (2, 127, 1),
     (1, 129, 2), (2, 201, 6), (1, 446, 6), (1, 1370, 2), (1, 4101, 2), (2, 2053, 3), (1, 1100, 1),
     # last query tile with 33..64 rows (two busy waves), one row, none
-    (1, 1064, 2), (2, 1153, 1), (1, 1024, 1), (1, 1280, 2)])
+    (1, 1064, 2), (2, 1153, 1), (1, 1024, 1), (1, 1280, 2),
+    # last query tile of 1..32 rows, whose waves split the keys: 32 rows, 33
+    # (not split), one key past a full tile, a last key tile of one key
+    (1, 32, 1), (1, 160, 2), (1, 161, 1), (3, 4097, 1), (1, 2113, 2)])
 def test_attention_matches_oracle(batch, tokens, heads):
     """N(0, 1) q and k: logits with a std of about 8 (log2 units), nearly one-hot rows."""
     say(f"attention N(0,1) batch={batch} tokens={tokens} heads={heads}")
@@ -256,16 +259,19 @@ def test_attention_workload_logits(batch, tokens, heads, logit_std):
     _gate_heads(*_run_attention(q, k, v))
 
 
-# the spike in the first key tile, or in the third (it then moves the running max mid-row)
-@pytest.mark.parametrize("spike", [3, 150])
-def test_attention_large_logits_stay_finite(spike):
+# the spike in the first key tile, or in the third (it then moves the running
+# max mid-row); at 150 tokens the last 22 queries sit in a key-split tile, and
+# the merge must drop the partial results of the waves that never saw the spike
+@pytest.mark.parametrize("tokens", [200, 150])
+@pytest.mark.parametrize("spike", [3, 140])
+def test_attention_large_logits_stay_finite(spike, tokens):
     # spike logit ~ 64 * 5000 * 8 * ln2 = 1.8e6, far beyond fp16's 65504; it wins every row
-    say(f"attention large logits, spike at key {spike}")
+    say(f"attention large logits, spike at key {spike}, tokens {tokens}")
     e = RNG.choice([-1.0, 1.0], size=64)
-    qr = 5000.0 * (e + 0.05 * RNG.standard_normal((1, 2, 200, 64)))
-    kr = RNG.standard_normal((1, 2, 200, 64))
+    qr = 5000.0 * (e + 0.05 * RNG.standard_normal((1, 2, tokens, 64)))
+    kr = RNG.standard_normal((1, 2, tokens, 64))
     kr[:, :, spike] = 8.0 * e
-    q, k, v, got = _run_attention(qr, kr, RNG.standard_normal((1, 2, 200, 64)))
+    q, k, v, got = _run_attention(qr, kr, RNG.standard_normal((1, 2, tokens, 64)))
     assert np.isfinite(got).all()
     for h in range(2):
         ref, smax = O.sdpa(q[0, h], k[0, h], v[0, h], math.log(2.0))
@@ -278,10 +284,11 @@ def test_attention_large_logits_stay_finite(spike):
 # Logits (log2 units) about `jump` higher in every key tile after the first, for
 # every query: 5 leaves each p <= 2^8 but lane sums of 32 p far above 2^8; 12
 # and 40 exceed the running max by more than 8 and move it on the second tile.
+@pytest.mark.parametrize("tokens", [300, 280])   # 280: the last 24 queries split the keys
 @pytest.mark.parametrize("jump", [5.0, 12.0, 40.0])
-def test_attention_rising_logits(jump):
-    say(f"attention rising logits, jump {jump}")
-    batch, tokens, heads = 1, 300, 2
+def test_attention_rising_logits(jump, tokens):
+    say(f"attention rising logits, jump {jump}, tokens {tokens}")
+    batch, heads = 1, 2
     e = RNG.choice([-1.0, 1.0], size=64)
     qr = e + 0.05 * RNG.standard_normal((batch, heads, tokens, 64))
     kr = 0.02 * RNG.standard_normal((batch, heads, tokens, 64))

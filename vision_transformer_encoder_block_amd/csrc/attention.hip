@@ -27,6 +27,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace vit {
 namespace {
@@ -51,6 +52,7 @@ struct AttnArgs {
   int N, H, nv;
   int qtiles;      // query tiles per (b, h); the grid is 1-D
   int B;
+  int split;       // 1: the last query tile holds 1..32 queries and its waves split the keys
 };
 
 // Workgroup id -> (query tile, head, image).  Workgroups are handed
@@ -90,8 +92,18 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
   const bf16_t* Kp = a.K + bh * N * 64;
   const bf16_t* Vp = a.Vt + bh * 64 * nv;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const int qrow = qt * 32 * NW + wave * 32 + lrow;
-  const bool idle = __builtin_amdgcn_readfirstlane(qt * 32 * NW + wave * 32) >= N;
+  // A last query tile with only 1..32 queries would leave one wave doing the
+  // whole key range while three idle: instead all NW waves take its 32 query
+  // rows, wave w the key half w % 2 of the tiles of parity w / 2, and they
+  // merge their partial results at the end.  Whether a tile splits depends on
+  // the sequence length only, so outputs do not depend on the batch.
+  static_assert(NW == 4, "the key split pairs 2 tile parities with 2 key halves");
+  const bool split = a.split && qt == a.qtiles - 1;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int kb_own = wave_u & 1, par = wave_u >> 1;
+  const int row0 = split ? qt * 32 * NW : qt * 32 * NW + wave * 32;
+  const int qrow = row0 + lrow;
+  const bool idle = __builtin_amdgcn_readfirstlane(row0) >= N;
 
   // rows past N read as zeros through the buffer range checks
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qp, (uint32_t)N * 128u);
@@ -107,7 +119,6 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
   // swizzled reads below look for it.  K rows past N come back as zeros; the
   // V^T columns of keys >= N (padding of unspecified content) are zeroed in
   // LDS once the ragged last tile has landed, so they meet p = 0 as zeros.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t kv_base = lds_addr(&KV[0][0][0]);
   uint32_t k_off[IPW], v_off[IPW];
 #pragma unroll
@@ -195,151 +206,223 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
   // arbiter otherwise favours the oldest waves; their workgroup finishes
   // first and leaves the CU with fewer waves to hide latency for the rest.
   __builtin_amdgcn_s_setprio(3);
-  // One key tile; the first is peeled off the loop (first == true: the tile
-  // max always sets m_run).
-  auto step = [&](int i, bool first) __attribute__((always_inline)) {
-    const int t = i;
-    if (4 * i >= nt && 4 * (i - 1) < nt) __builtin_amdgcn_s_setprio(2);
-    if (2 * i >= nt && 2 * (i - 1) < nt) __builtin_amdgcn_s_setprio(1);
-    if (4 * i >= 3 * nt && 4 * (i - 1) < 3 * nt) __builtin_amdgcn_s_setprio(0);
-    const int stage = i % S;
-    if (!idle) {  // wave-uniform: waves whose 32 query rows all lie past N only load and sync
-      const uint4* Ks = KV[stage][0];
-      const uint4* Vs = KV[stage][1];
+  // The work of one wave on one key tile: NKB 32-key halves starting at half
+  // kb0 (2 and 0 for a whole tile).  `first` marks the wave's first tile, where
+  // the tile max always sets m_run.
+  auto compute = [&](auto nkb_c, int t, int stage, int kb0, bool first) __attribute__((always_inline)) {
+    constexpr int NKB = decltype(nkb_c)::value;
+    const uint4* Ks = KV[stage][0];
+    const uint4* Vs = KV[stage][1];
 
-      // S^T for keys t*64 + kb*32 + [0, 32): element e <-> key 8*(e/4) + 4*lhalf + e%4.
-      // All K fragments are read before the MFMAs, and the V fragments right
-      // after them, so the LDS latency of both hides under MFMA and softmax work.
-      bf16x8 vf[2][4];
-      f32x16 s[2];
-      // s = S^T - m_run (the first tile runs with m_run = 0); keys past N
-      // (last tile only) get -inf.  The V fragments are read right after the
-      // K fragments on the first call.
-      auto logits = [&](bool read_v) {
-        bf16x8 kf[2][4];
+    // S^T for keys t*64 + kb*32 + [0, 32): element e <-> key 8*(e/4) + 4*lhalf + e%4.
+    // All K fragments are read before the MFMAs, and the V fragments right
+    // after them, so the LDS latency of both hides under MFMA and softmax work.
+    // vf[db][j] and pf[j] belong to the 16-key step 2 kb0 + j of the tile.
+    bf16x8 vf[2][2 * NKB];
+    f32x16 s[NKB];
+    // s = S^T - m_run (the first tile runs with m_run = 0); keys past N
+    // (last tile only) get -inf.  The V fragments are read right after the
+    // K fragments on the first call.
+    auto logits = [&](bool read_v) {
+      bf16x8 kf[NKB][4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int r = kb * 32 + lrow;
+      for (int kk = 0; kk < NKB; ++kk) {
+        const int r = (kb0 + kk) * 32 + lrow;
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) kf[kb][ks] = as_bf16x8(Ks[r * 8 + swz(r, ks * 2 + lhalf)]);
+        for (int ks = 0; ks < 4; ++ks) kf[kk][ks] = as_bf16x8(Ks[r * 8 + swz(r, ks * 2 + lhalf)]);
+      }
+      if (read_v) {
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const int r = db * 32 + lrow;
+#pragma unroll
+          for (int j = 0; j < 2 * NKB; ++j) vf[db][j] = as_bf16x8(Vs[r * 8 + swz(r, (2 * kb0 + j) * 2 + lhalf)]);
         }
-        if (read_v) {
+      }
 #pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            const int r = db * 32 + lrow;
+      for (int kk = 0; kk < NKB; ++kk) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) vf[db][ks] = as_bf16x8(Vs[r * 8 + swz(r, ks * 2 + lhalf)]);
+        for (int e = 0; e < 16; ++e) s[kk][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) s[kk] = mfma32x32x16(kf[kk][ks], qf[ks], s[kk]);
+        s[kk] = mfma32x32x16(ones, mneg, s[kk]);
+      }
+      if ((t + 1) * KT > N) {
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = t * KT + (kb0 + kk) * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
+            if (key >= N) s[kk][e] = -INFINITY;
           }
+      }
+    };
+    // probabilities p = 2^s, packed as the B operand of the key steps of
+    // P V; returns this lane's sum of its 16 NKB (a tree of pairwise adds)
+    bf16x8 pf[2 * NKB];
+    auto probs = [&]() {
+      float ps[2 * NKB];
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[kk][half * 8 + e]);
+          ps[kk * 2 + half] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+          uint4 u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                               pack_bf16x2(p[6], p[7]));
+          pf[kk * 2 + half] = as_bf16x8(u);
         }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) s[kb] = mfma32x32x16(kf[kb][ks], qf[ks], s[kb]);
-          s[kb] = mfma32x32x16(ones, mneg, s[kb]);
-        }
-        if ((t + 1) * KT > N) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int key = t * KT + kb * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
-              if (key >= N) s[kb][e] = -INFINITY;
-            }
-        }
-      };
-      // probabilities p = 2^s, packed as the B operand of the 4 key steps of
-      // P V; returns this lane's sum of its 32 (a tree of pairwise adds)
-      bf16x8 pf[4];
-      auto probs = [&]() {
-        float ps[4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[kb][half * 8 + e]);
-            ps[kb * 2 + half] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-            uint4 u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                                 pack_bf16x2(p[6], p[7]));
-            pf[kb * 2 + half] = as_bf16x8(u);
-          }
-        }
-        return (ps[0] + ps[1]) + (ps[2] + ps[3]);
-      };
-      // The tile max moves the reference max m_run (and rescales O and l)
-      // only when some query's tile max exceeds it by more than 8, so every
-      // p = 2^(s - m_run) <= 2^8; the first tile always sets it.  Numerator and
-      // denominator share m_run, so the final O / l is unchanged.
-      auto rescale_by_max = [&]() {
-        // tile max of this lane's 32 logits: maxima of groups of three
-        // (v_max3_f32), then of the group maxima (17 instructions, depth 4)
-        auto sv = [&](int f) { return s[f >> 4][f & 15]; };
+      }
+      if constexpr (NKB == 2) return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      else return ps[0] + ps[1];
+    };
+    // The tile max moves the reference max m_run (and rescales O and l)
+    // only when some query's tile max exceeds it by more than 8, so every
+    // p = 2^(s - m_run) <= 2^8; the first tile always sets it.  Numerator and
+    // denominator share m_run, so the final O / l is unchanged.
+    auto rescale_by_max = [&]() {
+      // tile max of this lane's logits: maxima of groups of three
+      // (v_max3_f32), then of the group maxima
+      auto sv = [&](int f) { return s[f >> 4][f & 15]; };
+      float mt;
+      if constexpr (NKB == 2) {
         float g3[11];
 #pragma unroll
         for (int i = 0; i < 10; ++i) g3[i] = fmaxf(fmaxf(sv(3 * i), sv(3 * i + 1)), sv(3 * i + 2));
         g3[10] = fmaxf(sv(30), sv(31));
         const float u0 = fmaxf(fmaxf(g3[0], g3[1]), g3[2]), u1 = fmaxf(fmaxf(g3[3], g3[4]), g3[5]);
         const float u2 = fmaxf(fmaxf(g3[6], g3[7]), g3[8]), u3 = fmaxf(g3[9], g3[10]);
-        float mt = fmaxf(fmaxf(fmaxf(u0, u1), u2), u3);
-        mt = half_swap_max(mt);
-        if (t == 0 || __builtin_amdgcn_ballot_w64(mt > 8.0f)) {
-          const float shift = t == 0 ? mt : fmaxf(mt, 0.f);
-          const float alpha = t == 0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
-          l_run *= alpha;
+        mt = fmaxf(fmaxf(fmaxf(u0, u1), u2), u3);
+      } else {
+        float g3[5];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            o[0][e] *= alpha;
-            o[1][e] *= alpha;
-          }
-          m_run += shift;
-          set_mneg(m_run);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[kb][e] -= shift;
-        }
-      };
-      // After the first tile, probabilities first, against the current m_run:
-      // the tile max is only needed when some p may exceed 2^8, and a lane's
-      // sum of its 32 p exceeding 2^8 is necessary for that (rare once m_run
-      // has settled).  Such a tile is recomputed from the K tile still in
-      // LDS, with the max-based rescale above; as the rescale decision is the
-      // max test either way, the results do not depend on which path ran.
-      logits(true);
-      float lsum = first ? 0.f : probs();
-      if (first || __builtin_amdgcn_ballot_w64(lsum > 256.0f)) {
-        // read K again rather than keep s or the K fragments in registers
-        // through the fast path (the clobber stops the compiler reusing them)
-        asm volatile("" ::: "memory");
-        logits(false);
-        rescale_by_max();
-        lsum = probs();
+        for (int i = 0; i < 5; ++i) g3[i] = fmaxf(fmaxf(sv(3 * i), sv(3 * i + 1)), sv(3 * i + 2));
+        mt = fmaxf(fmaxf(fmaxf(g3[0], g3[1]), g3[2]), fmaxf(fmaxf(g3[3], g3[4]), sv(15)));
       }
-      l_run += lsum;
-      // O^T[d, q] += V^T[d, keys] P^T[keys, q]; d = db*32 + row of the MFMA
+      mt = half_swap_max(mt);
+      if (first || __builtin_amdgcn_ballot_w64(mt > 8.0f)) {
+        const float shift = first ? mt : fmaxf(mt, 0.f);
+        const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-shift);
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+        for (int e = 0; e < 16; ++e) {
+          o[0][e] *= alpha;
+          o[1][e] *= alpha;
+        }
+        m_run += shift;
+        set_mneg(m_run);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) o[db] = mfma32x32x16(vf[db][ks], pf[ks], o[db]);
+        for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[kk][e] -= shift;
+      }
+    };
+    // After the first tile, probabilities first, against the current m_run:
+    // the tile max is only needed when some p may exceed 2^8, and a lane's
+    // sum of its p exceeding 2^8 is necessary for that (rare once m_run has
+    // settled).  Such a tile is recomputed from the K tile still in LDS, with
+    // the max-based rescale above; as the rescale decision is the max test
+    // either way, the results do not depend on which path ran.
+    logits(true);
+    float lsum = first ? 0.f : probs();
+    if (first || __builtin_amdgcn_ballot_w64(lsum > 256.0f)) {
+      // read K again rather than keep s or the K fragments in registers
+      // through the fast path (the clobber stops the compiler reusing them)
+      asm volatile("" ::: "memory");
+      logits(false);
+      rescale_by_max();
+      lsum = probs();
     }
+    l_run += lsum;
+    // O^T[d, q] += V^T[d, keys] P^T[keys, q]; d = db*32 + row of the MFMA
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int j = 0; j < 2 * NKB; ++j) o[db] = mfma32x32x16(vf[db][j], pf[j], o[db]);
+  };
+  // The K / V^T pipeline after the work on tile i: refill the stage read in
+  // the previous step (every wave passed the barrier after it), then wait for
+  // this wave's part of tile i + 1 and publish it; the barrier also retires
+  // this step's stage.
+  auto advance = [&](int i) __attribute__((always_inline)) {
     if (i + 1 < nt) {
-      // refill the stage read in the previous step (every wave passed the
-      // barrier after it), then wait for this wave's part of tile i + 1 and
-      // publish it; the barrier also retires this step's stage
-      if (i + S - 1 < nt) issue(t + S - 1, (i + S - 1) % S);
+      if (i + S - 1 < nt) issue(i + S - 1, (i + S - 1) % S);
       wait_tiles(min(S - 2, nt - 2 - i));
       barrier_keep_loads();
-      if ((t + 2) * KT > N) {
-        fix_last(t + 1, (i + 1) % S);
+      if ((i + 2) * KT > N) {
+        fix_last(i + 1, (i + 1) % S);
         __syncthreads();
       }
     }
   };
-  step(0, true);
-  for (int i = 1; i < nt; ++i) step(i, false);
+  auto priority = [&](int i) __attribute__((always_inline)) {
+    if (4 * i >= nt && 4 * (i - 1) < nt) __builtin_amdgcn_s_setprio(2);
+    if (2 * i >= nt && 2 * (i - 1) < nt) __builtin_amdgcn_s_setprio(1);
+    if (4 * i >= 3 * nt && 4 * (i - 1) < 3 * nt) __builtin_amdgcn_s_setprio(0);
+  };
+  // A split wave has keys at all only if its first key half starts before N
+  // (only the last tile is ragged).
+  const bool split_busy = split && par < nt && par * KT + kb_own * 32 < N;
+
+  if (split) {  // workgroup-uniform
+    for (int i = 0; i < nt; ++i) {
+      priority(i);
+      if ((i & 1) == par && i * KT + kb_own * 32 < N)
+        compute(std::integral_constant<int, 1>{}, i, i % S, kb_own, i == par);
+      advance(i);
+    }
+  } else {
+    // One key tile; the first is peeled off the loop (the tile max always
+    // sets m_run there).  Waves whose 32 query rows all lie past N
+    // (wave-uniform) only load and sync.
+    auto step = [&](int i, auto first_c) __attribute__((always_inline)) {
+      priority(i);
+      if (!idle) compute(std::integral_constant<int, 2>{}, i, i % S, 0, decltype(first_c)::value);
+      advance(i);
+    };
+    step(0, std::true_type{});
+    for (int i = 1; i < nt; ++i) step(i, std::false_type{});
+  }
+
+  if (split) {
+    // Merge the NW partial results (each relative to its own m_run) into wave
+    // 0 through LDS, in wave order: O = sum_w 2^(m_w - M) O_w, l likewise,
+    // M = max_w m_w over the waves that saw keys (wave 0 always does).
+    constexpr int F = 34;  // floats per lane: m, l, O^T (2 x 16)
+    static_assert(NW * F * 64 * 4 <= (int)sizeof(KV), "merge buffer");
+    float* mb = reinterpret_cast<float*>(&KV[0][0][0]);
+    __syncthreads();  // every wave is done reading the last K / V^T stage
+    float* mine = mb + wave * F * 64 + lane;
+    mine[0] = split_busy ? m_run : -INFINITY;
+    mine[64] = l_run;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mine[(2 + db * 16 + e) * 64] = o[db][e];
+    __syncthreads();
+    if (wave != 0) return;
+    float mw[NW], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      mw[w] = mb[w * F * 64 + lane];
+      M = fmaxf(M, mw[w]);
+    }
+    l_run = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float* src = mb + w * F * 64 + lane;
+      const float sc = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+      l_run += sc * src[64];
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] += sc * src[(2 + db * 16 + e) * 64];
+    }
+  }
 
   const float l = half_swap_sum(l_run);
   const float inv = 1.0f / l;
@@ -360,14 +443,16 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
 }  // namespace
 
 // Every query tile runs against the whole key range in one pass (a partly
-// filled last tile included: its idle waves only take part in the loads and
-// barriers), so no workspace is needed.
+// filled last tile included: with 33..127 queries its idle waves only take
+// part in the loads and barriers, with 1..32 its waves split the keys and
+// merge in LDS), so no workspace is needed.
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
                             int heads, int nv, uint16_t* o, hipStream_t s) {
   if (batch <= 0 || tokens <= 0 || heads <= 0 || nv < tokens || nv % 64 != 0) return hipErrorInvalidValue;
   if ((size_t)nv * 128 >= (1ull << 32)) return hipErrorInvalidValue;
   const int qtiles = (tokens + QT - 1) / QT;
-  AttnArgs a{q, k, vt, o, tokens, heads, nv, qtiles, batch};
+  const int rem = tokens % QT;
+  AttnArgs a{q, k, vt, o, tokens, heads, nv, qtiles, batch, rem > 0 && rem <= 32 ? 1 : 0};
   hipLaunchKernelGGL((attention_kernel<4>), dim3(qtiles * heads * batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
