@@ -322,6 +322,9 @@ PMC_OPS = {
     "vitl16_1024_b1": {"fc1": _has("EpiGeluBf16"), "attention": _has("attention_kernel"),
                        "layernorm": _has("layernorm_kernel"), "qkv": _has("EpiQKV"),
                        "out_proj|fc2": _has("EpiResidual", without=("EpiResidualLN",))},
+    # counter run of `bench.py --head-only --copy-calibration`: the Bottleneck
+    # 3x3 ConvX launches, six per head forward and the ones timed alone
+    "semantic_head_b8": {"convx": _has("EpiChanLN<128>", "AMapConv3")},
 }
 
 WORKLOADS = {"vits16_336_b32": ("vits16_336", 32), "vitl16_1024_b1": ("vitl16_1024", 1)}
@@ -507,7 +510,7 @@ def bench_head(steps=30, warmup=5):
                          "(Bottleneck ConvX: 3x3 conv + channel LN + SiLU, M = 10952, N = 128, K = 1152)",
                          "achieved": conv_tf,
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": conv_tf / PEAK_BF16_TFLOPS,
-                         "avg_launch_us": ms_conv * 1e3, "traffic": None}}
+                         "avg_launch_us": ms_conv * 1e3, "traffic": traffic_for("semantic_head_b8", "convx")}}
 
 
 def bench_fp8(steps=30, warmup=5):
@@ -597,8 +600,8 @@ def main():
     ap.add_argument("--gemm-vs-library", action="store_true",
                     help="run only the comparison of the library's GEMM with hipBLASLt (through torch) and print it")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "WORKLOAD"),
-                    help="host only: turn two rocprofv3 --pmc CSVs of --breakdown-only WORKLOAD into "
-                         "profiles/hbm_traffic.json")
+                    help="host only: turn two rocprofv3 --pmc CSVs of --breakdown-only WORKLOAD (or of "
+                         "--head-only for semantic_head_b8) into profiles/hbm_traffic.json")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("CSV", "WORKLOAD"),
                     help="host only: matrix-core utilisation table from a rocprofv3 --pmc CSV of "
                          "--breakdown-only WORKLOAD")
@@ -618,6 +621,8 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
 
+    if args.copy_calibration:
+        copy_calibration()
     if args.head_only:
         print(json.dumps(bench_head(args.steps, args.warmup)), flush=True)
         return
@@ -627,8 +632,6 @@ def main():
     if args.gemm_vs_library:
         print(json.dumps(gemm_vs_library(args.steps, args.warmup)), flush=True)
         return
-    if args.copy_calibration:
-        copy_calibration()
     if args.breakdown_only:
         name, batch = WORKLOADS[args.breakdown_only]
         import synth

@@ -58,8 +58,10 @@ def check_labels(got, ref):
 
 
 @pytest.mark.parametrize("batch,gh,gw,out", [(2, 6, 5, (84, 70)), (3, 13, 11, (100, 90)), (1, 1, 1, (7, 5)),
-                                             (1, 20, 17, (42, 30)),    # GroupNorm: 2 pixels per thread
-                                             (1, 50, 45, (33, 61))])   # GroupNorm: > 2048 pixels (loop)
+                                             (1, 20, 17, (42, 30)),    # GroupNorm: 1 float4 per thread
+                                             (1, 50, 45, (33, 61)),    # GroupNorm: 5 float4 per thread
+                                             (1, 64, 128, (70, 60)),   # GroupNorm: 8192 pixels, 16 per thread
+                                             (1, 96, 90, (50, 40))])   # GroupNorm: > 8192 pixels (loop)
 def test_head_matches_oracle_small_grids(batch, gh, gw, out):
     require_gpu()
     cfg = synth.preset("vits14_518")

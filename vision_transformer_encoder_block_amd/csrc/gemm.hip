@@ -210,6 +210,27 @@ struct EpiBiasF32 {
   }
 };
 
+// fp32 output in groups of 8 columns (the GroupNorm groups of the head):
+// column n of row m at out[(n / 8) * gstride + 8 m + n % 8], so one group's
+// values over all rows form one contiguous run.  N is a multiple of 8 and
+// out, bias are 16-byte aligned, so every lane's 4 columns are one store.
+struct EpiBiasF32G8 {
+  const float* bias;
+  float* out;
+  size_t gstride;
+  using Col = float4;
+  using Row = NoRow;
+  __device__ Col col4(int n, int nvalid) const { return bias ? load4(bias + n, nvalid, true) : make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ Row pre(int, int, int) const { return {}; }
+  __device__ void finish4(float (&v)[4], const Col& b, const Row&) const {
+    v[0] += b.x, v[1] += b.y, v[2] += b.z, v[3] += b.w;
+  }
+  __device__ void write4(int m, int n, const float (&v)[4], int) const {
+    *reinterpret_cast<float4*>(out + (size_t)(n >> 3) * gstride + (size_t)m * 8 + (n & 7)) =
+        make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
 // fp8 products: acc is the fp32 sum of products of E4M3 values; `scale`
 // (the product of the two operands' dequantisation scales) restores the units:
 // out = acc * scale + bias, in fp32 or bf16.
@@ -1038,8 +1059,12 @@ template <int C, class AM>
 hipError_t run_chan_ln(const bf16_t* A, const bf16_t* W, int M, int K, const EpiParams& ep, hipStream_t s, AM am) {
   const EpiChanLN<C> e{ep.bias, ep.ln_g, ep.ln_b, ep.eps, ep.silu, ep.ln2_g, ep.ln2_b, (bf16_t*)ep.out, ep.ldc, ep.c0};
   // 32-row tiles (about 1.3 workgroups per CU at 8 x 37 x 37 pixels) measured
-  // faster than 64-row ones for every conv of the head (b8: 288 vs 298 us)
-  return run<Cfg<32, C, 64, 1, 4, 2>>(A, W, M, C, K, e, s, am);
+  // faster than 64-row ones for every conv of the head (b8: 288 vs 298 us).
+  // These short loops (18-24 k-steps) wait on their loads: a third stage for
+  // the 128-channel tiles (60 KB, still two workgroups per CU) took the b8
+  // head from 298 to 268 us; the 256-channel tiles stay at two (a third, 108
+  // KB, leaves one workgroup per CU: 281 us).
+  return run<Cfg<32, C, 64, 1, 4, (C == 128 ? 3 : 2)>>(A, W, M, C, K, e, s, am);
 }
 
 // Checks shared by the linear and convolution forms of EPI_CHAN_LN.
@@ -1164,6 +1189,14 @@ hipError_t launch_gemm_conv3(const uint16_t* in, int ld_in, int c0, int C, int b
     }
     case EPI_CHAN_LN:
       return dispatch_chan_ln(in, W, (int)M, N, (int)K, ep, s, am);
+    case EPI_BIAS_F32_G8:
+      if (N % 8 || !ep.out || !al(ep.out, 16) || !al(ep.bias, 16) || ep.ldc < 0 || (size_t)ep.ldc < 8 * M)
+        return hipErrorInvalidValue;
+      // 64 x 128 tiles with a third stage (72 KB, two workgroups per CU): the
+      // head's smoothing conv (K = 2304, 344 tiles at b8) waits on its loads;
+      // the third stage took the b8 head from 258.6 to 251.1 us
+      return run<Cfg<64, 128, 64, 2, 2, 3>>(in, W, (int)M, N, (int)K,
+                                            EpiBiasF32G8{ep.bias, (float*)ep.out, (size_t)ep.ldc}, s, am);
     default:
       return hipErrorInvalidValue;
   }

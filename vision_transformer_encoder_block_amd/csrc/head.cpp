@@ -261,10 +261,6 @@ int vit_head_forward(vit_head* h, const float* d_taps, int batch, float* d_logit
   auto gemm_f32 = [&](const uint16_t* a, size_t wo, int N, int K, const float* bias, float* outp) {
     return vit::launch_gemm(a, bf(w, wo), M, N, K, f32_out(bias, outp, N), st);
   };
-  // 3x3 / pad 1 conv of channels c0 .. c0 + Cin of a channels-last buffer (implicit GEMM)
-  auto conv3_f32 = [&](const uint16_t* in, int ld, int c0, int Cin, size_t wo, int N, const float* bias, float* outp) {
-    return vit::launch_gemm_conv3(in, ld, c0, Cin, batch, c.grid_h, c.grid_w, bf(w, wo), N, f32_out(bias, outp, N), st);
-  };
 
   // ConvX blocks (conv, channel LayerNorm, SiLU; the output block adds the
   // final LayerNorm): the GEMM epilogue normalises whole pixel rows and writes
@@ -311,8 +307,16 @@ int vit_head_forward(vit_head* h, const float* d_taps, int batch, float* d_logit
     ep.ldc = W;
     HEAD_HIP(vit::launch_gemm(p4, bf(w, pl.lat_w), M, W, W, ep, st), "lateral conv");
   }
-  HEAD_HIP(conv3_f32(lat, W, 0, W, pl.sm_w, W, f32(w, pl.sm_b), f), "smoothing conv");
-  HEAD_HIP(vit::launch_groupnorm_gelu(f, batch, pl.P, W, c.groups, f32(w, pl.gn_g), f32(w, pl.gn_b), c.gn_eps, g, st),
+  {
+    // written group-major (8 channels x all pixels per group), the layout the
+    // GroupNorm reads as one contiguous run per (group, image)
+    vit::EpiParams ep = f32_out(f32(w, pl.sm_b), f, 8 * M);
+    ep.kind = vit::EPI_BIAS_F32_G8;
+    HEAD_HIP(vit::launch_gemm_conv3(lat, W, 0, W, batch, c.grid_h, c.grid_w, bf(w, pl.sm_w), W, ep, st),
+             "smoothing conv");
+  }
+  HEAD_HIP(vit::launch_groupnorm_gelu(f, (size_t)8 * M, batch, pl.P, W, c.groups, f32(w, pl.gn_g), f32(w, pl.gn_b),
+                                      c.gn_eps, g, st),
            "GroupNorm + GELU");
   HEAD_HIP(gemm_f32(g, pl.pred_w, C, W, f32(w, pl.pred_b), grid), "predict conv");
   HEAD_HIP(vit::launch_resize_nchw(grid, C, C, batch, c.grid_h, c.grid_w, d_logits, c.out_h, c.out_w, st),

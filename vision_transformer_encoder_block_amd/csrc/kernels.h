@@ -18,6 +18,8 @@ enum EpiKind {
   EPI_RESIDUAL_LN = 6, // EPI_RESIDUAL, then h = LayerNorm(out row) in bf16 (N = 384 only)
   EPI_CHAN_LN = 7,     // channel LayerNorm of the row (acc + bias), SiLU, optional second
                        // LayerNorm; bf16 into out + m * ldc + c0 (N = 128 or 256)
+  EPI_BIAS_F32_G8 = 8, // out_f32 in column groups of 8: out[(n/8) * ldc + 8 m + n % 8] = acc + bias[n]
+                       // (ldc >= 8 M; N a multiple of 8; 3x3 convolutions only)
 };
 
 struct EpiParams {
@@ -127,9 +129,11 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
 // ---- semantic head (channels-last activations, one row per pixel)
 // Taps [batch, ntaps, D, P] fp32 (channel-first) -> out bf16 [batch * P, ntaps * D].
 hipError_t launch_taps_cl(const float* taps, int batch, int ntaps, int D, int P, uint16_t* out, hipStream_t s);
-// GroupNorm (C = 8 * groups) of x [batch * P, C] fp32 per image, affine, exact GELU -> bf16 [batch * P, C].
-hipError_t launch_groupnorm_gelu(const float* x, int batch, int P, int C, int groups, const float* g, const float* b,
-                                 float eps, uint16_t* out, hipStream_t s);
+// GroupNorm (C = 8 * groups) per image, affine, exact GELU -> bf16 [batch * P, C].  x is
+// group-major fp32 (EPI_BIAS_F32_G8's layout): group j's 8 channels of pixel row m at
+// x + j * gstride + 8 m (gstride >= 8 * batch * P).
+hipError_t launch_groupnorm_gelu(const float* x, size_t gstride, int batch, int P, int C, int groups, const float* g,
+                                 const float* b, float eps, uint16_t* out, hipStream_t s);
 // Bilinear resize (half-pixel centres) of class-minor in [batch * gh * gw, ldi]
 // to out [batch, classes, H, W] fp32.
 hipError_t launch_resize_nchw(const float* in, int ldi, int classes, int batch, int gh, int gw, float* out, int H,
