@@ -3,9 +3,12 @@
 Codes are integers decided from the same float32 product on both sides, so they
 must agree bit for bit.
 
-The GEMM multiplies E4M3 values, whose products are exact; measured on the
-gfx950 matrix core, a single product and any sum whose products lie within a
-few octaves are exact as well.  Each instruction adds its 64 products with a
+The GEMM multiplies E4M3 values, whose products are exact.  With codes of
+magnitude [1, 4) every 64-product group sums exactly in 16 bits, so the only
+rounding is the fp32 accumulation across groups: those cases take a bound
+derived from that alone and must match a model of the accumulation bit for bit
+(test_linear_fp8_exact_groups).  Measured on the gfx950 matrix core, a single
+product and any sum whose products lie within a few octaves are exact as well.  Each instruction adds its 64 products with a
 limited number of bits below the largest of them: when one group mixes
 magnitudes far apart, its error measured up to 2^-11.1 of its largest product
 (random codes over the whole E4M3 range).  The bound is therefore, per output,
@@ -119,6 +122,63 @@ def test_linear_fp8_encoder_shapes_sampled(M, N, K):
     qa, qw = random_codes(rng, (M, K)), random_codes(rng, (N, K))
     rows = np.unique(np.concatenate([[0, 1, 127, 128, M - 1], rng.integers(0, M, 60)]))
     check_linear(qa, qw, 1.0 / 64, rng.standard_normal(N).astype(np.float32), True, rows)
+
+
+def narrow_codes(rng, shape):
+    """E4M3 codes of magnitude in [1, 4) (exponent fields 7 and 8, any mantissa), both signs."""
+    c = rng.integers(0x38, 0x48, shape).astype(np.uint8)
+    return c | (rng.integers(0, 2, shape).astype(np.uint8) << 7)
+
+
+def group_accumulation_model(qa, qw, scale, bias):
+    """The kernel's arithmetic when every 64-product group sums exactly: E4M3
+    values of magnitude [1, 4) have 4 significant bits, so their products have
+    at most 8 and lie in [1, 16); a group of 64 then sums to less than 2^10
+    with its lowest bit at 2^-6, 16 bits that any adder of fp32 width or more
+    holds exactly.  The instructions add their group sums to the fp32
+    accumulator in k order, one rounding (to nearest even) per group; the
+    epilogue is one fp32 fma (acc * scale + bias)."""
+    A, W = Q.dequantize_e4m3(qa, 1.0), Q.dequantize_e4m3(qw, 1.0)
+    K = A.shape[1]
+    acc = np.zeros((A.shape[0], W.shape[0]), np.float32)
+    for g in range(0, K, 64):
+        acc = (acc.astype(np.float64) + A[:, g:g + 64] @ W[:, g:g + 64].T).astype(np.float32)
+    y = acc.astype(np.float64) * np.float64(np.float32(scale))
+    if bias is not None:
+        y = y + bias.astype(np.float64)
+    return y.astype(np.float32), np.abs(A) @ np.abs(W).T
+
+
+@pytest.mark.parametrize("M,N,K,out_f32", [(300, 200, 1536, True), (257, 130, 4096, True), (300, 200, 1536, False)])
+def test_linear_fp8_exact_groups(M, N, K, out_f32):
+    """Codes whose group sums are exact: the only error left is the fp32
+    accumulation across the K / 64 groups, a bound that follows from the
+    arithmetic alone, |err| <= scale (K / 64 - 1) 2^-24 sum |a w| + 2^-24 |y|
+    (+ 2^-8 |y| for bf16 out).  Beyond the bound, the kernel must reproduce the
+    model of that accumulation above bit for bit (also after the bf16 rounding):
+    a wrong group order, a dropped or doubled group, a wrong scale or an extra
+    rounding step all break it."""
+    require_gpu()
+    rng = np.random.default_rng(M + N + K)
+    qa, qw = narrow_codes(rng, (M, K)), narrow_codes(rng, (N, K))
+    bias = rng.standard_normal(N).astype(np.float32)
+    scale = 0.01
+    out = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.bfloat16, device="cuda")
+    vit.vit_op_linear_fp8(codes_dev(qa), codes_dev(qw), M, N, K, scale, torch.from_numpy(bias).cuda(), out)
+    got = host(out).astype(np.float64)
+    model, absp = group_accumulation_model(qa, qw, scale, bias)
+    ref = Q.linear_fp8(qa, scale, qw, 1.0, bias)
+    bound = np.float32(scale) * (K // 64 - 1) * 2.0 ** -24 * absp + 2.0 ** -24 * np.abs(ref) \
+        + (0 if out_f32 else 2.0 ** -8 * np.abs(ref)) + 1e-30
+    err = np.abs(got - ref)
+    model64 = model.astype(np.float64)
+    if not out_f32:
+        model64 = host(torch.from_numpy(model).to(torch.bfloat16)).astype(np.float64)
+    off = np.abs(got - model64) / np.maximum(np.spacing(np.abs(model).astype(np.float32)).astype(np.float64), 1e-45)
+    say(f"fp8 exact groups {M}x{N}x{K} {'fp32' if out_f32 else 'bf16'}: max err / bound {(err / bound).max():.3f}, "
+        f"{(got == model64).mean():.4f} of outputs equal to the accumulation model, max {off.max():.1f} fp32 units off")
+    assert (err <= bound).all()
+    assert off.max() == 0.0
 
 
 def test_quantized_linear_end_to_end():
