@@ -111,6 +111,109 @@ def test_linear(M, N, K, epi):
     assert not bad.any(), (np.argwhere(bad)[:5], np.abs(got - ref).max())
 
 
+def _unit_bf16(shape):
+    """bf16 values of magnitude [1, 2): random sign and 7-bit mantissa."""
+    m = RNG.integers(0, 128, shape)
+    return (1.0 + m / 128.0) * np.where(RNG.integers(0, 2, shape) == 1, -1.0, 1.0)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("epi", [vit.EPI_BIAS_F32, vit.EPI_BIAS_BF16])
+def test_linear_exact_groups(M, N, K, epi):
+    """The GEMM's rounding, reproduced bit for bit.  With operands of magnitude
+    [1, 2) (8 significant bits) each product has at most 16 and lies in [1, 4),
+    so the 16 products one 32 x 32 x 16 MFMA adds sum to less than 2^6 with
+    their lowest bit at 2^-14: 20 bits, exact in any adder of fp32 width.  The
+    only roundings left are the fp32 accumulator taking each 16-wide k group in
+    k order (to nearest even) and the epilogue's bias add, then the bf16 store.
+    Every tile shape (64 x 64 .. 256 x 256, the extra rows of row tile 0,
+    ragged edges) must give exactly that; a wrong k order, a dropped or doubled
+    k group, or an extra rounding breaks it."""
+    say(f"linear exact groups M={M} N={N} K={K} epi={epi}")
+    a = _unit_bf16((M, K))
+    w = _unit_bf16((N, K))
+    a_d, a_r = bf16_dev(a)
+    w_d, w_r = bf16_dev(w)
+    assert np.array_equal(a_r, a) and np.array_equal(w_r, w)
+    bias = (0.1 * RNG.standard_normal(N)).astype(np.float32)
+    acc = np.zeros((M, N), np.float32)
+    for g in range(0, K, 16):
+        acc = (acc.astype(np.float64) + a[:, g:g + 16] @ w[:, g:g + 16].T).astype(np.float32)
+    model = (acc.astype(np.float64) + bias.astype(np.float64)).astype(np.float32)
+    if epi == vit.EPI_BIAS_F32:
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    else:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        model = host(torch.from_numpy(model).to(torch.bfloat16))
+    vit.vit_op_linear(a_d, w_d, f32_dev(bias), M, N, K, epi, None, out)
+    got = host(out)
+    diff = got != model
+    say(f"  {diff.mean():.6f} of outputs differ from the accumulation model")
+    assert not diff.any(), (np.argwhere(diff)[:5], np.abs(got - model).max())
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 150, 384), (1000, 1536, 384), (4101, 1024, 128), (4100, 1024, 1024),
+                                   (1285, 16384, 256)])
+def test_linear_residual_exact_groups(M, N, K):
+    """The residual epilogue x += ls * (acc + b) bit for bit, with the operands
+    of test_linear_exact_groups and LayerScale values that are powers of two
+    (so ls * t is exact and a fused or a separate multiply-add give the same
+    bits): one rounding for acc + b, one for the update."""
+    say(f"linear residual exact groups M={M} N={N} K={K}")
+    a, w = _unit_bf16((M, K)), _unit_bf16((N, K))
+    a_d, _ = bf16_dev(a)
+    w_d, _ = bf16_dev(w)
+    bias = (0.1 * RNG.standard_normal(N)).astype(np.float32)
+    ls = (2.0 ** RNG.integers(-17, 2, N) * np.where(RNG.integers(0, 2, N) == 1, -1.0, 1.0)).astype(np.float32)
+    r0 = RNG.standard_normal((M, N)).astype(np.float32)
+    acc = np.zeros((M, N), np.float32)
+    for g in range(0, K, 16):
+        acc = (acc.astype(np.float64) + a[:, g:g + 16] @ w[:, g:g + 16].T).astype(np.float32)
+    t = (acc.astype(np.float64) + bias).astype(np.float32)
+    model = (r0.astype(np.float64) + ls.astype(np.float64) * t).astype(np.float32)
+    x = f32_dev(r0)
+    vit.vit_op_linear(a_d, w_d, f32_dev(bias), M, N, K, vit.EPI_RESIDUAL, f32_dev(ls), x)
+    got = host(x)
+    diff = got != model
+    say(f"  {diff.mean():.6f} of outputs differ from the model")
+    assert not diff.any(), (np.argwhere(diff)[:5], np.abs(got - model).max())
+
+
+@pytest.mark.parametrize("batch,tokens,heads", [(2, 201, 6), (1, 446, 6), (3, 70, 2), (1, 4101, 16)])
+def test_qkv_exact_groups(batch, tokens, heads):
+    """The fused Q/K/V projection bit for bit on operands whose k groups sum
+    exactly (see test_linear_exact_groups): q = bf16((acc + b) * log2(e)/8) with
+    two fp32 roundings, k = bf16(acc + b), and v = bf16(acc + b) at its permuted
+    v^T column; 4101 x 16 heads takes the 256 x 256 tiles."""
+    say(f"qkv exact groups batch={batch} tokens={tokens} heads={heads}")
+    D = 64 * heads
+    M = batch * tokens
+    h, w = _unit_bf16((M, D)), _unit_bf16((3 * D, D))
+    h_d, _ = bf16_dev(h)
+    w_d, _ = bf16_dev(w)
+    bias = (0.1 * RNG.standard_normal(3 * D)).astype(np.float32)
+    nv = (tokens + 63) // 64 * 64
+    q = torch.empty((batch, heads, tokens, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty_like(q)
+    vt = torch.zeros((batch, heads, 64, nv), dtype=torch.bfloat16, device="cuda")
+    vit.vit_op_qkv(h_d, w_d, f32_dev(bias), batch, tokens, heads, q, k, vt)
+    acc = np.zeros((M, 3 * D), np.float32)
+    for g in range(0, D, 16):
+        acc = (acc.astype(np.float64) + h[:, g:g + 16] @ w[:, g:g + 16].T).astype(np.float32)
+    t = (acc.astype(np.float64) + bias).astype(np.float32)
+    c = np.float32(math.log2(math.e) / 8.0)
+    qs = (t[:, :D].astype(np.float64) * np.float64(c)).astype(np.float32)
+    to_bf = lambda x: host(torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16))
+    ref_q = to_bf(qs).reshape(batch, tokens, heads, 64).transpose(0, 2, 1, 3)
+    ref_k = to_bf(t[:, D:2 * D]).reshape(batch, tokens, heads, 64).transpose(0, 2, 1, 3)
+    ref_v = to_bf(t[:, 2 * D:]).reshape(batch, tokens, heads, 64).transpose(0, 2, 3, 1)   # [b, h, d, t]
+    gq, gk, gv = host(q), host(k), host(vt)
+    cols = vt_position(np.arange(tokens))
+    assert np.array_equal(gq, ref_q)
+    assert np.array_equal(gk, ref_k)
+    assert np.array_equal(gv[:, :, :, cols], ref_v)
+
+
 def test_gelu_epilogue_wide_range():
     """GELU over pre-activations spanning [-8, 8] (every step of 1/16, exact in
     bf16), so the clamped ends of the epilogue's Phi lookup are exercised:
