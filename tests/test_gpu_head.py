@@ -174,6 +174,42 @@ def test_conv3x3_matches_oracle(batch, gh, gw, ld, c0, cin, n_out, bias):
     assert (err <= bound).all()
 
 
+@pytest.mark.parametrize("batch,gh,gw,ld,c0,cin,n_out,bias", [
+    (2, 5, 7, 640, 128, 128, 128, False), (1, 37, 37, 256, 0, 256, 256, True), (3, 1, 1, 128, 0, 128, 64, True),
+    (2, 9, 4, 192, 64, 64, 19, True)])
+def test_conv3x3_exact_groups(batch, gh, gw, ld, c0, cin, n_out, bias):
+    """The implicit-GEMM 3x3 conv bit for bit.  Inputs and weights of magnitude
+    [1, 2) (8 significant bits) make the 16 products of one MFMA sum exactly
+    (20 bits, as in the encoder's GEMM test), and the zero padding adds exact
+    zeros, so the result must equal the fp32 accumulation of the 16-wide k
+    groups of the (ky, kx, c) ordered columns in k order, then the bias add: a
+    wrong neighbour, a tap read from the wrong row or a missing zero breaks it."""
+    require_gpu()
+    say(f"conv3x3 exact groups batch {batch} grid {gh}x{gw} ld {ld} c0 {c0} cin {cin} -> {n_out}")
+    rng = np.random.default_rng(gh * 101 + cin + n_out)
+    unit = lambda shape: (1.0 + rng.integers(0, 128, shape) / 128.0) * np.where(rng.integers(0, 2, shape) == 1, -1, 1)
+    M = batch * gh * gw
+    xv, wv = unit((M, ld)), unit((n_out, 9 * cin))
+    x, wk = _round_bf16(xv), _round_bf16(wv)
+    assert np.array_equal(x.double().numpy(), xv) and np.array_equal(wk.double().numpy(), wv)
+    b = rng.standard_normal(n_out).astype(np.float32) if bias else np.zeros(n_out, np.float32)
+    out = torch.empty((M, n_out), device="cuda")
+    vit.vit_op_conv3x3(x.cuda(), ld, c0, cin, batch, gh, gw, wk.cuda(), torch.from_numpy(b).cuda() if bias else None,
+                       n_out, out)
+    got = host(out)
+    img = xv[:, c0:c0 + cin].reshape(batch, gh, gw, cin)
+    pad = np.zeros((batch, gh + 2, gw + 2, cin))
+    pad[:, 1:-1, 1:-1] = img
+    cols = np.concatenate([pad[:, ky:ky + gh, kx:kx + gw].reshape(M, cin) for ky in range(3) for kx in range(3)], axis=1)
+    acc = np.zeros((M, n_out), np.float32)
+    for g in range(0, 9 * cin, 16):
+        acc = (acc.astype(np.float64) + cols[:, g:g + 16] @ wv[:, g:g + 16].T).astype(np.float32)
+    model = (acc.astype(np.float64) + b.astype(np.float64)).astype(np.float32)
+    diff = got != model
+    say(f"  {diff.mean():.6f} of outputs differ from the accumulation model")
+    assert not diff.any(), (np.argwhere(diff)[:5], np.abs(got - model).max())
+
+
 def _ln_error(z, e_max, g, eps):
     """Bound on the change of LN(z) (channels on axis 1, per-channel affine g)
     when every input of a row moves by at most e_max of that row: the mean moves
