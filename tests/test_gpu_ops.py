@@ -362,6 +362,51 @@ def test_attention_workload_logits(batch, tokens, heads, logit_std):
     _gate_heads(*_run_attention(q, k, v))
 
 
+@pytest.mark.parametrize("batch,tokens,heads", [(1, 1, 1), (1, 5, 2), (2, 31, 2), (1, 64, 1), (1, 65, 3), (2, 129, 2),
+                                                (2, 201, 6), (2, 446, 6), (1, 1370, 2), (1, 2053, 3), (1, 4101, 16),
+                                                (1, 4097, 1), (1, 160, 2), (1, 161, 1)])
+def test_attention_exact_powers_of_two(batch, tokens, heads):
+    """The kernel bit for bit on inputs where every step is exact.  Each query
+    is a unit vector e_r (r one of 8 channels), each key holds logits in
+    {0, -1, -2, -3} on those channels, and keys 0, 32, 64 and 96 hold 0 on all
+    of them, so every wave's first key block (whole tiles, or the 32-key halves
+    of a key-split last query tile) contains the row maximum 0 and no rescale
+    happens.  Then p = 2^s exactly, the values are bf16 of magnitude [1, 2)
+    (7-bit mantissas), every partial sum of p v and of p is a multiple of 2^-10
+    below 2^14 (24 bits) and so exact in fp32 in any order, and the output is
+    bf16(fl32(O * fl32(1 / l))) with O = sum p v and l = sum p exact.  A wrong
+    mask, key order, value column, query row or head, a dropped or doubled key
+    tile, or a merge that weights the key-split partials wrongly breaks it."""
+    say(f"attention exact powers of two batch={batch} tokens={tokens} heads={heads}")
+    r = RNG.integers(0, 8, (batch, heads, tokens))
+    q = np.zeros((batch, heads, tokens, 64))
+    np.put_along_axis(q, r[..., None], 1.0, axis=3)
+    k = np.zeros((batch, heads, tokens, 64))
+    k[..., :8] = -RNG.integers(0, 4, (batch, heads, tokens, 8))
+    for anchor in (0, 32, 64, 96):
+        if anchor < tokens:
+            k[:, :, anchor, :8] = 0.0
+    v = (1.0 + RNG.integers(0, 128, (batch, heads, tokens, 64)) / 128.0) * \
+        np.where(RNG.integers(0, 2, (batch, heads, tokens, 64)) == 1, -1.0, 1.0)
+    qr, kr, vr, got = _run_attention(q, k, v)
+    assert np.array_equal(qr, q) and np.array_equal(kr, k) and np.array_equal(vr, v)
+    s = np.einsum("bhqc,bhkc->bhqk", q, k)                 # integers in [-3, 0]
+    p = np.exp2(s)                                          # exact powers of two
+    num = np.einsum("bhqk,bhkd->bhqd", p, v)                # exact (checked below)
+    l = p.sum(axis=3)
+    assert np.array_equal(num, np.round(num * 1024) / 1024)
+    assert np.einsum("bhqk,bhkd->bhqd", p, np.abs(v)).max() < 2 ** 14
+    inv = np.float32(1.0) / l.astype(np.float32)
+    o32 = num.astype(np.float32) * inv[..., None]
+    model = host(torch.from_numpy(np.ascontiguousarray(o32.transpose(0, 2, 1, 3))).to(torch.bfloat16))
+    diff = got != model
+    say(f"  {diff.mean():.6f} of outputs differ from the exact model")
+    assert not diff.any(), (np.argwhere(diff)[:5], np.abs(got - model).max())
+    # the model is the oracle's softmax attention up to the output rounding
+    ref, _ = O.sdpa(q[0, 0], k[0, 0], v[0, 0], math.log(2.0))
+    assert np.all(np.abs(model[0, :, 0] - ref) <= 2 ** -8 * np.abs(ref) + 1e-12)
+
+
 # the spike in the first key tile, or in the third (it then moves the running
 # max mid-row); at 150 tokens the last 22 queries sit in a key-split tile, and
 # the merge must drop the partial results of the waves that never saw the spike
