@@ -61,7 +61,8 @@ def check_labels(got, ref):
                                              (1, 20, 17, (42, 30)),    # GroupNorm: 1 float4 per thread
                                              (1, 50, 45, (33, 61)),    # GroupNorm: 5 float4 per thread
                                              (1, 64, 128, (70, 60)),   # GroupNorm: 8192 pixels, 16 per thread
-                                             (1, 96, 90, (50, 40))])   # GroupNorm: > 8192 pixels (loop)
+                                             (1, 96, 90, (50, 40)),    # GroupNorm: > 8192 pixels (loop)
+                                             (1, 3, 240, (5, 500))])   # 240 x 19 classes: the gather resize
 def test_head_matches_oracle_small_grids(batch, gh, gw, out):
     require_gpu()
     cfg = synth.preset("vits14_518")

@@ -178,6 +178,32 @@ __global__ __launch_bounds__(256) void resize_nchw_kernel(const float* __restric
   }
 }
 
+// The same resize for grids whose staged row would not fit (gw * classes >
+// kResizeLds): one thread per output pixel, gathering its four source pixels'
+// class vectors directly (horizontal blends first, then the vertical one).
+__global__ __launch_bounds__(256) void resize_nchw_gather_kernel(const float* __restrict__ in, int ldi, int classes,
+                                                                 int gh, int gw, float* __restrict__ out, int H, int W) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= H * W) return;
+  const int y = i / W, x = i - y * W, b = blockIdx.y;
+  int y0, y1, x0, x1;
+  float ly, lx;
+  bilinear_tap(y, gh, H, y0, y1, ly);
+  bilinear_tap(x, gw, W, x0, x1, lx);
+  const float* base = in + (size_t)b * gh * gw * ldi;
+  const float* r00 = base + (size_t)(y0 * gw + x0) * ldi;
+  const float* r01 = base + (size_t)(y0 * gw + x1) * ldi;
+  const float* r10 = base + (size_t)(y1 * gw + x0) * ldi;
+  const float* r11 = base + (size_t)(y1 * gw + x1) * ldi;
+  float* o = out + (size_t)b * classes * H * W + i;
+  const size_t plane = (size_t)H * W;
+  for (int c = 0; c < classes; ++c) {
+    const float top = (1.f - lx) * r00[c] + lx * r01[c];
+    const float bot = (1.f - lx) * r10[c] + lx * r11[c];
+    o[c * plane] = (1.f - ly) * top + ly * bot;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_taps_cl(const float* taps, int batch, int ntaps, int D, int P, uint16_t* out, hipStream_t s) {
@@ -202,9 +228,13 @@ hipError_t launch_groupnorm_gelu(const float* x, size_t gstride, int batch, int 
 hipError_t launch_resize_nchw(const float* in, int ldi, int classes, int batch, int gh, int gw, float* out, int H,
                               int W, hipStream_t s) {
   if (classes < 1 || ldi < classes || batch < 1 || batch > 65535 || H < 1 || W < 1 || (long)H * W > (1L << 30) ||
-      gh < 1 || gw < 1 || (long)gw * classes > kResizeLds)
+      gh < 1 || gw < 1)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(resize_nchw_kernel, dim3(H, batch), dim3(256), 0, s, in, ldi, classes, gh, gw, out, H, W);
+  if ((long)gw * classes <= kResizeLds)
+    hipLaunchKernelGGL(resize_nchw_kernel, dim3(H, batch), dim3(256), 0, s, in, ldi, classes, gh, gw, out, H, W);
+  else
+    hipLaunchKernelGGL(resize_nchw_gather_kernel, dim3((unsigned)(((long)H * W + 255) / 256), batch), dim3(256), 0, s,
+                       in, ldi, classes, gh, gw, out, H, W);
   return hipGetLastError();
 }
 
