@@ -48,6 +48,64 @@ def test_layernorm(rows, dim, out_fp32):
     assert np.all(np.abs(got - ref) <= tol), np.abs(got - ref).max()
 
 
+def _exact_ln_rows(rows, dim):
+    """Rows whose LayerNorm is exact in fp32: an integer mean m in [-3, 3] plus
+    deviations in +-pairs of 4, 8 and 12 (5 : 8 : 3 pairs per 16), so the sum
+    is exactly m dim, the mean exact, every deviation exact, the sum of squares
+    exactly 64 dim, the variance exactly 64 and var + 1e-6 rounds back to 64
+    (half an ulp there is 3.8e-6): the normalised values are d / 8, and
+    y = fl32(d/8 * g + b) (one fused multiply-add, d/8 exact)."""
+    assert dim % 32 == 0
+    per = dim // 32
+    base = np.array([4] * 5 * per + [8] * 8 * per + [12] * 3 * per, dtype=np.float64)
+    d = np.empty((rows, dim))
+    for r in range(rows):
+        half = base * np.where(RNG.integers(0, 2, base.size) == 1, -1.0, 1.0)
+        d[r] = RNG.permutation(np.concatenate([half, -half]))
+    assert np.all((d ** 2).sum(axis=1) == 64 * dim) and np.all(d.sum(axis=1) == 0)
+    m = RNG.integers(-3, 4, (rows, 1)).astype(np.float64)
+    return (m + d).astype(np.float32), d
+
+
+@pytest.mark.parametrize("rows,dim", [(5, 64), (33, 384), (7, 768), (41, 1024), (3, 1536)])
+def test_layernorm_exact(rows, dim):
+    """The LayerNorm kernel bit for bit on rows where every step is exact
+    (see _exact_ln_rows), fp32 and bf16 outputs; it also pins rsqrt(64) = 1/8."""
+    say(f"layernorm exact rows={rows} dim={dim}")
+    x, d = _exact_ln_rows(rows, dim)
+    g = (1 + 0.02 * RNG.standard_normal(dim)).astype(np.float32)
+    b = (0.02 * RNG.standard_normal(dim)).astype(np.float32)
+    model = ((d / 8.0) * g.astype(np.float64) + b.astype(np.float64)).astype(np.float32)
+    y32 = torch.empty((rows, dim), dtype=torch.float32, device="cuda")
+    vit.vit_op_layernorm(f32_dev(x), rows, dim, f32_dev(g), f32_dev(b), 1e-6, y32, 1)
+    assert np.array_equal(host(y32), model), np.abs(host(y32) - model).max()
+    y16 = torch.empty((rows, dim), dtype=torch.bfloat16, device="cuda")
+    vit.vit_op_layernorm(f32_dev(x), rows, dim, f32_dev(g), f32_dev(b), 1e-6, y16, 0)
+    assert np.array_equal(host(y16), host(torch.from_numpy(model).to(torch.bfloat16)))
+
+
+@pytest.mark.parametrize("M", [64, 446, 1000])
+def test_linear_residual_ln_exact(M):
+    """The LayerNorm half of the fused residual + LN epilogue bit for bit: with
+    A = 0 and a zero bias the update adds exactly 0, so x keeps the exact rows of
+    _exact_ln_rows and h must be bf16(fl32(d/8 * g + b))."""
+    say(f"linear residual ln exact M={M}")
+    N = K = 384
+    x, d = _exact_ln_rows(M, N)
+    a_d, _ = bf16_dev(np.zeros((M, K)))
+    w_d, _ = bf16_dev(RNG.standard_normal((N, K)) * 0.05)
+    ls = np.full(N, 1e-5, np.float32)
+    g = (1 + 0.02 * RNG.standard_normal(N)).astype(np.float32)
+    b = (0.02 * RNG.standard_normal(N)).astype(np.float32)
+    xd = f32_dev(x)
+    h = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    vit.vit_op_linear_residual_ln(a_d, w_d, f32_dev(np.zeros(N, np.float32)), f32_dev(ls), M, N, K, xd, f32_dev(g),
+                                  f32_dev(b), 1e-6, h)
+    assert np.array_equal(host(xd), x)
+    model = ((d / 8.0) * g.astype(np.float64) + b.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(host(h), host(torch.from_numpy(model).to(torch.bfloat16)))
+
+
 WIDTHS = [64 * v for v in list(range(1, 17)) + [20, 24, 32, 48, 64]]
 
 
