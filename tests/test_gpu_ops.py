@@ -272,6 +272,57 @@ def test_qkv_exact_groups(batch, tokens, heads):
     assert np.array_equal(gv[:, :, :, cols], ref_v)
 
 
+def _phi_table():
+    """The GELU epilogue's table, built the way the library builds it on the
+    host: Phi at -6 + i/64 (i < 769) from the C library's erfc in double, each
+    entry (Phi_i, Phi_(i+1) - Phi_i) rounded to float (the last difference 0)."""
+    tab = np.zeros((769, 2), np.float32)
+    prev = 0.5 * math.erfc(6.0 / math.sqrt(2.0))
+    for i in range(769):
+        x1 = -6.0 + (i + 1) / 64.0
+        nxt = 0.5 * math.erfc(-x1 / math.sqrt(2.0)) if i + 1 < 769 else prev
+        tab[i] = (np.float32(prev), np.float32(nxt - prev))
+        prev = nxt
+    return tab
+
+
+@pytest.mark.parametrize("M,N,K", [(1000, 1536, 384), (446, 1152, 384), (257, 384, 1536), (4101, 1024, 128)])
+def test_linear_gelu_exact_groups(M, N, K):
+    """The GELU epilogue bit for bit.  Operands of magnitude [1, 2) / 16 keep
+    every 16-product group exact (as in test_linear_exact_groups) and put the
+    pre-activations z = fl32(acc + b) mostly inside the table's [-6, 6].  The
+    kernel then computes t = clamp(fma(z, 64, 384), 0, 768), Phi =
+    fma(fract(t), d_i, Phi_i) with i = int(t), y = fl32(z Phi) and rounds to
+    bf16; the model below does the same on the same table.  (The fused
+    products are exact in float64, so only a double rounding at a float
+    midpoint, about one output in 2^29, could tell them apart.)"""
+    say(f"linear gelu exact groups M={M} N={N} K={K}")
+    a, w = _unit_bf16((M, K)) / 16.0, _unit_bf16((N, K)) / 16.0
+    a_d, a_r = bf16_dev(a)
+    w_d, w_r = bf16_dev(w)
+    assert np.array_equal(a_r, a) and np.array_equal(w_r, w)
+    bias = (0.5 * RNG.standard_normal(N)).astype(np.float32)
+    acc = np.zeros((M, N), np.float32)
+    for g in range(0, K, 16):
+        acc = (acc.astype(np.float64) + a[:, g:g + 16] @ w[:, g:g + 16].T).astype(np.float32)
+    z = (acc.astype(np.float64) + bias).astype(np.float32)
+    tab = _phi_table()
+    t = np.clip((z.astype(np.float64) * 64.0 + 384.0).astype(np.float32), np.float32(0), np.float32(768))
+    i = t.astype(np.int32)
+    f = (t - np.floor(t)).astype(np.float32)
+    phi = (f.astype(np.float64) * tab[i, 1].astype(np.float64) + tab[i, 0].astype(np.float64)).astype(np.float32)
+    y = (z.astype(np.float64) * phi.astype(np.float64)).astype(np.float32)
+    model = host(torch.from_numpy(y).to(torch.bfloat16))
+    inside = ((t > 0) & (t < 768)).mean()
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    vit.vit_op_linear(a_d, w_d, f32_dev(bias), M, N, K, vit.EPI_GELU_BF16, None, out)
+    got = host(out)
+    diff = got != model
+    say(f"  {inside:.3f} of pre-activations inside the table, {diff.mean():.7f} of outputs differ from the model")
+    assert inside > 0.9
+    assert not diff.any(), (np.argwhere(diff)[:5], np.abs(got - model).max())
+
+
 def test_gelu_epilogue_wide_range():
     """GELU over pre-activations spanning [-8, 8] (every step of 1/16, exact in
     bf16), so the clamped ends of the epilogue's Phi lookup are exercised:
