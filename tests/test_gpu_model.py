@@ -18,7 +18,7 @@ import torch
 import synth
 import vision_transformer_encoder_block_amd as vit
 from oracle import vit_oracle as O
-from tests.gpu_util import cosine, f32_dev, host, require_gpu, say
+from tests.gpu_util import cosine, exact_ln_rows, f32_dev, host, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -177,6 +177,47 @@ def test_depth_zero_model():
     ref = O.forward(x, P, cfg)
     tok, desc, _ = run_gpu(cfg, P, x)
     assert np.abs(tok - ref["tokens"]).max() <= 2e-3
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_patch_embedding_and_final_norm_exact(batch):
+    """Patchify, the patch-embedding GEMM and its token-row scatter, the CLS and
+    register rows and the final LayerNorm, bit for bit through vit_forward at
+    depth 0.  Patch weights are one-hot (output n takes pixel n of its patch in
+    (c, ky, kx) order, weight 1), patch bias and position table are 0, and the
+    pixels are small integers (exact in bf16) laid out so that every patch row,
+    and the CLS and register rows, are the exact-LayerNorm rows of
+    gpu_util.exact_ln_rows: the tokens must be fl32(d/8 * g + b) exactly.  A
+    wrong im2col order, patch-to-token placement or row offset breaks it."""
+    rng = np.random.default_rng(23 + batch)
+    cfg = synth.preset("vits16_224", depth=0, img_h=64, img_w=48)
+    D, p, R = cfg["dim"], cfg["patch"], cfg["registers"]
+    gh, gw = synth.grid(cfg)
+    say(f"patch embedding + final norm exact, batch {batch}, grid {gh}x{gw}, {R} registers")
+    P = synth.make_params(cfg)
+    w = np.zeros((D, 3 * p * p), np.float32)
+    w[np.arange(D), np.arange(D)] = 1.0
+    P["patch_w"] = w.reshape(D, 3, p, p)
+    P["patch_b"] = np.zeros(D, np.float32)
+    P["pos"] = np.zeros_like(P["pos"])
+    special, d_special = exact_ln_rows(rng, 1 + R, D)
+    P["cls"], P["reg"] = special[0], special[1:]
+    rows, d_rows = exact_ln_rows(rng, batch * gh * gw, D)
+    x = rng.integers(-20, 21, (batch, 3, gh * p, gw * p)).astype(np.float32)
+    for b in range(batch):
+        for py in range(gh):
+            for px in range(gw):
+                patch = x[b, :, py * p:(py + 1) * p, px * p:(px + 1) * p].reshape(-1).copy()
+                patch[:D] = rows[(b * gh + py) * gw + px]
+                x[b, :, py * p:(py + 1) * p, px * p:(px + 1) * p] = patch.reshape(3, p, p)
+    tok, _, _ = run_gpu(cfg, P, x)
+    g, be = P["norm_g"].astype(np.float64), P["norm_b"].astype(np.float64)
+    dev = np.concatenate([np.repeat(d_special[None], batch, 0),
+                          d_rows.reshape(batch, gh * gw, D)], axis=1)          # [b, 1 + R + P, D]
+    model = ((dev / 8.0) * g + be).astype(np.float32).astype(np.float64)
+    diff = tok != model
+    say(f"  {diff.mean():.6f} of token values differ from the exact model")
+    assert not diff.any(), (np.argwhere(diff)[:5], np.abs(tok - model).max())
 
 
 # ------------------------------------------------------------------ the five workloads

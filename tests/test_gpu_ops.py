@@ -19,7 +19,7 @@ import synth
 import vision_transformer_encoder_block_amd as vit
 from oracle import vit_oracle as O
 from tests.attention_gate import accepted, attention_check, logit_factor, workload_qkv
-from tests.gpu_util import bf16_dev, f32_dev, host, require_gpu, say, vt_position
+from tests.gpu_util import bf16_dev, exact_ln_rows, f32_dev, host, require_gpu, say, vt_position
 
 pytestmark = pytest.mark.gpu
 RNG = np.random.default_rng(2024)
@@ -49,22 +49,9 @@ def test_layernorm(rows, dim, out_fp32):
 
 
 def _exact_ln_rows(rows, dim):
-    """Rows whose LayerNorm is exact in fp32: an integer mean m in [-3, 3] plus
-    deviations in +-pairs of 4, 8 and 12 (5 : 8 : 3 pairs per 16), so the sum
-    is exactly m dim, the mean exact, every deviation exact, the sum of squares
-    exactly 64 dim, the variance exactly 64 and var + 1e-6 rounds back to 64
-    (half an ulp there is 3.8e-6): the normalised values are d / 8, and
-    y = fl32(d/8 * g + b) (one fused multiply-add, d/8 exact)."""
-    assert dim % 32 == 0
-    per = dim // 32
-    base = np.array([4] * 5 * per + [8] * 8 * per + [12] * 3 * per, dtype=np.float64)
-    d = np.empty((rows, dim))
-    for r in range(rows):
-        half = base * np.where(RNG.integers(0, 2, base.size) == 1, -1.0, 1.0)
-        d[r] = RNG.permutation(np.concatenate([half, -half]))
-    assert np.all((d ** 2).sum(axis=1) == 64 * dim) and np.all(d.sum(axis=1) == 0)
-    m = RNG.integers(-3, 4, (rows, 1)).astype(np.float64)
-    return (m + d).astype(np.float32), d
+    """Rows whose LayerNorm is exact (gpu_util.exact_ln_rows); y = fl32(d/8 * g + b)
+    with one fused multiply-add, d/8 exact."""
+    return exact_ln_rows(RNG, rows, dim)
 
 
 @pytest.mark.parametrize("rows,dim", [(5, 64), (33, 384), (7, 768), (41, 1024), (3, 1536)])
