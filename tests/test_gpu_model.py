@@ -220,6 +220,47 @@ def test_patch_embedding_and_final_norm_exact(batch):
     assert not diff.any(), (np.argwhere(diff)[:5], np.abs(tok - model).max())
 
 
+def test_taps_exact():
+    """The four channel-first taps bit for bit: DINOv2-S/14 layout (taps after
+    blocks 3, 6, 9, 12) on a 3 x 3 grid with LayerScale 0, so every block adds
+    exactly 0 to the exact-LayerNorm rows of the patch embedding above, and each
+    tap [b, t, c, y, x] and the final tokens must equal fl32(d/8 * g + b) of
+    their row."""
+    rng = np.random.default_rng(31)
+    cfg = synth.preset("vits14_518", img_h=42, img_w=42, layerscale=0.0, bf16_params=False, sink=False)
+    D, p, R = cfg["dim"], cfg["patch"], cfg["registers"]
+    gh, gw = synth.grid(cfg)
+    batch = 2
+    say(f"taps exact, grid {gh}x{gw}, {len(cfg['taps'])} taps")
+    P = synth.make_params(cfg)
+    K = 3 * p * p
+    w = np.zeros((D, K), np.float32)
+    w[np.arange(D), np.arange(D)] = 1.0
+    P["patch_w"] = w.reshape(D, 3, p, p)
+    P["patch_b"] = np.zeros(D, np.float32)
+    P["pos"] = np.zeros_like(P["pos"])
+    special, d_special = exact_ln_rows(rng, 1 + R, D)
+    P["cls"] = special[0]
+    if R:
+        P["reg"] = special[1:]
+    rows, d_rows = exact_ln_rows(rng, batch * gh * gw, D)
+    x = rng.integers(-20, 21, (batch, 3, gh * p, gw * p)).astype(np.float32)
+    for b in range(batch):
+        for py in range(gh):
+            for px in range(gw):
+                patch = x[b, :, py * p:(py + 1) * p, px * p:(px + 1) * p].reshape(-1).copy()
+                patch[:D] = rows[(b * gh + py) * gw + px]
+                x[b, :, py * p:(py + 1) * p, px * p:(px + 1) * p] = patch.reshape(3, p, p)
+    tok, _, taps = run_gpu(cfg, P, x, with_taps=True)
+    g, be = P["norm_g"].astype(np.float64), P["norm_b"].astype(np.float64)
+    norm = ((d_rows / 8.0) * g + be).astype(np.float32).astype(np.float64).reshape(batch, gh, gw, D)
+    want_taps = np.repeat(norm.transpose(0, 3, 1, 2)[:, None], len(cfg["taps"]), axis=1)
+    assert taps.shape == want_taps.shape
+    assert np.array_equal(taps, want_taps), np.abs(taps - want_taps).max()
+    dev = np.concatenate([np.repeat(d_special[None], batch, 0), d_rows.reshape(batch, gh * gw, D)], axis=1)
+    assert np.array_equal(tok, ((dev / 8.0) * g + be).astype(np.float32).astype(np.float64))
+
+
 # ------------------------------------------------------------------ the five workloads
 
 def test_vits16_224_b1():
