@@ -198,7 +198,7 @@ def test_linear_exact_groups(M, N, K, epi):
 
 
 @pytest.mark.parametrize("M,N,K", [(5, 150, 384), (1000, 1536, 384), (4101, 1024, 128), (4100, 1024, 1024),
-                                   (1285, 16384, 256)])
+                                   (4101, 1024, 1024), (1285, 16384, 256)])
 def test_linear_residual_exact_groups(M, N, K):
     """The residual epilogue x += ls * (acc + b) bit for bit, with the operands
     of test_linear_exact_groups and LayerScale values that are powers of two

@@ -497,8 +497,9 @@ struct AMapConv3 {
 
 // XR = 32: the workgroups of row tile xt_tm also compute the 1..32 rows at the
 // end of A that follow the last full row tile (M mod BM <= 32), with the W tile
-// they already hold; each wave takes a 32 x 32 block of those rows, at the
-// columns of its wm-th 32-column block.  This saves a row of tiles that would
+// they already hold; each wave of the first two wave rows (wm = 0, 1) takes a
+// 32 x 32 block of those rows, at the columns of its wm-th 32-column block
+// (a 64-column wave tile has two).  This saves a row of tiles that would
 // each stream a whole W tile for a few rows.  Row tile 0 takes them: it is
 // dispatched first, so its longer workgroups do not form the kernel's tail.
 template <int BM, int BN, int BKT, int WGM, int WGN, int S, class Epi, class AM = AMapLinear, class MT = MmaBf16,
@@ -522,8 +523,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   constexpr int KS = BKT / MT::KPM;                 // MFMA k-steps per stage
   constexpr int STAGE_BYTES = (BM + BN + XR) * BKT * ES;  // A rows, W rows, then the extra A rows
   static_assert(XR == 0 || (XR == 32 && !HasRowLN<Epi>::value && !HasChanLN<Epi>::value && !HasTransposed<Epi>::value && !AM::kConv &&
-                            WGM == 2 && WTN == 64 && XR / (64 / (BKT * MT::ES / 16)) <= WGM * WGN),
-                "extra rows: plain row epilogues, one 32-column block per wave");
+                            (WGM == 2 || WGM == 4) && WTN == 64 && XR / (64 / (BKT * MT::ES / 16)) <= WGM * WGN),
+                "extra rows: plain row epilogues, one 32-column block per wave of the first two wave rows");
   static_assert(CPR == 4 || CPR == 8 || CPR == 16, "BK");
   static_assert(!AM::kConv || ES == 2, "implicit convolution reads bf16 activations");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
@@ -644,7 +645,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
       bw[buf][j] = MT::frag(Bc[r * CPR + swz_c<CPR>(r, qd)], Bc[r * CPR + swz_c<CPR>(r, qd + MT::CPF - 1)]);
     }
     if constexpr (XR > 0) {
-      if (xt) {
+      if (xt && wm < 2) {
         const uint4* Xc = Bc + BN * CPR;
         ax[buf] = MT::frag(Xc[lrow * CPR + swz_c<CPR>(lrow, qd)], Xc[lrow * CPR + swz_c<CPR>(lrow, qd + MT::CPF - 1)]);
       }
@@ -658,7 +659,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
     // columns wn * WTN + wm * 32 + [0, 32): the wm-th of the wave's B blocks,
     // chosen by a select (an index by the runtime wm would go through memory)
     if constexpr (XR > 0) {
-      if (xt) acc_x = MT::mma(ax[buf], wm ? bw[buf][1] : bw[buf][0], acc_x);
+      if (xt && wm < 2) acc_x = MT::mma(ax[buf], wm ? bw[buf][1] : bw[buf][0], acc_x);
     }
   };
   // wait until at most `later` stages of this wave's loads are in flight
@@ -943,7 +944,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
       wave_sync();
     }
     if constexpr (XR > 0) {
-      if (xt) {  // workgroup-uniform
+      if (xt && wm < 2) {  // wave-uniform
         // the extra rows: staged in the first 32 columns of the wave's area
 #pragma unroll
         for (int e = 0; e < 16; ++e) stage[((e >> 2) * 8 + lhalf * 4 + (e & 3)) * LD + lrow] = acc_x[e];
@@ -970,7 +971,7 @@ struct Cfg {
 // the last full row tile (see gemm_bf16_kernel's XR).
 template <class C, class Epi, class AM, class MT>
 constexpr bool takes_extra_rows() {
-  return (C::BM == 128 || C::BM == 256) && C::WGM == 2 && C::BN / C::WGN == 64 && !HasRowLN<Epi>::value &&
+  return (C::BM == 128 || C::BM == 256) && (C::WGM == 2 || C::WGM == 4) && C::BN / C::WGN == 64 && !HasRowLN<Epi>::value &&
          !HasChanLN<Epi>::value && !HasTransposed<Epi>::value && !AM::kConv && std::is_same<MT, MmaBf16>::value;
 }
 
@@ -1001,6 +1002,12 @@ using CfgMid = Cfg<128, 128, 64, 2, 2, 2>;
 using CfgSmall = Cfg<64, 128, 64, 2, 2, 2>;
 using CfgBig = Cfg<256, 256, 64, 2, 4, 2>;
 using CfgTiny = Cfg<64, 64, 64, 2, 2, 2>;
+// 128 x 128 with 8 waves (32 x 64 wave tiles, two waves per SIMD), for grids
+// of at most one tile per CU with extra rows (ViT-L/16 b1 out-proj and fc2):
+// the second wave of a SIMD covers the first one's load waits.  Only the
+// extra-rows form exists: without the extra A rows the eight waves' epilogue
+// staging would not fit the two stages.
+using CfgMidW8 = Cfg<128, 128, 64, 4, 2, 2>;
 // fp8 operands: a K step of 128 values is the same 128-byte row slice as 64 bf16 values
 using CfgMid8 = Cfg<128, 128, 128, 2, 2, 2>;
 using CfgSmall8 = Cfg<64, 128, 128, 2, 2, 2>;
@@ -1028,6 +1035,18 @@ hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const
     return run<CfgTiny>(A, W, M, N, K, epi, s, am);
   }
   if (K <= 512 && mid_tiles < 512) return run<CfgSmall>(A, W, M, N, K, epi, s, am);
+  if constexpr (takes_extra_rows<CfgMidW8, Epi, AM, MmaBf16>()) {
+    // ViT-L/16 b1 out-proj and fc2 (4101 x 1024, 256 tiles): 18.5 -> 18.1 us and
+    // 47.6 -> 46.1 us, forward 6.019 -> 5.982 ms (same-process A/B, outputs
+    // bit-identical)
+    using C = CfgMidW8;
+    const int tiles_n = (N + C::BN - 1) / C::BN, full = M / C::BM, rem = M % C::BM;
+    if ((long)full * tiles_n <= 256 && full >= 1 && rem > 0 && rem <= 32) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<C::BM, C::BN, C::BK, C::WGM, C::WGN, C::S, Epi, AM, MmaBf16, 32>),
+                         dim3(full * tiles_n), dim3(64 * C::WGM * C::WGN), 0, s, A, W, M, N, K, full, tiles_n, epi, am, 0);
+      return hipGetLastError();
+    }
+  }
   return run<CfgMid>(A, W, M, N, K, epi, s, am);
 }
 
