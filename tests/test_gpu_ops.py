@@ -117,6 +117,7 @@ def test_layernorm_every_supported_width(dim):
 SHAPES = [(1, 64, 64), (5, 150, 384), (130, 384, 384), (446, 1152, 384), (1000, 1536, 384), (257, 384, 1536),
           (4101, 1024, 128), (300, 96, 768),
           (3000, 3000, 640),   # 128 x 128 tiles, ragged in M and N
+          (4160, 2000, 320),   # 8-wave 128 x 128 tiles (K <= 512) staging 16 rows at a time, ragged in M and N
           (4100, 8200, 192),   # 256 x 256 tiles (M N >= 32M), ragged in M and N
           # 128 x 128 tiles whose last full row tile also takes the 1..32 rows after it
           (4101, 4096, 128), (4128, 3072, 192), (3969, 2048, 256), (4100, 1024, 1024),
@@ -198,7 +199,7 @@ def test_linear_exact_groups(M, N, K, epi):
 
 
 @pytest.mark.parametrize("M,N,K", [(5, 150, 384), (1000, 1536, 384), (4101, 1024, 128), (4100, 1024, 1024),
-                                   (4101, 1024, 1024), (1285, 16384, 256)])
+                                   (4101, 1024, 1024), (4160, 2000, 320), (1285, 16384, 256)])
 def test_linear_residual_exact_groups(M, N, K):
     """The residual epilogue x += ls * (acc + b) bit for bit, with the operands
     of test_linear_exact_groups and LayerScale values that are powers of two
@@ -273,7 +274,8 @@ def _phi_table():
     return tab
 
 
-@pytest.mark.parametrize("M,N,K", [(1000, 1536, 384), (446, 1152, 384), (257, 384, 1536), (4101, 1024, 128)])
+@pytest.mark.parametrize("M,N,K", [(1000, 1536, 384), (446, 1152, 384), (257, 384, 1536), (4101, 1024, 128),
+                                   (4160, 2000, 320)])
 def test_linear_gelu_exact_groups(M, N, K):
     """The GELU epilogue bit for bit.  Operands of magnitude [1, 2) / 16 keep
     every 16-product group exact (as in test_linear_exact_groups) and put the

@@ -876,22 +876,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
     }
   }
   if constexpr (!HasRowLN<Epi>::value && !HasChanLN<Epi>::value) {
-    // Each wave stages one 32-row block of its tile at a time (row stride WTN + 8
-    // floats: the two lane halves land on disjoint banks), then every lane
-    // handles 4 consecutive columns of PASSES rows.  The staging areas live in
-    // the (now idle) LDS of the pipeline stages.
+    // Each wave stages SR rows of one 32-row block of its tile at a time (32, or
+    // 16 where the waves' 32-row areas would not fit the stages; row stride
+    // WTN + 8 floats: the two lane halves land on disjoint banks), then every
+    // lane handles 4 consecutive columns of PASSES rows.  The staging areas
+    // live in the (now idle) LDS of the pipeline stages.
     constexpr int LD = WTN + 8;
     constexpr int LPR = WTN / 4;                   // lanes per staged row
     constexpr int RPP = 64 / LPR;                  // rows per pass
-    constexpr int PASSES = (32 + RPP - 1) / RPP;
-    constexpr int WAVE_BYTES = 32 * LD * 4;
+    constexpr int SR = (STAGE_BYTES / (32 * LD * 4)) * S >= NW ? 32 : 16;  // rows staged at a time
+    constexpr int PASSES = (SR + RPP - 1) / RPP;
+    constexpr int WAVE_BYTES = SR * LD * 4;
     constexpr int WPB = STAGE_BYTES / WAVE_BYTES;  // waves per stage object
     static_assert(LPR <= 64, "staging pass shape");
     static_assert(WPB >= 1 && WPB * S >= NW, "staging must fit in the stage LDS");
     float* stage = nullptr;
     static_for<0, S>([&](auto s) {
       if (wave / WPB == decltype(s)::value)
-        stage = reinterpret_cast<float*>(stage_lds<STAGE_BYTES, decltype(s)::value>()) + (wave % WPB) * 32 * LD;
+        stage = reinterpret_cast<float*>(stage_lds<STAGE_BYTES, decltype(s)::value>()) + (wave % WPB) * SR * LD;
     });
     const int cl = (lane % LPR) * 4;
     const int n = n0 + wn * WTN + cl;
@@ -902,7 +904,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
     const int n_rd = lane_ok ? n : n0;
     const int nvalid_rd = lane_ok ? nvalid : min(4, N - n0);
     const typename Epi::Col cc = epi.col4(n_rd, nvalid_rd);
-    // One staged 32-row block (rows row0 + [0, 32)): this lane's 4 columns at
+    // One staged block of SR rows (rows row0 + [0, SR)): this lane's 4 columns at
     // column nl (ok: inside the block and the matrix), with the read-side
     // column nl_rd / count nv_rd and the column constants c.
     auto emit = [&](int row0, int nl, int nv, bool ok, int nl_rd, int nv_rd, const typename Epi::Col& c) {
@@ -911,7 +913,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
       const int mb = row0 + lane / LPR;
 #pragma unroll
       for (int pass = 0; pass < PASSES; ++pass) {
-        const int r = min(pass * RPP + lane / LPR, 31);
+        const int r = min(pass * RPP + lane / LPR, SR - 1);
         const float4 t = *reinterpret_cast<const float4*>(stage + r * LD + cl);
         v[pass][0] = t.x;
         v[pass][1] = t.y;
@@ -930,22 +932,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
 #pragma unroll
       for (int pass = 0; pass < PASSES; ++pass) {
         const int r = pass * RPP + lane / LPR;
-        if (ok && r < 32 && mb + pass * RPP < M) write4_any(epi, mb + pass * RPP, nl, v[pass], nv, c, 0);
+        if (ok && r < SR && mb + pass * RPP < M) write4_any(epi, mb + pass * RPP, nl, v[pass], nv, c, 0);
       }
     };
+    // accumulator element e holds row 8 (e / 4) + 4 lhalf + e % 4 of its block:
+    // rows [16 h, 16 h + 16) are elements 8 h .. 8 h + 7
+    constexpr int EH = SR / 2;  // elements per staged part
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int h = 0; h < 32 / SR; ++h) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) stage[((e >> 2) * 8 + lhalf * 4 + (e & 3)) * LD + j * 32 + lrow] = acc[i][j][e];
-      wave_sync();
-      emit(m0 + wm * WTM + i * 32, n, nvalid, lane_ok, n_rd, nvalid_rd, cc);
-      wave_sync();
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = h * EH; e < h * EH + EH; ++e)
+            stage[((e >> 2) * 8 + lhalf * 4 + (e & 3) - h * SR) * LD + j * 32 + lrow] = acc[i][j][e];
+        wave_sync();
+        emit(m0 + wm * WTM + i * 32 + h * SR, n, nvalid, lane_ok, n_rd, nvalid_rd, cc);
+        wave_sync();
+      }
     }
     if constexpr (XR > 0) {
       if (xt && wm < 2) {  // wave-uniform
         // the extra rows: staged in the first 32 columns of the wave's area
+        static_assert(SR == 32, "extra rows are staged whole");
 #pragma unroll
         for (int e = 0; e < 16; ++e) stage[((e >> 2) * 8 + lhalf * 4 + (e & 3)) * LD + lrow] = acc_x[e];
         wave_sync();
@@ -1002,11 +1012,11 @@ using CfgMid = Cfg<128, 128, 64, 2, 2, 2>;
 using CfgSmall = Cfg<64, 128, 64, 2, 2, 2>;
 using CfgBig = Cfg<256, 256, 64, 2, 4, 2>;
 using CfgTiny = Cfg<64, 64, 64, 2, 2, 2>;
-// 128 x 128 with 8 waves (32 x 64 wave tiles, two waves per SIMD), for grids
-// of at most one tile per CU with extra rows (ViT-L/16 b1 out-proj and fc2):
-// the second wave of a SIMD covers the first one's load waits.  Only the
-// extra-rows form exists: without the extra A rows the eight waves' epilogue
-// staging would not fit the two stages.
+// 128 x 128 with 8 waves (32 x 64 wave tiles): two waves per SIMD for grids of
+// at most one tile per CU with extra rows (ViT-L/16 b1 out-proj and fc2), where
+// the second wave of a SIMD covers the first one's load waits, and four for
+// short-K products with two workgroups per CU.  Without extra rows the eight
+// waves stage their epilogue rows 16 at a time (32 would not fit the stages).
 using CfgMidW8 = Cfg<128, 128, 64, 4, 2, 2>;
 // fp8 operands: a K step of 128 values is the same 128-byte row slice as 64 bf16 values
 using CfgMid8 = Cfg<128, 128, 128, 2, 2, 2>;
@@ -1046,6 +1056,14 @@ hipError_t dispatch(const bf16_t* A, const bf16_t* W, int M, int N, int K, const
                          dim3(full * tiles_n), dim3(64 * C::WGM * C::WGN), 0, s, A, W, M, N, K, full, tiles_n, epi, am, 0);
       return hipGetLastError();
     }
+  }
+  if constexpr (!AM::kConv) {
+    // short-K products with several tiles per CU (ViT-S fc1, 14272 x 1536 x
+    // 384: 37.8 -> 34.6 us; DINOv2-S @518 b8 fc1: 29.5 -> 27.4 us; same-process
+    // A/B, outputs bit-identical): two 8-wave workgroups per CU put four waves
+    // on each SIMD, so one workgroup's epilogue overlaps the other's loads.
+    // Longer K gained nothing (ViT-L b4 out-proj 48.7 -> 50.4 us).
+    if (K <= 512) return run<CfgMidW8>(A, W, M, N, K, epi, s, am);
   }
   return run<CfgMid>(A, W, M, N, K, epi, s, am);
 }
