@@ -225,7 +225,7 @@ def test_linear_residual_exact_groups(M, N, K):
     assert not diff.any(), (np.argwhere(diff)[:5], np.abs(got - model).max())
 
 
-@pytest.mark.parametrize("batch,tokens,heads", [(2, 201, 6), (1, 446, 6), (3, 70, 2), (1, 4101, 16)])
+@pytest.mark.parametrize("batch,tokens,heads", [(2, 201, 6), (1, 446, 6), (3, 70, 2), (1, 4101, 16), (20, 446, 6)])
 def test_qkv_exact_groups(batch, tokens, heads):
     """The fused Q/K/V projection bit for bit on operands whose k groups sum
     exactly (see test_linear_exact_groups): q = bf16((acc + b) * log2(e)/8) with
@@ -370,7 +370,8 @@ def test_linear_residual_ln(M, K):
 # the last three: 128-row tiles with a ragged last row tile of 5, 32 and 5 rows
 # (ViT-L/16 @1024 b1), V^T columns included
 @pytest.mark.parametrize("batch,tokens,heads", [(1, 5, 1), (2, 201, 6), (1, 446, 6), (3, 70, 2),
-                                                (1, 133, 16), (2, 80, 10), (1, 4101, 16)])
+                                                (1, 133, 16), (2, 80, 10), (1, 4101, 16),
+                                                (20, 446, 6)])  # 8-wave tiles, V^T staged 16 rows at a time
 def test_qkv_split(batch, tokens, heads):
     say(f"qkv batch={batch} tokens={tokens} heads={heads}")
     D = 64 * heads
