@@ -1020,6 +1020,10 @@ hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi&
 using CfgMid = Cfg<128, 128, 64, 2, 2, 2>;
 using CfgSmall = Cfg<64, 128, 64, 2, 2, 2>;
 using CfgBig = Cfg<256, 256, 64, 2, 4, 2>;
+// 256 x 256 on 16 waves (64 x 64 wave tiles, four waves per SIMD at <= 128
+// VGPRs), epilogue rows staged 16 at a time: the fused Q/K/V projection, which
+// takes no extra rows (with them the 16-wave kernels spill)
+using CfgBig16 = Cfg<256, 256, 64, 4, 4, 2>;
 using CfgTiny = Cfg<64, 64, 64, 2, 2, 2>;
 // 128 x 128 with 8 waves (32 x 64 wave tiles): two waves per SIMD for grids of
 // at most one tile per CU with extra rows (ViT-L/16 b1 out-proj and fc2), where
@@ -1110,8 +1114,10 @@ const float2* phi_table_device() {
 hipError_t dispatch_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, const EpiQKV& epi, hipStream_t s) {
   const long mid_tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
   const long outs = (long)M * N;
-  if ((outs >= 32L * 1024 * 1024 || (K >= 1024 && outs >= 8L * 1024 * 1024)) && (2 * epi.D) % CfgBig::BN == 0)
-    return run<CfgBig>(A, W, M, N, K, epi, s);
+  // 16 waves: ViT-L/16 b1 4101 x 3072 x 1024 37.3 -> 34.6 us, b4 132.3 -> 123.2 us
+  // against 8 (same-process A/B, q and k bit-identical)
+  if ((outs >= 32L * 1024 * 1024 || (K >= 1024 && outs >= 8L * 1024 * 1024)) && (2 * epi.D) % CfgBig16::BN == 0)
+    return run<CfgBig16>(A, W, M, N, K, epi, s);
   if (K <= 512 && mid_tiles < 512) return run<CfgSmall>(A, W, M, N, K, epi, s);
   // short K: 8-wave tiles as in dispatch (DINOv2-S @518 b8, 10960 x 1152 x
   // 384: 22.3 -> 20.9 us; ViT-S b32 25.9 -> 25.6 us; same-process A/B)
