@@ -53,7 +53,26 @@ struct AttnArgs {
   int qtiles;      // query tiles per (b, h); the grid is 1-D
   int B;
   int split;       // 1: the last query tile holds 1..32 queries and its waves split the keys
+  int n_attn;      // workgroups that compute attention; the ones after them prefetch
+  const uint4* pf; // region the prefetch workgroups read into the caches (or null)
+  uint32_t pf_chunks;  // its length in 16-byte chunks
 };
+
+// Workgroups past the attention grid read a region of memory that the next
+// kernels will stream (weights of a later layer) and discard it: the lines
+// then sit in the last-level cache when those kernels start, instead of
+// coming from HBM at their first touch.  Attention itself needs little of
+// the memory system, so the reads run in its shadow.
+__device__ __forceinline__ void prefetch_region(const uint4* p, uint32_t n, uint32_t w, uint32_t nw) {
+  uint32_t acc = 0;
+  const uint32_t stride = nw * blockDim.x;
+#pragma unroll 8
+  for (uint32_t i = w * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  asm volatile("" ::"v"(acc));  // keeps the loads
+}
 
 // Workgroup id -> (query tile, head, image).  Workgroups are handed
 // to the 8 XCDs round-robin by id; the ids are renumbered so that each XCD
@@ -83,6 +102,10 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
   static_assert(S * L < 64, "vmcnt range");
   __shared__ uint4 KV[S][2][KT * 8];  // [stage][K | V^T][16-byte chunk]
 
+  if ((int)blockIdx.x >= a.n_attn) {  // workgroup-uniform
+    prefetch_region(a.pf, a.pf_chunks, blockIdx.x - a.n_attn, gridDim.x - a.n_attn);
+    return;
+  }
   const int N = a.N, H = a.H, nv = a.nv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int qt, h, b;
@@ -447,13 +470,26 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
 // part in the loads and barriers, with 1..32 its waves split the keys and
 // merge in LDS), so no workspace is needed.
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
-                            int heads, int nv, uint16_t* o, hipStream_t s) {
+                            int heads, int nv, uint16_t* o, const void* prefetch, size_t prefetch_bytes,
+                            hipStream_t s) {
   if (batch <= 0 || tokens <= 0 || heads <= 0 || nv < tokens || nv % 64 != 0) return hipErrorInvalidValue;
   if ((size_t)nv * 128 >= (1ull << 32)) return hipErrorInvalidValue;
+  if (prefetch != nullptr && (reinterpret_cast<uintptr_t>(prefetch) % 16 != 0 || prefetch_bytes >= (1ull << 32)))
+    return hipErrorInvalidValue;
   const int qtiles = (tokens + QT - 1) / QT;
   const int rem = tokens % QT;
-  AttnArgs a{q, k, vt, o, tokens, heads, nv, qtiles, batch, rem > 0 && rem <= 32 ? 1 : 0};
-  hipLaunchKernelGGL((attention_kernel<4>), dim3(qtiles * heads * batch), dim3(256), 0, s, a);
+  const int n_attn = qtiles * heads * batch;
+  // About 32 chunks of 16 bytes per prefetching lane, at most 64 workgroups.
+  // They run beside the attention workgroups only if the whole grid is
+  // resident at once (three workgroups per CU on the 256 CUs of an MI355X);
+  // otherwise they would wait for a free slot and lengthen the launch.
+  constexpr int kResident = 3 * 256;
+  const uint32_t chunks = prefetch ? (uint32_t)(prefetch_bytes / 16) : 0u;
+  int n_pf = chunks ? (int)std::min<uint32_t>(64u, (chunks + 256u * 32u - 1) / (256u * 32u)) : 0;
+  if (n_attn + n_pf > kResident) n_pf = 0;
+  AttnArgs a{q, k, vt, o, tokens, heads, nv, qtiles, batch, rem > 0 && rem <= 32 ? 1 : 0,
+             n_attn, static_cast<const uint4*>(prefetch), chunks};
+  hipLaunchKernelGGL((attention_kernel<4>), dim3(n_attn + n_pf), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

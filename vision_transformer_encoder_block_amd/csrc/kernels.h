@@ -122,9 +122,12 @@ hipError_t launch_patchify(const float* img, int batch, int H, int W, int p, int
 hipError_t launch_pos_resample(const float* pos_in, int gh, int gw, float* pos_out, int th, int tw, int dim,
                                hipStream_t s);
 
-// Attention core (see vit_op_attention); no workspace.
+// Attention core (see vit_op_attention); no workspace.  Extra workgroups
+// read [prefetch, prefetch + prefetch_bytes) (16-byte aligned, < 4 GiB; may be null)
+// and discard it, so that a later kernel finds it in the last-level cache.
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int batch, int tokens,
-                            int heads, int nv, uint16_t* o, hipStream_t s);
+                            int heads, int nv, uint16_t* o, const void* prefetch, size_t prefetch_bytes,
+                            hipStream_t s);
 
 // ---- semantic head (channels-last activations, one row per pixel)
 // Taps [batch, ntaps, D, P] fp32 (channel-first) -> out bf16 [batch * P, ntaps * D].

@@ -40,6 +40,7 @@ int hip_fail(hipError_t e, const char* what) {
   } while (0)
 
 constexpr size_t kAlign = 256;
+constexpr size_t kLastLevelCacheBytes = 256ull << 20;  // MI355X Infinity Cache
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
@@ -391,7 +392,22 @@ int run_encoder(vit_model* m, const Acts& a, const Geom& g, const float* images,
     eq.heads = pl.heads;
     eq.nv = g.nv;
     VIT_HIP(vit::launch_gemm(a.h, w.wqkv, M, 3 * D, D, eq, st), "qkv");
-    VIT_HIP(vit::launch_attention(a.q, a.k, a.vt, batch, N, pl.heads, g.nv, a.o, st),
+    // While attention runs (it needs little of the memory system), spare
+    // workgroups of its launch read this block's remaining weights (out
+    // projection, fc1, fc2) and the next block's Q/K/V weights, which lie
+    // contiguous in the weight buffer.  Weights larger than the last-level
+    // cache (256 MB on an MI355X) are evicted by the rest of a forward, so
+    // each GEMM would otherwise fetch its weights from HBM at first use;
+    // smaller models keep theirs cached and skip the extra reads.
+    const void* pf = nullptr;
+    size_t pf_bytes = 0;
+    if (pl.wl.total > kLastLevelCacheBytes) {
+      const char* pf_end = l + 1 < pl.L ? (const char*)(m->blocks[l + 1].wqkv + (size_t)3 * D * D)
+                                        : (const char*)(w.w2 + (size_t)D * Hm);
+      pf = w.wo;
+      pf_bytes = (size_t)(pf_end - (const char*)w.wo);
+    }
+    VIT_HIP(vit::launch_attention(a.q, a.k, a.vt, batch, N, pl.heads, g.nv, a.o, pf, pf_bytes, st),
             "attention");
     vit::EpiParams eo;
     eo.kind = fuse_ln ? vit::EPI_RESIDUAL_LN : vit::EPI_RESIDUAL;
@@ -831,7 +847,7 @@ int vit_op_attention(const void* q, const void* k, const void* vt, int batch, in
   if (!q || !k || !vt || !o) return fail(VIT_ERR_ARG, "NULL pointer");
   if (batch < 1 || tokens < 1 || heads < 1 || heads > 64) return fail(VIT_ERR_SHAPE, "bad batch/tokens/heads");
   VIT_HIP(vit::launch_attention((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, batch, tokens, heads,
-                                round_up(tokens, 64), (uint16_t*)o, (hipStream_t)stream),
+                                round_up(tokens, 64), (uint16_t*)o, nullptr, 0, (hipStream_t)stream),
           "attention");
   return VIT_OK;
 }
