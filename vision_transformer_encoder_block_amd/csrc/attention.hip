@@ -58,21 +58,6 @@ struct AttnArgs {
   uint32_t pf_chunks;  // its length in 16-byte chunks
 };
 
-// Workgroups past the attention grid read a region of memory that the next
-// kernels will stream (weights of a later layer) and discard it: the lines
-// then sit in the last-level cache when those kernels start, instead of
-// coming from HBM at their first touch.  Attention itself needs little of
-// the memory system, so the reads run in its shadow.
-__device__ __forceinline__ void prefetch_region(const uint4* p, uint32_t n, uint32_t w, uint32_t nw) {
-  uint32_t acc = 0;
-  const uint32_t stride = nw * blockDim.x;
-#pragma unroll 8
-  for (uint32_t i = w * blockDim.x + threadIdx.x; i < n; i += stride) {
-    const uint4 v = p[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
-  }
-  asm volatile("" ::"v"(acc));  // keeps the loads
-}
 
 // Workgroup id -> (query tile, head, image).  Workgroups are handed
 // to the 8 XCDs round-robin by id; the ids are renumbered so that each XCD
@@ -102,6 +87,8 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void attention_kernel(AttnArgs a)
   static_assert(S * L < 64, "vmcnt range");
   __shared__ uint4 KV[S][2][KT * 8];  // [stage][K | V^T][16-byte chunk]
 
+  // Workgroups past the attention grid read weights that the next kernels
+  // will stream (attention itself needs little of the memory system).
   if ((int)blockIdx.x >= a.n_attn) {  // workgroup-uniform
     prefetch_region(a.pf, a.pf_chunks, blockIdx.x - a.n_attn, gridDim.x - a.n_attn);
     return;
@@ -481,9 +468,9 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
   const int n_attn = qtiles * heads * batch;
   // About 32 chunks of 16 bytes per prefetching lane, at most 64 workgroups.
   // They run beside the attention workgroups only if the whole grid is
-  // resident at once (three workgroups per CU on the 256 CUs of an MI355X);
-  // otherwise they would wait for a free slot and lengthen the launch.
-  constexpr int kResident = 3 * 256;
+  // resident at once (three workgroups per CU); otherwise they would wait for
+  // a free slot and lengthen the launch.
+  constexpr int kResident = 3 * kComputeUnits;
   const uint32_t chunks = prefetch ? (uint32_t)(prefetch_bytes / 16) : 0u;
   int n_pf = chunks ? (int)std::min<uint32_t>(64u, (chunks + 256u * 32u - 1) / (256u * 32u)) : 0;
   if (n_attn + n_pf > kResident) n_pf = 0;

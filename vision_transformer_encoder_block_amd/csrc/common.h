@@ -7,6 +7,9 @@
 
 namespace vit {
 
+// Compute units of an MI355X (8 XCDs of 32); launch shapes are sized for it.
+constexpr int kComputeUnits = 256;
+
 typedef uint16_t bf16_t;  // storage type of a bfloat16 value
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -178,5 +181,21 @@ inline FastDiv make_fastdiv(uint32_t d) {
 }
 
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.mul) + n) >> f.shift; }
+
+// Reads n 16-byte chunks from p, the chunks split over nw workgroups (this
+// is workgroup w), and discards them: the lines then sit in the last-level
+// cache when a later kernel streams the region, instead of coming from HBM
+// at its first touch.  Extra workgroups of a launch that leaves compute units
+// idle run this beside the launch's real work.
+__device__ __forceinline__ void prefetch_region(const uint4* p, uint32_t n, uint32_t w, uint32_t nw) {
+  uint32_t acc = 0;
+  const uint32_t stride = nw * blockDim.x;
+#pragma unroll 8
+  for (uint32_t i = w * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  asm volatile("" ::"v"(acc));  // keeps the loads
+}
 
 }  // namespace vit

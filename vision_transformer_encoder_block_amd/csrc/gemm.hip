@@ -23,6 +23,7 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <type_traits>
@@ -342,6 +343,10 @@ struct HasRowLN : std::false_type {};
 template <class E>
 struct HasRowLN<E, std::void_t<decltype(E::kD)>> : std::true_type {};
 template <class E, class = void>
+struct HasPrefetch : std::false_type {};
+template <class E>
+struct HasPrefetch<E, std::void_t<decltype(E::pf_chunks)>> : std::true_type {};
+template <class E, class = void>
 struct HasChanLN : std::false_type {};
 template <class E>
 struct HasChanLN<E, std::void_t<decltype(E::kC)>> : std::true_type {};
@@ -363,6 +368,10 @@ struct EpiResidualLN {
   const float* b;
   float eps;
   bf16_t* h;   // [M, kD] bf16
+  // workgroups past the tile grid read this region (16-byte chunks) into the
+  // caches: the next GEMMs' weights, on the CUs the row tiles leave idle
+  const uint4* pf = nullptr;
+  uint32_t pf_chunks = 0;
 };
 
 // Channel LayerNorm of whole rows (N = kC channels of a pixel), the semantic
@@ -531,6 +540,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
   static_assert(A_INS * RPI == BM && TOT * RPI == BM + BN && L >= 1, "DMA split");
   static_assert(S >= 2 && S * LHI < 64, "pipeline depth");
 
+  if constexpr (HasPrefetch<Epi>::value) {
+    const int tiles = tiles_m * tiles_n;
+    if ((int)blockIdx.x >= tiles) {  // workgroup-uniform
+      prefetch_region(epi.pf, epi.pf_chunks, blockIdx.x - tiles, gridDim.x - tiles);
+      return;
+    }
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -995,7 +1011,8 @@ constexpr bool takes_extra_rows() {
 }
 
 template <class C, class Epi, class AM = AMapLinear, class MT = MmaBf16>
-hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s, AM am = {}) {
+hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi& epi, hipStream_t s, AM am = {},
+               int extra_wgs = 0) {
   const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
   if (K % C::BK != 0) return hipErrorInvalidValue;
   if constexpr (takes_extra_rows<C, Epi, AM, MT>()) {
@@ -1008,8 +1025,9 @@ hipError_t run(const bf16_t* A, const bf16_t* W, int M, int N, int K, const Epi&
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_bf16_kernel<C::BM, C::BN, C::BK, C::WGM, C::WGN, C::S, Epi, AM, MT>), dim3(tiles_m * tiles_n),
-                     dim3(64 * C::WGM * C::WGN), 0, s, A, W, M, N, K, tiles_m, tiles_n, epi, am, -1);
+  hipLaunchKernelGGL((gemm_bf16_kernel<C::BM, C::BN, C::BK, C::WGM, C::WGN, C::S, Epi, AM, MT>),
+                     dim3(tiles_m * tiles_n + extra_wgs), dim3(64 * C::WGM * C::WGN), 0, s, A, W, M, N, K, tiles_m,
+                     tiles_n, epi, am, -1);
   return hipGetLastError();
 }
 
@@ -1216,7 +1234,21 @@ hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, int M, int N, int K
           reinterpret_cast<uintptr_t>(ep.h) % 8 != 0)
         return hipErrorInvalidValue;
       EpiResidualLN e{ep.bias, ep.ls, (float*)ep.out, ep.ln_g, ep.ln_b, ep.eps, (bf16_t*)ep.h};
-      return run<CfgRowLN>(A, W, M, N, K, e, s);
+      // One 64-row tile per CU (its two stages fill most of the LDS); where
+      // the tiles leave CUs idle, up to that many extra workgroups read the
+      // prefetch region there, about 32 chunks of 16 bytes per lane.
+      const int tiles = (M + CfgRowLN::BM - 1) / CfgRowLN::BM;
+      int extra = 0;
+      if (ep.prefetch && ep.prefetch_bytes >= 16 && tiles < kComputeUnits) {
+        if (reinterpret_cast<uintptr_t>(ep.prefetch) % 16 != 0 || ep.prefetch_bytes >= (1ull << 32))
+          return hipErrorInvalidValue;
+        const uint32_t chunks = (uint32_t)(ep.prefetch_bytes / 16);
+        constexpr uint32_t per_wg = 64u * CfgRowLN::WGM * CfgRowLN::WGN * 32u;
+        extra = (int)std::min<uint32_t>((uint32_t)(kComputeUnits - tiles), (chunks + per_wg - 1) / per_wg);
+        e.pf = static_cast<const uint4*>(ep.prefetch);
+        e.pf_chunks = chunks;
+      }
+      return run<CfgRowLN>(A, W, M, N, K, e, s, AMapLinear{}, extra);
     }
     case EPI_CHAN_LN:
       return dispatch_chan_ln(A, W, M, N, K, ep, s, AMapLinear{});

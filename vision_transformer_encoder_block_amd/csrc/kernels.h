@@ -44,6 +44,10 @@ struct EpiParams {
   const float* ln_b = nullptr;
   float eps = 0.f;
   uint16_t* h = nullptr;
+  // EPI_RESIDUAL_LN: a region (16-byte aligned, < 4 GiB) that workgroups on
+  // the CUs the row tiles leave idle read into the caches, or null
+  const void* prefetch = nullptr;
+  size_t prefetch_bytes = 0;
   // EPI_CHAN_LN (out is bf16 here)
   int c0 = 0;
   bool silu = false;

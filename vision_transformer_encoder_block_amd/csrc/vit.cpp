@@ -419,6 +419,12 @@ int run_encoder(vit_model* m, const Acts& a, const Geom& g, const float* images,
     eo.ln_b = w.ln2_b;
     eo.eps = eps;
     eo.h = a.h;
+    // The row-LayerNorm GEMMs run one 64-row tile per CU; on the CUs they leave
+    // idle, extra workgroups read the weights of the GEMMs that follow (here
+    // fc1 and fc2, contiguous), which the rest of a forward evicts from the
+    // last-level cache between uses.
+    eo.prefetch = w.w1;
+    eo.prefetch_bytes = (size_t)((const char*)(w.w2 + (size_t)D * Hm) - (const char*)w.w1);
     VIT_HIP(vit::launch_gemm(a.o, w.wo, M, D, D, eo, st), "out projection");
     if (!fuse_ln) VIT_HIP(vit::launch_layernorm(a.x, M, D, w.ln2_g, w.ln2_b, eps, a.h, false, st), "ln2");
     vit::EpiParams e1;
@@ -439,6 +445,10 @@ int run_encoder(vit_model* m, const Acts& a, const Geom& g, const float* images,
       e2.ln_b = m->blocks[l + 1].ln1_b;
       e2.eps = eps;
       e2.h = a.h;
+      // the next block's LN1 parameters, Q/K/V and out-projection weights
+      const BlockW& nx = m->blocks[l + 1];
+      e2.prefetch = nx.ln1_g;
+      e2.prefetch_bytes = (size_t)((const char*)(nx.wo + (size_t)D * D) - (const char*)nx.ln1_g);
     }
     VIT_HIP(vit::launch_gemm(a.f, w.w2, M, D, Hm, e2, st), "fc2");
     if (taps && l < 32 && ((pl.cfg.tap_mask >> l) & 1u)) {
