@@ -605,6 +605,9 @@ def main():
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("CSV", "WORKLOAD"),
                     help="host only: matrix-core utilisation table from a rocprofv3 --pmc CSV of "
                          "--breakdown-only WORKLOAD")
+    ap.add_argument("--forward-only", choices=sorted(WORKLOADS),
+                    help="run only the whole-forward timing of one workload (eager, then graph replays) and print "
+                         "its JSON (for kernel traces of the forward as it runs in the graph)")
     ap.add_argument("--breakdown-only", choices=sorted(WORKLOADS),
                     help="run only the per-op timing loops of one workload and print their JSON (for counter runs)")
     args = ap.parse_args()
@@ -631,6 +634,12 @@ def main():
         return
     if args.gemm_vs_library:
         print(json.dumps(gemm_vs_library(args.steps, args.warmup)), flush=True)
+        return
+    if args.forward_only:
+        name, batch = WORKLOADS[args.forward_only]
+        _, enc, res = bench_workload(name, batch, args.steps, args.warmup)
+        enc.close()
+        print(json.dumps(res), flush=True)
         return
     if args.breakdown_only:
         name, batch = WORKLOADS[args.breakdown_only]
