@@ -1236,14 +1236,15 @@ hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, int M, int N, int K
       EpiResidualLN e{ep.bias, ep.ls, (float*)ep.out, ep.ln_g, ep.ln_b, ep.eps, (bf16_t*)ep.h};
       // One 64-row tile per CU (its two stages fill most of the LDS); where
       // the tiles leave CUs idle, up to that many extra workgroups read the
-      // prefetch region there, about 32 chunks of 16 bytes per lane.
+      // prefetch region there, about 8 chunks of 16 bytes per lane, so that
+      // they finish well within the tiles' time.
       const int tiles = (M + CfgRowLN::BM - 1) / CfgRowLN::BM;
       int extra = 0;
       if (ep.prefetch && ep.prefetch_bytes >= 16 && tiles < kComputeUnits) {
         if (reinterpret_cast<uintptr_t>(ep.prefetch) % 16 != 0 || ep.prefetch_bytes >= (1ull << 32))
           return hipErrorInvalidValue;
         const uint32_t chunks = (uint32_t)(ep.prefetch_bytes / 16);
-        constexpr uint32_t per_wg = 64u * CfgRowLN::WGM * CfgRowLN::WGN * 32u;
+        constexpr uint32_t per_wg = 64u * CfgRowLN::WGM * CfgRowLN::WGN * 8u;
         extra = (int)std::min<uint32_t>((uint32_t)(kComputeUnits - tiles), (chunks + per_wg - 1) / per_wg);
         e.pf = static_cast<const uint4*>(ep.prefetch);
         e.pf_chunks = chunks;
