@@ -179,6 +179,37 @@ def test_depth_zero_model():
     assert np.abs(tok - ref["tokens"]).max() <= 2e-3
 
 
+@pytest.mark.parametrize("dim", [64, 384, 768, 1024, 1536])
+def test_descriptor_normalises_the_cls_row(dim):
+    """vit_descriptor: d = t[b, 0] / max(||t[b, 0]||, 1e-12) (the model card's
+    "Usage", F.normalize's eps), against the float64 definition on rows of very
+    different scales, a row of zeros (d = 0) and a row with one non-zero entry
+    (d = a unit vector, exactly).  Widths 384, 768 and 1024 take the register
+    path of the kernel, the others its strided loop."""
+    rng = np.random.default_rng(31 + dim)
+    cfg = synth.preset("vits16_224", depth=0, img_h=32, img_w=32, dim=dim, heads=dim // 64, mlp_hidden=4 * dim)
+    enc = vit.Encoder(cfg, synth.make_params(cfg), max_batch=6)
+    N = enc.tokens
+    t = rng.standard_normal((6, N, dim)).astype(np.float32)
+    t[:, 0] *= np.array([1.0, 1e-3, 1e3, 1e-20, 1.0, 1.0], np.float32)[:, None]
+    t[4, 0] = 0.0
+    t[5, 0] = 0.0
+    t[5, 0, dim // 3] = -2.5
+    desc = host(enc.descriptor(f32_dev(t)))
+    enc.close()
+    row = t[:, 0].astype(np.float64)
+    ref = row / np.maximum(np.linalg.norm(row, axis=1, keepdims=True), 1e-12)
+    err = np.abs(desc - ref)
+    say(f"  dim {dim}: max |desc - ref| = {err.max():.3e}")
+    # fp32: the sum of dim squares carries a relative error below dim 2^-24
+    # (halved by the square root), the reciprocal and the product one rounding each
+    assert (err <= np.abs(ref) * (dim + 8) * 2.0 ** -24 + 1e-30).all()
+    np.testing.assert_array_equal(desc[4], 0.0)
+    expect = np.zeros(dim)
+    expect[dim // 3] = -1.0
+    np.testing.assert_array_equal(desc[5], expect)
+
+
 @pytest.mark.parametrize("batch", [1, 3])
 def test_patch_embedding_and_final_norm_exact(batch):
     """Patchify, the patch-embedding GEMM and its token-row scatter, the CLS and

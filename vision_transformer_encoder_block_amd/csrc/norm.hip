@@ -125,14 +125,31 @@ __global__ __launch_bounds__(256) void ln_l2_kernel(const float* __restrict__ x,
         make_uint2(pack_bf16x2(v[k].x * inv, v[k].y * inv), pack_bf16x2(v[k].z * inv, v[k].w * inv));
 }
 
+// One wave per image.  F > 0: dim = 64 F, and the wave reads the whole row
+// into registers before it reduces (all loads in flight at once); F = 0: any
+// dim, a strided loop.  Both sum lane-wise in column order, so they agree bit
+// for bit.
+template <int F>
 __global__ __launch_bounds__(64) void descriptor_kernel(const float* __restrict__ x, size_t row_stride, int dim,
                                                         float* __restrict__ desc) {
   const int lane = threadIdx.x;
   const float* xr = x + (size_t)blockIdx.x * row_stride;
+  float* dr = desc + (size_t)blockIdx.x * dim;
   float s = 0.f;
-  for (int c = lane; c < dim; c += 64) s += xr[c] * xr[c];
-  const float inv = 1.0f / fmaxf(sqrtf(wave_sum(s)), 1e-12f);
-  for (int c = lane; c < dim; c += 64) desc[(size_t)blockIdx.x * dim + c] = xr[c] * inv;
+  if constexpr (F > 0) {
+    float v[F];
+#pragma unroll
+    for (int i = 0; i < F; ++i) v[i] = xr[lane + 64 * i];
+#pragma unroll
+    for (int i = 0; i < F; ++i) s += v[i] * v[i];
+    const float inv = 1.0f / fmaxf(sqrtf(wave_sum(s)), 1e-12f);
+#pragma unroll
+    for (int i = 0; i < F; ++i) dr[lane + 64 * i] = v[i] * inv;
+  } else {
+    for (int c = lane; c < dim; c += 64) s += xr[c] * xr[c];
+    const float inv = 1.0f / fmaxf(sqrtf(wave_sum(s)), 1e-12f);
+    for (int c = lane; c < dim; c += 64) dr[c] = xr[c] * inv;
+  }
 }
 
 template <template <int> class Launch, class... Args>
@@ -229,7 +246,14 @@ hipError_t launch_ln_l2(const float* x, int batch, int tokens, int first_patch, 
 
 hipError_t launch_descriptor(const float* x, int batch, size_t row_stride, int dim, float* desc, hipStream_t s) {
   if (batch <= 0 || dim <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(descriptor_kernel, dim3(batch), dim3(64), 0, s, x, row_stride, dim, desc);
+  if (dim == 384)
+    hipLaunchKernelGGL(descriptor_kernel<6>, dim3(batch), dim3(64), 0, s, x, row_stride, dim, desc);
+  else if (dim == 768)
+    hipLaunchKernelGGL(descriptor_kernel<12>, dim3(batch), dim3(64), 0, s, x, row_stride, dim, desc);
+  else if (dim == 1024)
+    hipLaunchKernelGGL(descriptor_kernel<16>, dim3(batch), dim3(64), 0, s, x, row_stride, dim, desc);
+  else
+    hipLaunchKernelGGL(descriptor_kernel<0>, dim3(batch), dim3(64), 0, s, x, row_stride, dim, desc);
   return hipGetLastError();
 }
 
