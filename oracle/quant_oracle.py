@@ -25,9 +25,17 @@ product is the float64 matrix product of the dequantised operands.
 Readings (listed in the design notes): per-tensor scales; saturation (not
 NaN) for magnitudes past 448; ties to even.
 
+The same layer with 8-bit integer operands (the INT8 builds the deployment
+article mentions): symmetric per-tensor quantisation q = the integer nearest
+to float32(x) * float32(s_inv), ties to even, clamped to [-127, 127] (the
+code -128 is left unused so that the range is symmetric), NaN -> 0.  The
+products are integers and their sums are exact, so the layer is
+y = sa * sw * (qa qw^T) + b with the integer matrix product taken exactly.
+
 Parity status: pinned by ``tests/test_oracle_quant.py`` (torch's float8_e4m3fn
 cast for every value in range, the format's closed-form extremes, brute force
-on tiny products).
+on tiny products; for int8, torch's qint8 quantisation in range, brute-force
+nearest integers, saturation and the closed-form all-extreme product).
 """
 
 from __future__ import annotations
@@ -77,6 +85,35 @@ def dequantize_e4m3(codes: np.ndarray, scale: float) -> np.ndarray:
 def linear_fp8(qa: np.ndarray, sa: float, qw: np.ndarray, sw: float, bias: np.ndarray | None) -> np.ndarray:
     """y = dequant(qa) @ dequant(qw)^T + b with qa [M, K], qw [N, K] E4M3 codes."""
     y = dequantize_e4m3(qa, sa) @ dequantize_e4m3(qw, sw).T
+    if bias is not None:
+        y = y + np.asarray(bias, F64)
+    return y
+
+
+INT8_MAX = 127
+
+
+def quantize_int8(x: np.ndarray, s_inv: float) -> np.ndarray:
+    """Codes (int8) of x * s_inv (product in float32): the nearest integer, ties
+    to even, clamped to [-127, 127] (infinities included); NaN gives 0."""
+    v = (np.asarray(x, np.float32) * np.float32(s_inv)).astype(F64)
+    q = np.clip(np.rint(np.nan_to_num(v, nan=0.0, posinf=INT8_MAX, neginf=-INT8_MAX)), -INT8_MAX, INT8_MAX)
+    return q.astype(np.int8)
+
+
+def dequantize_int8(codes: np.ndarray, scale: float) -> np.ndarray:
+    """Codes times the scale (float64)."""
+    return np.asarray(codes, F64) * F64(scale)
+
+
+def int8_products(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """The exact integer sums qa qw^T (int64) of qa [M, K] and qw [N, K] codes."""
+    return np.asarray(qa, np.int64) @ np.asarray(qw, np.int64).T
+
+
+def linear_int8(qa: np.ndarray, sa: float, qw: np.ndarray, sw: float, bias: np.ndarray | None) -> np.ndarray:
+    """y = sa * sw * (qa qw^T) + b with qa [M, K], qw [N, K] int8 codes."""
+    y = int8_products(qa, qw).astype(F64) * (F64(sa) * F64(sw))
     if bias is not None:
         y = y + np.asarray(bias, F64)
     return y
