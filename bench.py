@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+PEAK_INT8_TOPS = 5000.0    # MI355X dense int8 MFMA (TOP/s)
 PEAK_HBM_GBS = 8000.0
 METRIC = "images/s and % of bf16 MFMA peak, ViT-S/16@336 b32 and ViT-L/16@1024 b1"
 
@@ -514,9 +515,10 @@ def bench_head(steps=30, warmup=5):
 
 
 def bench_fp8(steps=30, warmup=5):
-    """The fp8 (E4M3) linear layer against the bf16 one on the same shapes: the
-    encoder's fc1 / fc2 (ViT-S/16 @336 b32, ViT-L/16 @1024 b1) and a square
-    8192^3 product; TFLOP/s against the fp8 dense peak (5.0 PF)."""
+    """The fp8 (E4M3) and int8 linear layers against the bf16 one on the same
+    shapes: the encoder's fc1 / fc2 (ViT-S/16 @336 b32, ViT-L/16 @1024 b1) and
+    a square 8192^3 product; TFLOP/s against the fp8 dense peak (5.0 PF) and
+    TOP/s against the int8 dense peak (5.0 POP/s)."""
     import torch
     import vision_transformer_encoder_block_amd as vit
     g = torch.Generator(device="cuda").manual_seed(8)
@@ -528,6 +530,9 @@ def bench_fp8(steps=30, warmup=5):
         bias = torch.zeros(N, device="cuda")
         out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         ms8 = time_loop(lambda: vit.vit_op_linear_fp8(qa, qw, M, N, K, 1.0, bias, out), steps, warmup)
+        ia = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+        iw = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+        msi = time_loop(lambda: vit.vit_op_linear_int8(ia, iw, M, N, K, 1.0 / 16384, bias, out), steps, warmup)
         a = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
         w = torch.randn(N, K, device="cuda", generator=g).to(torch.bfloat16)
         ms16 = time_loop(lambda: vit.vit_op_linear(a, w, bias, M, N, K, vit.EPI_BIAS_BF16, None, out), steps,
@@ -535,8 +540,10 @@ def bench_fp8(steps=30, warmup=5):
         fl = 2.0 * M * N * K
         res[name] = {"shape": [M, N, K], "fp8_us": ms8 * 1e3, "fp8_tflops": fl / (ms8 * 1e-3) / 1e12,
                      "fp8_frac_peak": fl / (ms8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                     "int8_us": msi * 1e3, "int8_tops": fl / (msi * 1e-3) / 1e12,
+                     "int8_frac_peak": fl / (msi * 1e-3) / 1e12 / PEAK_INT8_TOPS,
                      "bf16_us": ms16 * 1e3, "bf16_tflops": fl / (ms16 * 1e-3) / 1e12, "speedup": ms16 / ms8}
-        del qa, qw, a, w, out
+        del qa, qw, ia, iw, a, w, out
     return res
 
 

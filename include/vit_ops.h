@@ -123,6 +123,28 @@ int vit_op_quantize_fp8(const void* x, int x_bf16, size_t n, float s_inv, void* 
 int vit_op_linear_fp8(const void* a, const void* w, int M, int N, int K, float scale, const float* bias, void* out,
                       int out_f32, void* stream);
 
+/* ---- low-precision (int8) linear layer ------------------------------------
+ * The same Linear layer with 8-bit integer operands (the DINOv2 deployment
+ * article's INT8 engines), on gfx950's int8 matrix cores
+ * (v_mfma_i32_32x32x32_i8).  Quantisation is symmetric with one scale per
+ * tensor: a scale s = amax / 127 (vit_op_absmax) maps the largest magnitude to
+ * the largest code. */
+
+/* int8 codes: out[i] = the integer nearest to x[i] * s_inv (the product rounded
+ * to fp32 first), ties to even, clamped to [-127, 127] (infinities included;
+ * the code -128 is never produced), NaN -> 0.  x fp32 or bf16 [n]; out int8
+ * [n], 4-byte aligned; s_inv finite. */
+int vit_op_quantize_int8(const void* x, int x_bf16, size_t n, float s_inv, void* out, void* stream);
+
+/* out[m, n] = scale * sum_k A[m, k] W[n, k] + bias[n] with A [M, K] and W
+ * [N, K] int8 codes (row-major, K contiguous), scale = s_a * s_w, bias [N]
+ * fp32 or NULL, out [M, N] fp32 (out_f32 = 1) or bf16.  K must be a multiple
+ * of 128 and at most 131072, so that the int32 sums (exact) cannot overflow;
+ * each sum is then rounded to fp32 (nearest even) and out = fma(sum, scale,
+ * bias) in fp32, rounded to bf16 (nearest even) for bf16 output. */
+int vit_op_linear_int8(const void* a, const void* w, int M, int N, int K, float scale, const float* bias, void* out,
+                       int out_f32, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,6 +26,7 @@ __all__ = [
     "Encoder", "EncoderGraph", "EPI_BIAS_BF16", "EPI_GELU_BF16", "EPI_RESIDUAL", "EPI_BIAS_F32",
     "HeadConfig", "HeadSizes", "head_config_preset", "head_config", "head_plan", "pack_head_params", "SemanticHead",
     "vit_op_conv3x3", "vit_op_convx", "vit_op_absmax", "vit_op_quantize_fp8", "vit_op_linear_fp8",
+    "vit_op_quantize_int8", "vit_op_linear_int8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvit.so")
@@ -98,6 +99,8 @@ _SIGNATURES = {
     "vit_op_absmax": (_I, [_P, _I, ctypes.c_size_t, _P, _P]),
     "vit_op_quantize_fp8": (_I, [_P, _I, ctypes.c_size_t, ctypes.c_float, _P, _P]),
     "vit_op_linear_fp8": (_I, [_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _I, _P]),
+    "vit_op_quantize_int8": (_I, [_P, _I, ctypes.c_size_t, ctypes.c_float, _P, _P]),
+    "vit_op_linear_int8": (_I, [_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _I, _P]),
 }
 
 
@@ -437,6 +440,19 @@ def vit_op_linear_fp8(a, w, M, N, K, scale, bias, out, stream=None):
     import torch
     return _check("vit_op_linear_fp8", lib().vit_op_linear_fp8(_ptr(a), _ptr(w), M, N, K, scale, _ptr(bias), _ptr(out),
                                                                int(out.dtype == torch.float32), _stream(stream)))
+
+
+def vit_op_quantize_int8(x, n, s_inv, out, stream=None):
+    import torch
+    return _check("vit_op_quantize_int8", lib().vit_op_quantize_int8(_ptr(x), int(x.dtype == torch.bfloat16), n, s_inv,
+                                                                     _ptr(out), _stream(stream)))
+
+
+def vit_op_linear_int8(a, w, M, N, K, scale, bias, out, stream=None):
+    import torch
+    return _check("vit_op_linear_int8", lib().vit_op_linear_int8(_ptr(a), _ptr(w), M, N, K, scale, _ptr(bias),
+                                                                 _ptr(out), int(out.dtype == torch.float32),
+                                                                 _stream(stream)))
 
 
 class SemanticHead:

@@ -245,9 +245,10 @@ struct EpiBiasF32G8 {
   }
 };
 
-// fp8 products: acc is the fp32 sum of products of E4M3 values; `scale`
-// (the product of the two operands' dequantisation scales) restores the units:
-// out = acc * scale + bias, in fp32 or bf16.
+// 8-bit products: acc is the fp32 sum of products of E4M3 values, or the
+// exact int32 sum of int8 products converted to fp32; `scale` (the product of
+// the two operands' dequantisation scales) restores the units:
+// out = acc * scale + bias (one fused multiply-add), in fp32 or bf16.
 template <bool F32>
 struct EpiScale {
   float scale;
@@ -465,15 +466,23 @@ __device__ __forceinline__ int swz_c(int r, int c) {
 //         fragment is two chunks (32 values).  Lanes l and l + 32 hold the two
 //         halves of the 64 k values of row l % 32, in the same arrangement for
 //         A and B, which is all the dot products need.
+//   int8: v_mfma_i32_32x32x32_i8; a lane's fragment is one chunk (16 values),
+//         the byte layout of the bf16 case.  The int32 accumulators travel in
+//         the fp32 accumulator registers bit for bit (kIntAcc) and become fp32
+//         values after the main loop; integer sums are exact, so any split of
+//         the k values over the lanes gives the same result.
 typedef int int32x8 __attribute__((ext_vector_type(8)));
+typedef int int32x16 __attribute__((ext_vector_type(16)));
 struct MmaBf16 {
   static constexpr int ES = 2, KPM = 16, CPF = 1;  // bytes per value, k per MFMA, chunks per fragment
+  static constexpr bool kIntAcc = false;
   using Frag = bf16x8;
   __device__ static Frag frag(const uint4& c0, const uint4&) { return as_bf16x8(c0); }
   __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) { return mfma32x32x16(a, b, c); }
 };
 struct MmaFp8 {
   static constexpr int ES = 1, KPM = 64, CPF = 2;
+  static constexpr bool kIntAcc = false;
   using Frag = int32x8;
   __device__ static Frag frag(const uint4& c0, const uint4& c1) {
     Frag f;
@@ -483,6 +492,19 @@ struct MmaFp8 {
   }
   __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+struct MmaI8 {
+  static constexpr int ES = 1, KPM = 32, CPF = 1;
+  static constexpr bool kIntAcc = true;
+  using Frag = int32x4;
+  __device__ static Frag frag(const uint4& c0, const uint4&) {
+    Frag f;
+    f[0] = (int)c0.x, f[1] = (int)c0.y, f[2] = (int)c0.z, f[3] = (int)c0.w;
+    return f;
+  }
+  __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_bit_cast(f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, __builtin_bit_cast(int32x16, c), 0, 0, 0));
   }
 };
 
@@ -717,6 +739,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(const bf16_t*
     });
   }
   __syncthreads();
+  if constexpr (MT::kIntAcc) {  // int32 sums -> fp32 (round to nearest even), whole vectors at a time
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_convertvector(__builtin_bit_cast(int32x16, acc[i][j]), f32x16);
+  }
 
   // accumulator element e of block (i, j): row 8*(e/4) + 4*lhalf + e%4, column lrow
   if constexpr (HasChanLN<Epi>::value) {
@@ -1171,20 +1199,21 @@ hipError_t dispatch_chan_ln(const bf16_t* A, const bf16_t* W, int M, int N, int 
   return run_chan_ln<256>(A, W, M, K, ep, s, am);
 }
 
-// fp8 tiles, chosen by the same rules as the bf16 ones (no 256 x 256 tile:
-// its fp8 fragments would not fit the registers)
-template <class Epi>
-hipError_t dispatch_fp8(const uint8_t* A, const uint8_t* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
+// 8-bit tiles (fp8 or int8 operands, 128 values per K step), chosen by the
+// same rules as the bf16 ones (no 256 x 256 tile: its 8-bit fragments would
+// not fit the registers)
+template <class MT, class Epi>
+hipError_t dispatch_8bit(const void* A, const void* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   const auto a = reinterpret_cast<const bf16_t*>(A);
   const auto w = reinterpret_cast<const bf16_t*>(W);
   const long mid_tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
   if (mid_tiles < 256) {
     const long small_tiles = (long)((M + 63) / 64) * ((N + 127) / 128);
-    if (small_tiles >= 256) return run<CfgSmall8, Epi, AMapLinear, MmaFp8>(a, w, M, N, K, epi, s);
-    return run<CfgTiny8, Epi, AMapLinear, MmaFp8>(a, w, M, N, K, epi, s);
+    if (small_tiles >= 256) return run<CfgSmall8, Epi, AMapLinear, MT>(a, w, M, N, K, epi, s);
+    return run<CfgTiny8, Epi, AMapLinear, MT>(a, w, M, N, K, epi, s);
   }
-  if (K <= 1024 && mid_tiles < 512) return run<CfgSmall8, Epi, AMapLinear, MmaFp8>(a, w, M, N, K, epi, s);
-  return run<CfgMid8, Epi, AMapLinear, MmaFp8>(a, w, M, N, K, epi, s);
+  if (K <= 1024 && mid_tiles < 512) return run<CfgSmall8, Epi, AMapLinear, MT>(a, w, M, N, K, epi, s);
+  return run<CfgMid8, Epi, AMapLinear, MT>(a, w, M, N, K, epi, s);
 }
 
 }  // namespace
@@ -1269,8 +1298,19 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* W, int M, int N, int
   if ((size_t)(M + 256) * K >= (1ull << 32) || (size_t)(N + 256) * K >= (1ull << 32)) return hipErrorInvalidValue;
   auto al = [](const void* p, size_t n) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % n == 0; };
   const bool vec = N % 4 == 0 && ldc % 4 == 0 && al(bias, 16) && al(out, out_f32 ? 16 : 8);
-  if (out_f32) return dispatch_fp8(A, W, M, N, K, EpiScale<true>{scale, bias, out, ldc, vec}, s);
-  return dispatch_fp8(A, W, M, N, K, EpiScale<false>{scale, bias, out, ldc, vec}, s);
+  if (out_f32) return dispatch_8bit<MmaFp8>(A, W, M, N, K, EpiScale<true>{scale, bias, out, ldc, vec}, s);
+  return dispatch_8bit<MmaFp8>(A, W, M, N, K, EpiScale<false>{scale, bias, out, ldc, vec}, s);
+}
+
+hipError_t launch_gemm_int8(const int8_t* A, const int8_t* W, int M, int N, int K, float scale, const float* bias,
+                            void* out, int ldc, bool out_f32, hipStream_t s) {
+  // K * 127^2 < 2^31: the int32 sums cannot overflow
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || K > 131072 || ldc < N || !out) return hipErrorInvalidValue;
+  if ((size_t)(M + 256) * K >= (1ull << 32) || (size_t)(N + 256) * K >= (1ull << 32)) return hipErrorInvalidValue;
+  auto al = [](const void* p, size_t n) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % n == 0; };
+  const bool vec = N % 4 == 0 && ldc % 4 == 0 && al(bias, 16) && al(out, out_f32 ? 16 : 8);
+  if (out_f32) return dispatch_8bit<MmaI8>(A, W, M, N, K, EpiScale<true>{scale, bias, out, ldc, vec}, s);
+  return dispatch_8bit<MmaI8>(A, W, M, N, K, EpiScale<false>{scale, bias, out, ldc, vec}, s);
 }
 
 hipError_t launch_gemm_conv3(const uint16_t* in, int ld_in, int c0, int C, int batch, int gh, int gw,

@@ -77,6 +77,12 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* W, int M, int N, int
 // E4M3 codes of x[i] * s_inv (product in fp32; nearest value, ties to even,
 // saturated to +-448, sign kept, NaN -> 0x7F); x fp32 (x_bf16 == false) or bf16.
 hipError_t launch_quantize_fp8(const void* x, bool x_bf16, size_t n, float s_inv, uint8_t* out, hipStream_t s);
+// int8 codes of x * s_inv (nearest, ties to even, clamped to +-127, NaN -> 0).
+hipError_t launch_quantize_int8(const void* x, bool x_bf16, size_t n, float s_inv, int8_t* out, hipStream_t s);
+// int8 GEMM: out[m, n] = scale * sum_k A[m, k] W[n, k] + bias[n], the sums exact
+// in int32 (K <= 131072), then converted to fp32; K a multiple of 128.
+hipError_t launch_gemm_int8(const int8_t* A, const int8_t* W, int M, int N, int K, float scale, const float* bias,
+                            void* out, int ldc, bool out_f32, hipStream_t s);
 
 // amax[0] = max |x[i]| over n fp32 (or bf16) values (NaN ignored); amax is written, not accumulated.
 hipError_t launch_absmax(const void* x, bool x_bf16, size_t n, float* amax, hipStream_t s);

@@ -1,5 +1,5 @@
-// fp8 (OCP E4M3) quantisation for the low-precision linear layer: per-tensor
-// absolute maximum (to choose a scale) and the E4M3 codes of x * s_inv.
+// 8-bit quantisation for the low-precision linear layers: per-tensor absolute
+// maximum (to choose a scale) and the E4M3 or int8 codes of x * s_inv.
 #include <algorithm>
 
 #include "common.h"
@@ -23,11 +23,26 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return sign | (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);  // exponent 127 + E -> field E + 7
 }
 
+// int8 code of v: the nearest integer with ties to even (v_rndne), clamped to
+// [-127, 127] first (infinities included; clamping before rounding gives the
+// same code as rounding first), NaN -> 0.
+__device__ __forceinline__ uint32_t int8_code(float v) {
+  if (!(v == v)) return 0u;
+  return (uint32_t)(int)rintf(fminf(fmaxf(v, -127.f), 127.f)) & 0xFFu;
+}
+
 __device__ __forceinline__ float load_any(const void* x, bool bf, size_t i) {
   return bf ? bf2f(reinterpret_cast<const bf16_t*>(x)[i]) : reinterpret_cast<const float*>(x)[i];
 }
 
+template <bool INT8>
+__device__ __forceinline__ uint32_t code8(float v) {
+  if constexpr (INT8) return int8_code(v);
+  else return e4m3_code(v);
+}
+
 // Four consecutive values per thread.
+template <bool INT8>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, bool bf, size_t n, float s_inv,
                                                        uint8_t* __restrict__ out) {
   const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -35,10 +50,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   if (i + 4 <= n) {
     uint32_t w = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w |= e4m3_code(load_any(x, bf, i + j) * s_inv) << (8 * j);
+    for (int j = 0; j < 4; ++j) w |= code8<INT8>(load_any(x, bf, i + j) * s_inv) << (8 * j);
     *reinterpret_cast<uint32_t*>(out + i) = w;
   } else {
-    for (size_t j = i; j < n; ++j) out[j] = (uint8_t)e4m3_code(load_any(x, bf, j) * s_inv);
+    for (size_t j = i; j < n; ++j) out[j] = (uint8_t)code8<INT8>(load_any(x, bf, j) * s_inv);
   }
 }
 
@@ -66,8 +81,16 @@ __global__ __launch_bounds__(256) void absmax_kernel(const void* __restrict__ x,
 hipError_t launch_quantize_fp8(const void* x, bool x_bf16, size_t n, float s_inv, uint8_t* out, hipStream_t s) {
   if (!x || !out || n == 0 || reinterpret_cast<uintptr_t>(out) % 4) return hipErrorInvalidValue;
   const size_t threads = (n + 3) / 4;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, x_bf16, n, s_inv,
-                     out);
+  hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, x_bf16, n,
+                     s_inv, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_int8(const void* x, bool x_bf16, size_t n, float s_inv, int8_t* out, hipStream_t s) {
+  if (!x || !out || n == 0 || reinterpret_cast<uintptr_t>(out) % 4) return hipErrorInvalidValue;
+  const size_t threads = (n + 3) / 4;
+  hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, x_bf16, n,
+                     s_inv, reinterpret_cast<uint8_t*>(out));
   return hipGetLastError();
 }
 

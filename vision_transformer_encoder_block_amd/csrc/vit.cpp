@@ -832,6 +832,27 @@ int vit_op_linear_fp8(const void* a, const void* w, int M, int N, int K, float s
   return VIT_OK;
 }
 
+int vit_op_quantize_int8(const void* x, int x_bf16, size_t n, float s_inv, void* out, void* stream) {
+  if (!x || !out) return fail(VIT_ERR_ARG, "NULL pointer");
+  if (n == 0) return fail(VIT_ERR_SHAPE, "n must be >= 1");
+  if ((uintptr_t)out % 4) return fail(VIT_ERR_ARG, "out must be 4-byte aligned");
+  if (!std::isfinite(s_inv)) return fail(VIT_ERR_ARG, "s_inv must be finite");
+  VIT_HIP(vit::launch_quantize_int8(x, x_bf16 != 0, n, s_inv, (int8_t*)out, (hipStream_t)stream), "quantize int8");
+  return VIT_OK;
+}
+
+int vit_op_linear_int8(const void* a, const void* w, int M, int N, int K, float scale, const float* bias, void* out,
+                       int out_f32, void* stream) {
+  if (!a || !w || !out) return fail(VIT_ERR_ARG, "NULL pointer");
+  if (M < 1 || N < 1 || K < 128 || K % 128 || K > 131072)
+    return fail(VIT_ERR_SHAPE, "M, N >= 1 and K a multiple of 128 in [128, 131072]");
+  if (!std::isfinite(scale)) return fail(VIT_ERR_ARG, "scale must be finite");
+  VIT_HIP(vit::launch_gemm_int8((const int8_t*)a, (const int8_t*)w, M, N, K, scale, bias, out, N, out_f32 != 0,
+                                (hipStream_t)stream),
+          "linear int8");
+  return VIT_OK;
+}
+
 int vit_op_qkv(const void* h, const void* wqkv, const float* bqkv, int batch, int tokens, int heads, void* q, void* k,
                void* vt, void* stream) {
   if (!h || !wqkv || !bqkv || !q || !k || !vt) return fail(VIT_ERR_ARG, "NULL pointer");
