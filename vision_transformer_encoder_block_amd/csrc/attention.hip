@@ -58,7 +58,6 @@ struct AttnArgs {
   uint32_t pf_chunks;  // its length in 16-byte chunks
 };
 
-
 // Workgroup id -> (query tile, head, image).  Workgroups are handed
 // to the 8 XCDs round-robin by id; the ids are renumbered so that each XCD
 // gets a contiguous run of (image, head) pairs and all query tiles of a pair
